@@ -1,0 +1,156 @@
+"""Pins of the allocator specification model: the hand-traced example and the
+invariants the pages state, on random operation sequences."""
+
+import json
+import os
+
+import numpy as np
+import pytest
+
+from oracle.alloc_model import AllocError, AllocModel, ERR_INVALID, ERR_NO_BLOCKS, ERR_SEQ
+
+
+def test_hand_traced_example(golden_dir):
+    with open(os.path.join(golden_dir, "alloc_trace.json")) as f:
+        g = json.load(f)
+    m = AllocModel(g["num_blocks"], g["block_size"], g["free_order"])
+    for st in g["steps"]:
+        op = st["op"]
+        if op == "add":
+            m.add_seq(st["seq"])
+        elif op == "fork":
+            m.fork(st["parent"], st["child"])
+        elif op == "free":
+            m.free_seq(st["seq"])
+        elif op == "append":
+            if "error" in st:
+                before = (m.free_list(), [m.refcount(b) for b in range(g["num_blocks"])],
+                          {s: m.table(s) for s in m.tables})
+                with pytest.raises(AllocError) as e:
+                    m.append(st["seq"], st["n"])
+                assert e.value.code == st["error"]
+                after = (m.free_list(), [m.refcount(b) for b in range(g["num_blocks"])],
+                         {s: m.table(s) for s in m.tables})
+                assert before == after
+            else:
+                slots, cow = m.append(st["seq"], st["n"])
+                assert slots == st["slots"] and [list(p) for p in cow] == st["cow"], st
+    fin = g["final"]
+    assert {str(s): m.table(s) for s in m.tables} == fin["tables"]
+    assert {str(s): m.length(s) for s in m.tables} == fin["lens"]
+    assert [m.refcount(b) for b in range(g["num_blocks"])] == fin["refcounts"]
+    assert m.free_list() == fin["free"]
+
+
+def check_invariants(m: AllocModel):
+    bs = m.bs
+    holders = [0] * m.num_blocks
+    for s, tab in m.tables.items():
+        L = m.length(s)
+        # one block per started group of bs tokens: fill before allocate
+        assert len(tab) == -(-L // bs)
+        # only the last block may be partly filled: unused slots <= bs - 1
+        assert len(tab) * bs - L <= bs - 1 if tab else L == 0
+        assert len(set(tab)) == len(tab)
+        for b in tab:
+            holders[b] += 1
+    # a refcount is exactly the number of tables holding the block
+    assert holders == [m.refcount(b) for b in range(m.num_blocks)]
+    # free blocks are exactly those nobody holds
+    free = m.free_list()
+    assert sorted(free) == [b for b in range(m.num_blocks) if holders[b] == 0]
+    assert len(set(free)) == len(free)
+
+
+def test_random_op_sequences_keep_invariants():
+    rng = np.random.default_rng(11)
+    for trial in range(200):
+        nb = int(rng.integers(1, 24))
+        bs = int(rng.choice([1, 2, 4, 16]))
+        m = AllocModel(nb, bs, rng.permutation(nb))
+        live, nxt = [], 0
+        for _ in range(60):
+            r = rng.random()
+            try:
+                if r < 0.2 or not live:
+                    m.add_seq(nxt)
+                    live.append(nxt)
+                    nxt += 1
+                elif r < 0.35:
+                    p = int(rng.choice(live))
+                    m.fork(p, nxt)
+                    live.append(nxt)
+                    nxt += 1
+                elif r < 0.9:
+                    s = int(rng.choice(live))
+                    n = int(rng.integers(0, 3 * bs + 1))
+                    need_free = m.num_free()
+                    L0, tab0 = m.length(s), m.table(s)
+                    slots, cows = m.append(s, n)
+                    assert len(slots) == n and m.length(s) == L0 + n
+                    assert len(cows) <= 1
+                    # every slot lands in the sequence's own table at its position
+                    tab = m.table(s)
+                    for k, sl in enumerate(slots):
+                        pos = L0 + k
+                        assert sl == tab[pos // bs] * bs + pos % bs
+                    # never write into a block somebody else still holds
+                    for sl in slots:
+                        assert m.refcount(sl // bs) == 1
+                    # shared full blocks stay shared; only the partly-filled
+                    # shared last block is copied
+                    if cows:
+                        assert L0 % bs != 0 and cows[0][0] == tab0[-1]
+                else:
+                    s = int(rng.choice(live))
+                    m.free_seq(s)
+                    live.remove(s)
+            except AllocError as e:
+                assert e.code == ERR_NO_BLOCKS
+            check_invariants(m)
+
+
+def test_allocation_succeeds_whenever_enough_blocks_are_free():
+    # external fragmentation is gone: any free block serves any sequence
+    rng = np.random.default_rng(12)
+    for _ in range(50):
+        nb, bs = 16, 4
+        m = AllocModel(nb, bs, rng.permutation(nb))
+        m.add_seq(0)
+        m.append(0, int(rng.integers(0, nb * bs // 2)))
+        m.add_seq(1)
+        room = m.num_free() * bs
+        m.append(1, room)           # exactly fills the pool
+        assert m.num_free() == 0
+        with pytest.raises(AllocError):
+            m.append(1, 1)
+
+
+def test_errors_leave_state_unchanged():
+    m = AllocModel(4, 2, [3, 1, 0, 2])
+    m.add_seq(5)
+    m.append(5, 3)
+    snap = (m.free_list(), m.table(5), m.length(5))
+    with pytest.raises(AllocError) as e:
+        m.append(5, 10)
+    assert e.value.code == ERR_NO_BLOCKS
+    assert (m.free_list(), m.table(5), m.length(5)) == snap
+    for bad, code in [(lambda: m.append(9, 1), ERR_SEQ), (lambda: m.add_seq(5), ERR_SEQ),
+                      (lambda: m.fork(9, 10), ERR_SEQ), (lambda: m.fork(5, 5), ERR_SEQ),
+                      (lambda: m.free_seq(9), ERR_SEQ), (lambda: m.append(5, -1), ERR_INVALID)]:
+        with pytest.raises(AllocError) as e:
+            bad()
+        assert e.value.code == code
+    assert (m.free_list(), m.table(5), m.length(5)) == snap
+    with pytest.raises(AllocError):
+        AllocModel(3, 2, [0, 0, 1])
+
+
+def test_full_shared_block_is_not_copied():
+    m = AllocModel(6, 4, range(6))
+    m.add_seq(0)
+    m.append(0, 8)                  # two full blocks
+    m.fork(0, 1)
+    slots, cows = m.append(1, 1)    # next token opens a new block, no copy
+    assert cows == [] and slots == [2 * 4]
+    assert m.refcount(0) == 2 and m.refcount(1) == 2
