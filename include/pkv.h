@@ -1,0 +1,250 @@
+/* pkv.h -- PagedAttention decode for AMD Instinct MI355X (gfx950).
+ *
+ * C ABI of libpkv.so.  The library computes single-query attention for many
+ * sequences at once over a key/value cache that lives in fixed-size blocks
+ * scattered through device memory and reached only through a per-sequence
+ * block table, plus the scatter of each decode step's new key/value token
+ * into the slot the block manager handed out, and a host-side block manager
+ * with shared prefix blocks.
+ *
+ * Sources: "Day 6/90 of Inference Engineering" (PagedAttention notes: blocks
+ * handed out one at a time, fill before allocate, prefix sharing, block
+ * table); "PagedAttention Kernel：大模型推理优化的显存管理革新" §1 (fixed-size
+ * pages scattered through device memory), §2.2 (coalesced access, prefetch of
+ * the next page), §3.1 (QK^T per block, softmax, PV accumulated block by
+ * block), §3.2 (balancing uneven work), §6 (fp32 accumulation).
+ *
+ * Conventions shared by every device entry point
+ * ----------------------------------------------
+ *  - Every pointer argument of a device entry point is a DEVICE pointer
+ *    owned by the caller.  The library never allocates, frees or copies
+ *    device memory and never synchronises; all work is enqueued on `stream`
+ *    (a hipStream_t passed as void*; NULL = the null stream).
+ *  - Return value: PKV_OK (0) or a negative PKV_ERR_* code; on error nothing
+ *    has been enqueued and pkv_last_error() returns a message (thread-local).
+ *  - Only arguments visible on the host are checked (null pointers, sizes,
+ *    supported dtype / head_dim / block_size combinations, workspace size).
+ *    Device contents (block ids, lengths, slots) are trusted; a kernel that
+ *    meets a block id outside [0, num_blocks) or a length beyond the table
+ *    width skips the offending data and writes NaN for that sequence's heads
+ *    instead of reading out of bounds.
+ *  - Element types: PKV_F32 (fp32), PKV_BF16 (bfloat16), PKV_FP8_E4M3 (OCP
+ *    E4M3FN, stored as one byte).  Supported (query, cache) pairs:
+ *    (F32, F32), (BF16, BF16), (BF16, FP8_E4M3).  head_dim is 64 or 128,
+ *    block_size 16 or 32.
+ *
+ * Block pool layout (one pool for keys, one for values)
+ * ------------------------------------------------------
+ *  x = 16 / sizeof(element)            (4 fp32, 8 bf16, 16 fp8)
+ *  key_cache   [num_blocks][num_kv_heads][head_dim / x][block_size][x]
+ *  value_cache [num_blocks][num_kv_heads][head_dim][block_size]
+ *  Token position t of sequence s lives in block block_tables[s][t / bs] at
+ *  slot t % bs; a slot id is block * block_size + slot.  One (block, kv head)
+ *  tile of each pool is block_size*head_dim*sizeof(element) contiguous bytes.
+ *
+ *  Query, output and new-token rows are dense row-major:
+ *  query/out [num_seqs][num_q_heads][head_dim]; key/value
+ *  [num_tokens][num_kv_heads][head_dim].  Query head g reads kv head
+ *  g / (num_q_heads / num_kv_heads).
+ */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { PKV_F32 = 0, PKV_BF16 = 1, PKV_FP8_E4M3 = 2 } pkv_dtype;
+
+enum {
+  PKV_OK = 0,
+  PKV_ERR_INVALID = -1,     /* bad argument (null pointer, size, combination)   */
+  PKV_ERR_UNSUPPORTED = -2, /* valid but not built (dtype, head_dim, block_size) */
+  PKV_ERR_WORKSPACE = -3,   /* workspace missing or too small                   */
+  PKV_ERR_HIP = -4,         /* a HIP runtime call or kernel launch failed       */
+  PKV_ERR_NO_BLOCKS = -5,   /* allocator: not enough free blocks                */
+  PKV_ERR_SEQ = -6          /* allocator: unknown or duplicate sequence id      */
+};
+
+/* Message for the last error returned on this thread ("" if none). */
+const char* pkv_last_error(void);
+
+/* ABI version of this header (bumped on incompatible change). */
+int pkv_abi_version(void);
+#define PKV_ABI_VERSION 1
+
+/* ---------------------------------------------------------------------------
+ * paged_kv_write -- scatter new key/value rows into their slots.
+ * Each step's new token goes wherever the block manager put it ("Day 6/90 of
+ * Inference Engineering", PagedAttention notes).
+ *
+ *  key, value     [num_tokens][num_kv_heads][head_dim] of src_dtype (device)
+ *  key_cache,
+ *  value_cache    block pools of cache_dtype in the layout above (device)
+ *  slot_mapping   [num_tokens] int32 (device); token i goes to slot
+ *                 slot_mapping[i]; a negative slot skips the token, and so
+ *                 does a slot >= num_blocks * block_size.
+ *  src/cache      (F32 -> F32) and (BF16 -> BF16) copy bits; (BF16 -> FP8)
+ *                 stores E4M3FN(fp32(x) * fp32(1 / scale)) rounded to nearest
+ *                 even and saturated to +-448 (NaN -> 0x7F), with
+ *                 scale = k_scale for keys and v_scale for values (the
+ *                 dequantisation multipliers; ignored unless cache is FP8).
+ *  Two tokens mapped to the same slot race (the result is one of them).
+ * ------------------------------------------------------------------------- */
+int paged_kv_write(const void* key, const void* value, void* key_cache, void* value_cache,
+                   const int32_t* slot_mapping, int num_tokens, int num_kv_heads, int head_dim,
+                   int block_size, int num_blocks, pkv_dtype src_dtype, pkv_dtype cache_dtype,
+                   float k_scale, float v_scale, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Split-K partitions.  With partition_tokens = P > 0, sequence s is cut into
+ * n_s = max(1, ceil(context_lens[s] / P)) partitions of logical tokens
+ * [p*P, (p+1)*P); partition_offsets[s] = sum_{r<s} n_r, partition_offsets[S]
+ * = total_partitions.  paged_attention_partition_offsets computes that on the
+ * host from host-side lengths.
+ * ------------------------------------------------------------------------- */
+int paged_attention_partition_offsets(const int32_t* context_lens_host, int num_seqs,
+                                      int partition_tokens, int32_t* offsets_host_out,
+                                      int* total_partitions_out);
+
+/* Workspace bytes paged_attention_decode needs for total_partitions
+ * partitions: total_partitions * num_q_heads * (head_dim + 2) * 4. */
+size_t paged_attention_workspace_bytes(int total_partitions, int num_q_heads, int head_dim);
+
+/* ---------------------------------------------------------------------------
+ * paged_attention_decode -- out[s, g, :] = softmax(scale * K_s q_{s,g}) V_s
+ * over the context_lens[s] tokens of sequence s, with K_s, V_s read block by
+ * block through block_tables ("PagedAttention Kernel：大模型推理优化的显存管理
+ * 革新" §3.1: QK^T per block, softmax, PV; fp32 accumulation per §6).
+ *
+ *  out            [num_seqs][num_q_heads][head_dim] of q_dtype (device)
+ *  query          [num_seqs][num_q_heads][head_dim] of q_dtype (device)
+ *  key_cache,
+ *  value_cache    block pools of cache_dtype (device)
+ *  block_tables   [num_seqs][max_blocks_per_seq] int32 physical block ids
+ *                 (device); only the first ceil(context_lens[s]/block_size)
+ *                 entries of row s are read
+ *  context_lens   [num_seqs] int32 (device); 0 gives a zero output row
+ *  scale          softmax scale applied to q.k (fp32)
+ *  k_scale,v_scale dequantisation multipliers of an FP8 cache (else ignored)
+ *  partition_tokens 0 = one pass per sequence (no workspace needed);
+ *                 else P > 0, a multiple of block_size: split-K over
+ *                 partitions of P tokens, partials in `workspace`, then the
+ *                 split-K reduce (both launched here, in order, on `stream`)
+ *  partition_offsets [num_seqs + 1] int32 (device), as described above;
+ *                 NULL when partition_tokens == 0
+ *  total_partitions host copy of partition_offsets[num_seqs]
+ *  workspace      device scratch of >= paged_attention_workspace_bytes()
+ *                 bytes (caller-owned; contents need no initialisation)
+ * ------------------------------------------------------------------------- */
+int paged_attention_decode(void* out, const void* query, const void* key_cache,
+                           const void* value_cache, const int32_t* block_tables,
+                           int max_blocks_per_seq, const int32_t* context_lens, int num_seqs,
+                           int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                           int num_blocks, float scale, pkv_dtype q_dtype, pkv_dtype cache_dtype,
+                           float k_scale, float v_scale, int partition_tokens,
+                           const int32_t* partition_offsets, int total_partitions,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/* paged_attention_decode_partials -- the first of the two launches above on
+ * its own: writes `out` for sequences with a single partition and partials
+ * (m, l, unnormalised o) into `workspace` for the others.  Same arguments as
+ * paged_attention_decode; partition_tokens must be > 0. */
+int paged_attention_decode_partials(void* out, const void* query, const void* key_cache,
+                                    const void* value_cache, const int32_t* block_tables,
+                                    int max_blocks_per_seq, const int32_t* context_lens,
+                                    int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                                    int block_size, int num_blocks, float scale, pkv_dtype q_dtype,
+                                    pkv_dtype cache_dtype, float k_scale, float v_scale,
+                                    int partition_tokens, const int32_t* partition_offsets,
+                                    int total_partitions, void* workspace, size_t workspace_bytes,
+                                    void* stream);
+
+/* paged_attention_splitk_reduce -- combine the partials of every sequence
+ * with more than one partition ("PagedAttention Kernel" article §3.2: uneven
+ * pages need the work split): with running maxima m_p (log2 domain), sums
+ * l_p and unnormalised outputs o_p, out = sum_p 2^(m_p - M) o_p /
+ * sum_p 2^(m_p - M) l_p, M = max_p m_p.  Sequences with one partition are
+ * left untouched. */
+int paged_attention_splitk_reduce(void* out, const void* workspace, size_t workspace_bytes,
+                                  const int32_t* partition_offsets, int num_seqs,
+                                  int num_q_heads, int head_dim, int total_partitions,
+                                  pkv_dtype out_dtype, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * paged_kv_copy_blocks -- copy whole key and value blocks (all kv heads):
+ * for i < num_pairs, block pairs[2i] -> block pairs[2i+1], in both pools.
+ * Serves the allocator's copy-on-write of a shared, partly filled last block
+ * (prefix sharing, "Day 6/90 of Inference Engineering").  pairs is device
+ * int32 [num_pairs][2]; block_bytes = num_kv_heads*block_size*head_dim*elem.
+ * Destinations must be distinct and no destination may be a source.
+ * ------------------------------------------------------------------------- */
+int paged_kv_copy_blocks(void* key_cache, void* value_cache, const int32_t* pairs, int num_pairs,
+                         size_t block_bytes, int num_blocks, void* stream);
+
+/* paged_kv_gather -- read every sequence back through its block table into
+ * dense rows: k_out, v_out [cu_ctx[num_seqs]][num_kv_heads][head_dim] of
+ * cache_dtype bits, sequence s occupying rows cu_ctx[s] .. cu_ctx[s+1]-1
+ * (cu_ctx: device int32 [num_seqs+1], prefix sum of lengths; total_tokens
+ * = its last entry, passed from the host).  A test aid for bit-exact checks
+ * of the cache contents. */
+int paged_kv_gather(void* k_out, void* v_out, const void* key_cache, const void* value_cache,
+                    const int32_t* block_tables, int max_blocks_per_seq, const int32_t* cu_ctx,
+                    int num_seqs, int total_tokens, int num_kv_heads, int head_dim, int block_size,
+                    int num_blocks, pkv_dtype cache_dtype, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Host block allocator ("Day 6/90 of Inference Engineering", PagedAttention
+ * notes): hands out one block at a time, takes a new block only when the
+ * last one is full, shares prefix blocks by reference count and starts a
+ * new block where prompts diverge.  Host memory only; not thread-safe.
+ * Every call either succeeds or returns an error leaving the state as it
+ * was.  Policy, fixed so tables are reproducible:
+ *   - free list: FIFO queue initialised from free_order (NULL = 0..n-1);
+ *     allocation pops the front; a block whose refcount reaches 0 is pushed
+ *     to the back;
+ *   - fork(parent, child): child gets a copy of the parent's table and
+ *     length; every block gains one reference;
+ *   - append(seq, n): token by token -- if the sequence has no block or its
+ *     last block is full, pop a new block; else if the last block's refcount
+ *     is > 1, pop a new block, emit a copy-on-write pair (old, new), drop a
+ *     reference to old and replace it in the table; the token takes slot
+ *     table[pos / bs] * bs + pos % bs;
+ *   - free_seq: drop one reference per table entry, in table order.
+ * ------------------------------------------------------------------------- */
+typedef struct pkv_alloc pkv_alloc;
+
+/* NULL on invalid arguments (see pkv_last_error). free_order, if not NULL,
+ * must be a permutation of 0..num_blocks-1 (host memory, copied). */
+pkv_alloc* pkv_alloc_create(int num_blocks, int block_size, const int32_t* free_order);
+void pkv_alloc_destroy(pkv_alloc* a);
+int pkv_alloc_add_seq(pkv_alloc* a, int64_t seq);
+int pkv_alloc_fork(pkv_alloc* a, int64_t parent, int64_t child);
+/* slots_out: host int32 [n_tokens]; cow_pairs_out: host int32 [2*cow_cap]
+ * receiving (src, dst) pairs; *n_cow_out = pairs written (at most 1 per
+ * call).  cow_cap < 1 is an error only if a copy is needed. */
+int pkv_alloc_append(pkv_alloc* a, int64_t seq, int n_tokens, int32_t* slots_out,
+                     int32_t* cow_pairs_out, int cow_cap, int* n_cow_out);
+int pkv_alloc_free_seq(pkv_alloc* a, int64_t seq);
+/* Copies the table of seq into out (host, capacity cap); *n_out = its length. */
+int pkv_alloc_block_table(const pkv_alloc* a, int64_t seq, int32_t* out, int cap, int* n_out);
+/* Fills out[num_seqs][width] (host) with the tables of seqs[i], padded with
+ * pad; fails if a table is wider than width. */
+int pkv_alloc_fill_tables(const pkv_alloc* a, const int64_t* seqs, int num_seqs, int32_t* out,
+                          int width, int32_t pad);
+/* Length in tokens of seq, or a negative error. */
+int64_t pkv_alloc_seq_len(const pkv_alloc* a, int64_t seq);
+/* Refcount of a block, or a negative error. */
+int pkv_alloc_refcount(const pkv_alloc* a, int32_t block);
+int pkv_alloc_num_free(const pkv_alloc* a);
+/* Copies the free list, front first, into out (capacity cap); returns count. */
+int pkv_alloc_free_list(const pkv_alloc* a, int32_t* out, int cap);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H */

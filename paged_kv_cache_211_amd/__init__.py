@@ -1,0 +1,281 @@
+"""PagedAttention decode for AMD Instinct MI355X (gfx950).
+
+Thin Python binding over libpkv.so (include/pkv.h): every function takes
+torch tensors, checks that their shapes agree, and passes raw pointers, sizes
+and the current HIP stream to the C ABI.  All computation happens in the
+library's HIP kernels; nothing here computes attention, and there is no CPU
+fallback.
+
+    key_cache   [num_blocks, H_kv, head_dim // x, block_size, x]
+    value_cache [num_blocks, H_kv, head_dim, block_size]
+    x = 16 // element size (4 fp32, 8 bf16, 16 fp8)
+
+fp8 pools are torch.uint8 (or torch.float8_e4m3fn) tensors of E4M3FN codes.
+"""
+
+from __future__ import annotations
+
+import ctypes
+
+import numpy as np
+import torch
+
+from . import _native
+from ._native import PKV_BF16, PKV_F32, PKV_FP8_E4M3, PkvError, check, lib
+
+__all__ = [
+    "PkvError", "paged_kv_write", "paged_attention_decode", "paged_attention_decode_partials",
+    "paged_attention_splitk_reduce", "paged_kv_copy_blocks", "paged_kv_gather",
+    "paged_attention_partition_offsets", "paged_attention_workspace_bytes", "BlockAllocator",
+    "empty_pools", "cache_dtype_code",
+]
+
+lib()  # fail at import if the library is missing or incomplete
+
+_CODES = {torch.float32: PKV_F32, torch.bfloat16: PKV_BF16, torch.uint8: PKV_FP8_E4M3,
+          torch.float8_e4m3fn: PKV_FP8_E4M3}
+
+
+def cache_dtype_code(t: torch.Tensor) -> int:
+    try:
+        return _CODES[t.dtype]
+    except KeyError:
+        raise PkvError(-1, f"unsupported tensor dtype {t.dtype}") from None
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _need(t: torch.Tensor, name: str, dtype=None):
+    if not t.is_cuda:
+        raise PkvError(-1, f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise PkvError(-1, f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise PkvError(-1, f"{name} must be {dtype}, got {t.dtype}")
+
+
+def _pool_shape(key_cache: torch.Tensor, value_cache: torch.Tensor):
+    if key_cache.dim() != 5 or value_cache.dim() != 4:
+        raise PkvError(-1, "key_cache must be 5-D and value_cache 4-D")
+    nb, H, dx, bs, x = key_cache.shape
+    D = dx * x
+    if tuple(value_cache.shape) != (nb, H, D, bs) or value_cache.dtype != key_cache.dtype:
+        raise PkvError(-1, f"value_cache shape {tuple(value_cache.shape)} does not match key_cache")
+    if x * key_cache.element_size() != 16:
+        raise PkvError(-1, "key_cache last dim must hold 16 bytes")
+    return nb, H, D, bs
+
+
+def empty_pools(num_blocks: int, num_kv_heads: int, head_dim: int, block_size: int,
+                dtype: torch.dtype, device="cuda"):
+    """Allocate (uninitialised) key and value pools in the library's layout."""
+    es = torch.empty((), dtype=dtype).element_size()
+    x = 16 // es
+    kc = torch.empty((num_blocks, num_kv_heads, head_dim // x, block_size, x), dtype=dtype, device=device)
+    vc = torch.empty((num_blocks, num_kv_heads, head_dim, block_size), dtype=dtype, device=device)
+    return kc, vc
+
+
+def paged_kv_write(key, value, key_cache, value_cache, slot_mapping, k_scale=1.0, v_scale=1.0,
+                   stream=None):
+    nb, H, D, bs = _pool_shape(key_cache, value_cache)
+    for t, n in ((key, "key"), (value, "value"), (key_cache, "key_cache"), (value_cache, "value_cache")):
+        _need(t, n)
+    _need(slot_mapping, "slot_mapping", torch.int32)
+    T = key.shape[0]
+    if tuple(key.shape) != (T, H, D) or tuple(value.shape) != (T, H, D) or slot_mapping.numel() != T:
+        raise PkvError(-1, "key/value must be [T, H_kv, head_dim] with T slots")
+    check(lib().paged_kv_write(_ptr(key), _ptr(value), _ptr(key_cache), _ptr(value_cache),
+                               _ptr(slot_mapping), T, H, D, bs, nb, cache_dtype_code(key),
+                               cache_dtype_code(key_cache), float(k_scale), float(v_scale),
+                               _stream(stream)))
+
+
+def paged_attention_partition_offsets(context_lens_host, partition_tokens: int):
+    """Host-side partition offsets: (int32 numpy [S+1], total partitions)."""
+    lens = np.ascontiguousarray(np.asarray(context_lens_host, dtype=np.int32))
+    S = lens.size
+    off = np.zeros(S + 1, dtype=np.int32)
+    tot = ctypes.c_int(0)
+    check(lib().paged_attention_partition_offsets(
+        lens.ctypes.data_as(_native.pi32), S, int(partition_tokens),
+        off.ctypes.data_as(_native.pi32), ctypes.byref(tot)))
+    return off, tot.value
+
+
+def paged_attention_workspace_bytes(total_partitions: int, num_q_heads: int, head_dim: int) -> int:
+    return int(lib().paged_attention_workspace_bytes(total_partitions, num_q_heads, head_dim))
+
+
+def _decode_args(out, query, key_cache, value_cache, block_tables, context_lens, scale, k_scale,
+                 v_scale, partition_tokens, partition_offsets, total_partitions, workspace):
+    nb, H, D, bs = _pool_shape(key_cache, value_cache)
+    for t, n in ((out, "out"), (query, "query"), (key_cache, "key_cache"), (value_cache, "value_cache")):
+        _need(t, n)
+    _need(block_tables, "block_tables", torch.int32)
+    _need(context_lens, "context_lens", torch.int32)
+    S, Hq, Dq = query.shape
+    if Dq != D or tuple(out.shape) != (S, Hq, D) or out.dtype != query.dtype:
+        raise PkvError(-1, "query/out must be [S, H_q, head_dim] of one dtype")
+    if block_tables.dim() != 2 or block_tables.shape[0] != S or context_lens.numel() != S:
+        raise PkvError(-1, "block_tables must be [S, max_blocks] and context_lens [S]")
+    ws_bytes = 0
+    if partition_tokens:
+        if partition_offsets is None or workspace is None:
+            raise PkvError(-3, "split-K needs partition_offsets and a workspace")
+        _need(partition_offsets, "partition_offsets", torch.int32)
+        _need(workspace, "workspace")
+        ws_bytes = workspace.numel() * workspace.element_size()
+    return (_ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache), _ptr(block_tables),
+            block_tables.shape[1], _ptr(context_lens), S, Hq, H, D, bs, nb, float(scale),
+            cache_dtype_code(query), cache_dtype_code(key_cache), float(k_scale), float(v_scale),
+            int(partition_tokens), _ptr(partition_offsets), int(total_partitions), _ptr(workspace),
+            ws_bytes)
+
+
+def paged_attention_decode(out, query, key_cache, value_cache, block_tables, context_lens, scale,
+                           k_scale=1.0, v_scale=1.0, partition_tokens=0, partition_offsets=None,
+                           total_partitions=0, workspace=None, stream=None):
+    args = _decode_args(out, query, key_cache, value_cache, block_tables, context_lens, scale,
+                        k_scale, v_scale, partition_tokens, partition_offsets, total_partitions,
+                        workspace)
+    check(lib().paged_attention_decode(*args, _stream(stream)))
+
+
+def paged_attention_decode_partials(out, query, key_cache, value_cache, block_tables, context_lens,
+                                    scale, k_scale=1.0, v_scale=1.0, partition_tokens=0,
+                                    partition_offsets=None, total_partitions=0, workspace=None,
+                                    stream=None):
+    args = _decode_args(out, query, key_cache, value_cache, block_tables, context_lens, scale,
+                        k_scale, v_scale, partition_tokens, partition_offsets, total_partitions,
+                        workspace)
+    check(lib().paged_attention_decode_partials(*args, _stream(stream)))
+
+
+def paged_attention_splitk_reduce(out, workspace, partition_offsets, total_partitions, stream=None):
+    _need(out, "out")
+    _need(workspace, "workspace")
+    _need(partition_offsets, "partition_offsets", torch.int32)
+    S, Hq, D = out.shape
+    check(lib().paged_attention_splitk_reduce(
+        _ptr(out), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _ptr(partition_offsets), S, Hq, D, int(total_partitions), cache_dtype_code(out),
+        _stream(stream)))
+
+
+def paged_kv_copy_blocks(key_cache, value_cache, pairs, stream=None):
+    nb, H, D, bs = _pool_shape(key_cache, value_cache)
+    _need(key_cache, "key_cache")
+    _need(value_cache, "value_cache")
+    _need(pairs, "pairs", torch.int32)
+    n = pairs.numel() // 2
+    block_bytes = H * bs * D * key_cache.element_size()
+    check(lib().paged_kv_copy_blocks(_ptr(key_cache), _ptr(value_cache), _ptr(pairs), n,
+                                     block_bytes, nb, _stream(stream)))
+
+
+def paged_kv_gather(k_out, v_out, key_cache, value_cache, block_tables, cu_ctx, total_tokens,
+                    stream=None):
+    nb, H, D, bs = _pool_shape(key_cache, value_cache)
+    for t, n in ((k_out, "k_out"), (v_out, "v_out"), (key_cache, "key_cache"), (value_cache, "value_cache")):
+        _need(t, n)
+    _need(block_tables, "block_tables", torch.int32)
+    _need(cu_ctx, "cu_ctx", torch.int32)
+    if tuple(k_out.shape) != (total_tokens, H, D) or tuple(v_out.shape) != (total_tokens, H, D):
+        raise PkvError(-1, "k_out/v_out must be [total_tokens, H_kv, head_dim]")
+    S = cu_ctx.numel() - 1
+    check(lib().paged_kv_gather(_ptr(k_out), _ptr(v_out), _ptr(key_cache), _ptr(value_cache),
+                                _ptr(block_tables), block_tables.shape[1], _ptr(cu_ctx), S,
+                                int(total_tokens), H, D, bs, nb, cache_dtype_code(key_cache),
+                                _stream(stream)))
+
+
+class BlockAllocator:
+    """Host block allocator of libpkv (pkv_alloc_*); not thread-safe."""
+
+    def __init__(self, num_blocks: int, block_size: int, free_order=None):
+        self.num_blocks, self.block_size = int(num_blocks), int(block_size)
+        fo = None
+        if free_order is not None:
+            self._fo = np.ascontiguousarray(np.asarray(free_order, dtype=np.int32))
+            if self._fo.size != num_blocks:
+                raise PkvError(-1, "free_order must have num_blocks entries")
+            fo = self._fo.ctypes.data_as(_native.pi32)
+        h = lib().pkv_alloc_create(int(num_blocks), int(block_size), fo)
+        if not h:
+            raise PkvError(-1, lib().pkv_last_error().decode())
+        self._h = ctypes.c_void_p(h)
+
+    def close(self):
+        if getattr(self, "_h", None):
+            lib().pkv_alloc_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def add_seq(self, seq: int):
+        check(lib().pkv_alloc_add_seq(self._h, int(seq)))
+
+    def fork(self, parent: int, child: int):
+        check(lib().pkv_alloc_fork(self._h, int(parent), int(child)))
+
+    def append(self, seq: int, n: int):
+        """Returns (slots int32 [n], cow pairs int32 [k, 2])."""
+        slots = np.zeros(max(int(n), 1), dtype=np.int32)
+        cow = np.zeros(2, dtype=np.int32)
+        ncow = ctypes.c_int(0)
+        check(lib().pkv_alloc_append(self._h, int(seq), int(n), slots.ctypes.data_as(_native.pi32),
+                                     cow.ctypes.data_as(_native.pi32), 1, ctypes.byref(ncow)))
+        return slots[:int(n)], cow[:2 * ncow.value].reshape(-1, 2)
+
+    def free_seq(self, seq: int):
+        check(lib().pkv_alloc_free_seq(self._h, int(seq)))
+
+    def seq_len(self, seq: int) -> int:
+        r = lib().pkv_alloc_seq_len(self._h, int(seq))
+        if r < 0:
+            check(int(r))
+        return int(r)
+
+    def block_table(self, seq: int) -> np.ndarray:
+        cap = self.seq_len(seq) // self.block_size + 1
+        out = np.zeros(cap, dtype=np.int32)
+        n = ctypes.c_int(0)
+        check(lib().pkv_alloc_block_table(self._h, int(seq), out.ctypes.data_as(_native.pi32), cap,
+                                          ctypes.byref(n)))
+        return out[:n.value]
+
+    def fill_tables(self, seqs, width: int, pad: int = -1) -> np.ndarray:
+        seqs = np.ascontiguousarray(np.asarray(seqs, dtype=np.int64))
+        out = np.zeros((seqs.size, int(width)), dtype=np.int32)
+        check(lib().pkv_alloc_fill_tables(self._h, seqs.ctypes.data_as(_native.pi64), seqs.size,
+                                          out.ctypes.data_as(_native.pi32), int(width), int(pad)))
+        return out
+
+    def refcount(self, block: int) -> int:
+        return check_nonneg(lib().pkv_alloc_refcount(self._h, int(block)))
+
+    def num_free(self) -> int:
+        return check_nonneg(lib().pkv_alloc_num_free(self._h))
+
+    def free_list(self) -> list:
+        out = np.zeros(self.num_blocks, dtype=np.int32)
+        n = lib().pkv_alloc_free_list(self._h, out.ctypes.data_as(_native.pi32), self.num_blocks)
+        return [int(b) for b in out[:check_nonneg(n)]]
+
+
+def check_nonneg(r: int) -> int:
+    if r < 0:
+        check(r)
+    return r

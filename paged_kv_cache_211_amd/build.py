@@ -1,0 +1,62 @@
+"""Build libpkv.so in-tree with hipcc for gfx950.
+
+    python -m paged_kv_cache_211_amd.build          # or __graft_entry__.build()
+
+Every HIP source is compiled with packed fp32 instructions disabled
+(``-Xclang -target-feature -Xclang -packed-fp32-ops``); the host compiler
+warns that it does not know the feature, which is harmless.
+"""
+
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+import tempfile
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB = os.path.join(PKG, "libpkv.so")
+ARCH = "gfx950"
+
+SOURCES = ["api.cpp", "allocator.cpp", "kv_ops.hip", "decode.hip"]
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found (expected /opt/rocm/bin/hipcc)")
+
+
+def compile_cmd(out: str) -> list[str]:
+    srcs = [os.path.join(CSRC, s) for s in SOURCES]
+    return [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            "-Wno-unused-command-line-argument",
+            "-I", INCLUDE, "-I", CSRC, *srcs, "-o", out]
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source into libpkv.so (always recompiles)."""
+    fd, tmp = tempfile.mkstemp(prefix="libpkv.", suffix=".so.tmp", dir=PKG)
+    os.close(fd)
+    cmd = compile_cmd(tmp)
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        os.unlink(tmp)
+        raise RuntimeError(f"hipcc failed ({r.returncode}):\n{r.stdout}\n{r.stderr}")
+    noise = [l for l in r.stderr.splitlines() if "packed-fp32-ops" not in l and l.strip()]
+    if verbose and noise:
+        print("\n".join(noise), file=sys.stderr)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

@@ -1,0 +1,273 @@
+// C ABI of libpkv: argument checks, dtype dispatch and launches on the
+// caller's stream.  Only what the host can see is checked; device contents
+// are trusted (the kernels themselves refuse out-of-range block ids).
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include <hip/hip_runtime.h>
+
+#include "pkv.h"
+#include "pkv_internal.h"
+
+namespace pkv {
+
+static thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+void clear_error() { g_err[0] = 0; }
+
+static bool valid_dtype(int t) { return t == PKV_F32 || t == PKV_BF16 || t == PKV_FP8_E4M3; }
+
+static int hip_status(int e, const char* what) {
+  if (e != hipSuccess)
+    return fail(PKV_ERR_HIP, "%s: %s", what, hipGetErrorString((hipError_t)e));
+  clear_error();
+  return PKV_OK;
+}
+
+struct DecodeCall {
+  void* out;
+  const void* query;
+  const void* key_cache;
+  const void* value_cache;
+  const int32_t* block_tables;
+  int max_blocks_per_seq;
+  const int32_t* context_lens;
+  int num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks;
+  float scale;
+  pkv_dtype q_dtype, cache_dtype;
+  float k_scale, v_scale;
+  int partition_tokens;
+  const int32_t* partition_offsets;
+  int total_partitions;
+  void* workspace;
+  size_t workspace_bytes;
+};
+
+static int check_decode(const DecodeCall& c, DecodeArgs* a) {
+  if (!c.out || !c.query || !c.key_cache || !c.value_cache || !c.block_tables || !c.context_lens)
+    return fail(PKV_ERR_INVALID, "null pointer argument");
+  if (c.num_seqs < 0 || c.num_q_heads <= 0 || c.num_kv_heads <= 0 || c.max_blocks_per_seq <= 0 ||
+      c.num_blocks <= 0)
+    return fail(PKV_ERR_INVALID, "sizes must be positive");
+  if (c.num_q_heads % c.num_kv_heads != 0)
+    return fail(PKV_ERR_INVALID, "num_q_heads %% num_kv_heads != 0");
+  if (!valid_dtype(c.q_dtype) || !valid_dtype(c.cache_dtype))
+    return fail(PKV_ERR_INVALID, "unknown dtype");
+  if (!std::isfinite(c.scale)) return fail(PKV_ERR_INVALID, "scale must be finite");
+  const int G = c.num_q_heads / c.num_kv_heads;
+  if (!decode_supported(c.q_dtype, c.cache_dtype, c.head_dim, c.block_size, G))
+    return fail(PKV_ERR_UNSUPPORTED, "unsupported (q %d, cache %d, head_dim %d, block_size %d)",
+                (int)c.q_dtype, (int)c.cache_dtype, c.head_dim, c.block_size);
+  const bool fp8 = c.cache_dtype == PKV_FP8_E4M3;
+  if (fp8 && (!(c.k_scale > 0.f) || !(c.v_scale > 0.f) || !std::isfinite(c.k_scale) ||
+              !std::isfinite(c.v_scale)))
+    return fail(PKV_ERR_INVALID, "fp8 scales must be positive and finite");
+  if (c.partition_tokens < 0 || (c.partition_tokens % c.block_size) != 0)
+    return fail(PKV_ERR_INVALID, "partition_tokens must be 0 or a positive multiple of block_size");
+  if (c.partition_tokens > 0) {
+    if (!c.partition_offsets) return fail(PKV_ERR_INVALID, "partition_offsets is null");
+    if (c.total_partitions < c.num_seqs) return fail(PKV_ERR_INVALID, "total_partitions < num_seqs");
+    const size_t need = paged_attention_workspace_bytes(c.total_partitions, c.num_q_heads, c.head_dim);
+    if (!c.workspace || c.workspace_bytes < need)
+      return fail(PKV_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", need, c.workspace_bytes);
+  }
+  if ((size_t)c.num_blocks * c.block_size > (size_t)INT32_MAX)
+    return fail(PKV_ERR_INVALID, "num_blocks * block_size exceeds int32 slots");
+
+  a->out = c.out;
+  a->q = c.query;
+  a->kc = c.key_cache;
+  a->vc = c.value_cache;
+  a->tables = c.block_tables;
+  a->lens = c.context_lens;
+  a->part_off = c.partition_tokens > 0 ? c.partition_offsets : nullptr;
+  a->ws = (float*)c.workspace;
+  a->max_blocks = c.max_blocks_per_seq;
+  a->S = c.num_seqs;
+  a->Hq = c.num_q_heads;
+  a->Hkv = c.num_kv_heads;
+  a->D = c.head_dim;
+  a->BS = c.block_size;
+  a->nb = c.num_blocks;
+  a->partition = c.partition_tokens;
+  a->total_parts = c.partition_tokens > 0 ? c.total_partitions : 0;
+  a->qk_mult = c.scale * (fp8 ? c.k_scale : 1.f) * kLog2eHost;
+  a->v_mult = fp8 ? c.v_scale : 1.f;
+  a->q_dtype = c.q_dtype;
+  a->kv_dtype = c.cache_dtype;
+  return PKV_OK;
+}
+
+}  // namespace pkv
+
+using namespace pkv;
+
+extern "C" {
+
+const char* pkv_last_error(void) { return g_err; }
+
+int pkv_abi_version(void) { return PKV_ABI_VERSION; }
+
+int paged_kv_write(const void* key, const void* value, void* key_cache, void* value_cache,
+                   const int32_t* slot_mapping, int num_tokens, int num_kv_heads, int head_dim,
+                   int block_size, int num_blocks, pkv_dtype src_dtype, pkv_dtype cache_dtype,
+                   float k_scale, float v_scale, void* stream) {
+  if (num_tokens < 0 || num_kv_heads <= 0 || num_blocks <= 0)
+    return fail(PKV_ERR_INVALID, "sizes must be positive");
+  if (num_tokens == 0) return PKV_OK;
+  if (!key || !value || !key_cache || !value_cache || !slot_mapping)
+    return fail(PKV_ERR_INVALID, "null pointer argument");
+  if (!valid_dtype(src_dtype) || !valid_dtype(cache_dtype))
+    return fail(PKV_ERR_INVALID, "unknown dtype");
+  const bool ok = (src_dtype == PKV_F32 && cache_dtype == PKV_F32) ||
+                  (src_dtype == PKV_BF16 && cache_dtype == PKV_BF16) ||
+                  (src_dtype == PKV_BF16 && cache_dtype == PKV_FP8_E4M3);
+  if (!ok) return fail(PKV_ERR_UNSUPPORTED, "unsupported write %d -> %d", (int)src_dtype, (int)cache_dtype);
+  if ((head_dim != 64 && head_dim != 128) || (block_size != 16 && block_size != 32))
+    return fail(PKV_ERR_UNSUPPORTED, "head_dim must be 64/128 and block_size 16/32");
+  if ((size_t)num_blocks * block_size > (size_t)INT32_MAX)
+    return fail(PKV_ERR_INVALID, "num_blocks * block_size exceeds int32 slots");
+  float k_inv = 1.f, v_inv = 1.f;
+  if (cache_dtype == PKV_FP8_E4M3) {
+    if (!(k_scale > 0.f) || !(v_scale > 0.f) || !std::isfinite(k_scale) || !std::isfinite(v_scale))
+      return fail(PKV_ERR_INVALID, "fp8 scales must be positive and finite");
+    k_inv = 1.f / k_scale;  // one correctly rounded fp32 division
+    v_inv = 1.f / v_scale;
+  }
+  return hip_status(launch_kv_write(key, value, key_cache, value_cache, slot_mapping, num_tokens,
+                                    num_kv_heads, head_dim, block_size, num_blocks, src_dtype,
+                                    cache_dtype, k_inv, v_inv, stream),
+                    "paged_kv_write launch");
+}
+
+int paged_attention_partition_offsets(const int32_t* context_lens_host, int num_seqs,
+                                      int partition_tokens, int32_t* offsets_host_out,
+                                      int* total_partitions_out) {
+  if (num_seqs < 0 || partition_tokens <= 0 || !offsets_host_out || (num_seqs > 0 && !context_lens_host))
+    return fail(PKV_ERR_INVALID, "bad arguments");
+  int64_t acc = 0;
+  offsets_host_out[0] = 0;
+  for (int s = 0; s < num_seqs; ++s) {
+    const int64_t L = context_lens_host[s];
+    if (L < 0) return fail(PKV_ERR_INVALID, "negative context length at %d", s);
+    const int64_t n = L == 0 ? 1 : (L + partition_tokens - 1) / partition_tokens;
+    acc += n;
+    if (acc > INT32_MAX) return fail(PKV_ERR_INVALID, "too many partitions");
+    offsets_host_out[s + 1] = (int32_t)acc;
+  }
+  if (total_partitions_out) *total_partitions_out = (int)acc;
+  return PKV_OK;
+}
+
+size_t paged_attention_workspace_bytes(int total_partitions, int num_q_heads, int head_dim) {
+  if (total_partitions <= 0 || num_q_heads <= 0 || head_dim <= 0) return 0;
+  return (size_t)total_partitions * num_q_heads * (head_dim + 2) * sizeof(float);
+}
+
+static int decode_common(const DecodeCall& c, bool reduce, void* stream) {
+  DecodeArgs a;
+  int rc = check_decode(c, &a);
+  if (rc) return rc;
+  if (c.num_seqs == 0) return PKV_OK;
+  rc = hip_status(launch_decode(a, stream), "paged_attention_decode launch");
+  if (rc || !reduce || c.partition_tokens == 0) return rc;
+  return hip_status(launch_splitk_reduce(c.out, a.ws, c.partition_offsets, c.num_seqs,
+                                         c.num_q_heads, c.head_dim, c.total_partitions,
+                                         c.q_dtype, stream),
+                    "paged_attention_splitk_reduce launch");
+}
+
+int paged_attention_decode(void* out, const void* query, const void* key_cache,
+                           const void* value_cache, const int32_t* block_tables,
+                           int max_blocks_per_seq, const int32_t* context_lens, int num_seqs,
+                           int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                           int num_blocks, float scale, pkv_dtype q_dtype, pkv_dtype cache_dtype,
+                           float k_scale, float v_scale, int partition_tokens,
+                           const int32_t* partition_offsets, int total_partitions,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  DecodeCall c{out, query, key_cache, value_cache, block_tables, max_blocks_per_seq, context_lens,
+               num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, scale,
+               q_dtype, cache_dtype, k_scale, v_scale, partition_tokens, partition_offsets,
+               total_partitions, workspace, workspace_bytes};
+  return decode_common(c, true, stream);
+}
+
+int paged_attention_decode_partials(void* out, const void* query, const void* key_cache,
+                                    const void* value_cache, const int32_t* block_tables,
+                                    int max_blocks_per_seq, const int32_t* context_lens,
+                                    int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                                    int block_size, int num_blocks, float scale, pkv_dtype q_dtype,
+                                    pkv_dtype cache_dtype, float k_scale, float v_scale,
+                                    int partition_tokens, const int32_t* partition_offsets,
+                                    int total_partitions, void* workspace, size_t workspace_bytes,
+                                    void* stream) {
+  if (partition_tokens <= 0) return fail(PKV_ERR_INVALID, "partition_tokens must be > 0");
+  DecodeCall c{out, query, key_cache, value_cache, block_tables, max_blocks_per_seq, context_lens,
+               num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, scale,
+               q_dtype, cache_dtype, k_scale, v_scale, partition_tokens, partition_offsets,
+               total_partitions, workspace, workspace_bytes};
+  return decode_common(c, false, stream);
+}
+
+int paged_attention_splitk_reduce(void* out, const void* workspace, size_t workspace_bytes,
+                                  const int32_t* partition_offsets, int num_seqs,
+                                  int num_q_heads, int head_dim, int total_partitions,
+                                  pkv_dtype out_dtype, void* stream) {
+  if (!out || !workspace || !partition_offsets) return fail(PKV_ERR_INVALID, "null pointer argument");
+  if (num_seqs < 0 || num_q_heads <= 0 || total_partitions < num_seqs)
+    return fail(PKV_ERR_INVALID, "bad sizes");
+  if (head_dim != 64 && head_dim != 128) return fail(PKV_ERR_UNSUPPORTED, "head_dim must be 64/128");
+  if (out_dtype != PKV_F32 && out_dtype != PKV_BF16)
+    return fail(PKV_ERR_UNSUPPORTED, "output dtype must be F32 or BF16");
+  const size_t need = paged_attention_workspace_bytes(total_partitions, num_q_heads, head_dim);
+  if (workspace_bytes < need)
+    return fail(PKV_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", need, workspace_bytes);
+  if (num_seqs == 0) return PKV_OK;
+  return hip_status(launch_splitk_reduce(out, (const float*)workspace, partition_offsets, num_seqs,
+                                         num_q_heads, head_dim, total_partitions, out_dtype, stream),
+                    "paged_attention_splitk_reduce launch");
+}
+
+int paged_kv_copy_blocks(void* key_cache, void* value_cache, const int32_t* pairs, int num_pairs,
+                         size_t block_bytes, int num_blocks, void* stream) {
+  if (num_pairs < 0 || num_blocks <= 0) return fail(PKV_ERR_INVALID, "bad sizes");
+  if (num_pairs == 0) return PKV_OK;
+  if (!key_cache || !value_cache || !pairs) return fail(PKV_ERR_INVALID, "null pointer argument");
+  if (block_bytes == 0 || block_bytes % 16 != 0)
+    return fail(PKV_ERR_INVALID, "block_bytes must be a positive multiple of 16");
+  return hip_status(launch_copy_blocks(key_cache, value_cache, pairs, num_pairs, block_bytes,
+                                       num_blocks, stream),
+                    "paged_kv_copy_blocks launch");
+}
+
+int paged_kv_gather(void* k_out, void* v_out, const void* key_cache, const void* value_cache,
+                    const int32_t* block_tables, int max_blocks_per_seq, const int32_t* cu_ctx,
+                    int num_seqs, int total_tokens, int num_kv_heads, int head_dim, int block_size,
+                    int num_blocks, pkv_dtype cache_dtype, void* stream) {
+  if (num_seqs < 0 || total_tokens < 0 || num_kv_heads <= 0 || num_blocks <= 0 ||
+      max_blocks_per_seq <= 0)
+    return fail(PKV_ERR_INVALID, "bad sizes");
+  if (total_tokens == 0 || num_seqs == 0) return PKV_OK;
+  if (!k_out || !v_out || !key_cache || !value_cache || !block_tables || !cu_ctx)
+    return fail(PKV_ERR_INVALID, "null pointer argument");
+  if (!valid_dtype(cache_dtype)) return fail(PKV_ERR_INVALID, "unknown dtype");
+  if ((head_dim != 64 && head_dim != 128) || (block_size != 16 && block_size != 32))
+    return fail(PKV_ERR_UNSUPPORTED, "head_dim must be 64/128 and block_size 16/32");
+  return hip_status(launch_gather(k_out, v_out, key_cache, value_cache, block_tables,
+                                  max_blocks_per_seq, cu_ctx, num_seqs, total_tokens, num_kv_heads,
+                                  head_dim, block_size, num_blocks, cache_dtype, stream),
+                    "paged_kv_gather launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,195 @@
+// Block-pool maintenance kernels: the per-step slot scatter of new key/value
+// rows, whole-block copies for copy-on-write, and a gather of sequences back
+// into dense rows.
+//
+// "Day 6/90 of Inference Engineering" (PagedAttention notes): each decode
+// step writes its token into whichever block the manager handed out, and a
+// prompt that diverges from a shared prefix continues in a fresh block.
+//
+// Pool layout (elements of E bytes, X = 16 / E):
+//   key   [NB][H][D/X][BS][X]    value [NB][H][D][BS]
+
+#include <hip/hip_runtime.h>
+
+#include "pkv_device.h"
+#include "pkv_internal.h"
+
+namespace pkv {
+namespace {
+
+// One thread per (token, kv head, 16-byte key unit of the cache): it writes
+// that key unit and the X value elements of the same dims.
+template <int SRC, int CACHE>
+__global__ __launch_bounds__(256) void kv_write_kernel(const void* __restrict__ key,
+                                                       const void* __restrict__ value,
+                                                       uint8_t* __restrict__ kc,
+                                                       uint8_t* __restrict__ vc,
+                                                       const int32_t* __restrict__ slots, int T,
+                                                       int H, int D, int BS, int nb, float k_inv,
+                                                       float v_inv) {
+  constexpr int E = CACHE == PKV_F32 ? 4 : CACHE == PKV_BF16 ? 2 : 1;
+  constexpr int X = 16 / E;
+  const int units = D / X;
+  const long gid = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= (long)T * H * units) return;
+  const int c = (int)(gid % units);
+  const int h = (int)((gid / units) % H);
+  const int t = (int)(gid / ((long)units * H));
+  const int slot = slots[t];
+  if (slot < 0 || slot >= nb * BS) return;
+  const int b = slot / BS, o = slot % BS;
+  const size_t row = ((size_t)t * H + h) * D + (size_t)c * X;   // first source element
+  const size_t kdst = ((((size_t)b * H + h) * (D / X) + c) * BS + o) * 16;
+  const size_t vdst0 = (((size_t)b * H + h) * D + (size_t)c * X) * BS + o;  // element index
+
+  if constexpr (CACHE == PKV_F32) {
+    const f32x4 k4 = *(const f32x4*)((const float*)key + row);
+    const f32x4 v4 = *(const f32x4*)((const float*)value + row);
+    *(f32x4*)(kc + kdst) = k4;
+    float* vd = (float*)vc + vdst0;
+    vd[0] = v4.x; vd[BS] = v4.y; vd[2 * BS] = v4.z; vd[3 * BS] = v4.w;
+  } else if constexpr (CACHE == PKV_BF16) {
+    const u32x4 k8 = *(const u32x4*)((const uint16_t*)key + row);
+    const u32x4 v8 = *(const u32x4*)((const uint16_t*)value + row);
+    *(u32x4*)(kc + kdst) = k8;
+    uint16_t* vd = (uint16_t*)vc + vdst0;
+    const uint32_t vw[4] = {v8.x, v8.y, v8.z, v8.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      vd[(2 * i) * BS] = (uint16_t)(vw[i] & 0xffffu);
+      vd[(2 * i + 1) * BS] = (uint16_t)(vw[i] >> 16);
+    }
+  } else {  // bf16 -> fp8 E4M3FN, quantise on write
+    const uint16_t* ks = (const uint16_t*)key + row;
+    const uint16_t* vs = (const uint16_t*)value + row;
+    const u32x4 ka = *(const u32x4*)ks, kb = *(const u32x4*)(ks + 8);
+    const u32x4 va = *(const u32x4*)vs, vb = *(const u32x4*)(vs + 8);
+    const uint32_t kw[8] = {ka.x, ka.y, ka.z, ka.w, kb.x, kb.y, kb.z, kb.w};
+    const uint32_t vw[8] = {va.x, va.y, va.z, va.w, vb.x, vb.y, vb.z, vb.w};
+    uint32_t kout[4] = {0, 0, 0, 0};
+    uint8_t* vd = vc + vdst0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t k0 = f32_to_e4m3(bf16_lo(kw[i]) * k_inv);
+      const uint32_t k1 = f32_to_e4m3(bf16_hi(kw[i]) * k_inv);
+      kout[i / 2] |= (k0 | (k1 << 8)) << (16 * (i % 2));
+      vd[(2 * i) * BS] = (uint8_t)f32_to_e4m3(bf16_lo(vw[i]) * v_inv);
+      vd[(2 * i + 1) * BS] = (uint8_t)f32_to_e4m3(bf16_hi(vw[i]) * v_inv);
+    }
+    *(u32x4*)(kc + kdst) = u32x4{kout[0], kout[1], kout[2], kout[3]};
+  }
+}
+
+// One workgroup per (pair, pool): copies block_bytes from block src to dst.
+__global__ __launch_bounds__(256) void copy_blocks_kernel(uint8_t* __restrict__ kc,
+                                                          uint8_t* __restrict__ vc,
+                                                          const int32_t* __restrict__ pairs,
+                                                          size_t block_bytes, int nb) {
+  const int src = pairs[2 * blockIdx.x], dst = pairs[2 * blockIdx.x + 1];
+  if ((unsigned)src >= (unsigned)nb || (unsigned)dst >= (unsigned)nb) return;
+  uint8_t* pool = blockIdx.y == 0 ? kc : vc;
+  const u32x4* s = (const u32x4*)(pool + (size_t)src * block_bytes);
+  u32x4* d = (u32x4*)(pool + (size_t)dst * block_bytes);
+  const size_t n = block_bytes / 16;
+  for (size_t i = threadIdx.x; i < n; i += 256) d[i] = s[i];
+}
+
+// One thread per (output row, kv head, 16-byte unit of the dense row).
+template <int CACHE>
+__global__ __launch_bounds__(256) void gather_kernel(uint8_t* __restrict__ k_out,
+                                                     uint8_t* __restrict__ v_out,
+                                                     const uint8_t* __restrict__ kc,
+                                                     const uint8_t* __restrict__ vc,
+                                                     const int32_t* __restrict__ tables,
+                                                     int max_blocks,
+                                                     const int32_t* __restrict__ cu_ctx, int S,
+                                                     int T, int H, int D, int BS, int nb) {
+  constexpr int E = CACHE == PKV_F32 ? 4 : CACHE == PKV_BF16 ? 2 : 1;
+  constexpr int X = 16 / E;
+  const int units = D / X;
+  const long gid = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= (long)T * H * units) return;
+  const int c = (int)(gid % units);
+  const int h = (int)((gid / units) % H);
+  const int r = (int)(gid / ((long)units * H));
+  int lo = 0, hi = S;  // largest s with cu_ctx[s] <= r
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) / 2;
+    if (cu_ctx[mid] <= r) lo = mid; else hi = mid;
+  }
+  const int s = lo, t = r - cu_ctx[s];
+  const int jb = t / BS, o = t % BS;
+  const size_t dst = (((size_t)r * H + h) * D + (size_t)c * X) * E;
+  u32x4 kz = {0, 0, 0, 0}, vz = {0, 0, 0, 0};
+  const int b = jb < max_blocks ? tables[(size_t)s * max_blocks + jb] : -1;
+  if ((unsigned)b < (unsigned)nb) {
+    kz = *(const u32x4*)(kc + ((((size_t)b * H + h) * (D / X) + c) * BS + o) * 16);
+    const size_t v0 = (((size_t)b * H + h) * D + (size_t)c * X) * BS + o;  // element index
+    uint32_t wv[4] = {0, 0, 0, 0};
+#pragma unroll
+    for (int i = 0; i < X; ++i) {
+      uint32_t e;
+      if constexpr (E == 4) e = ((const uint32_t*)vc)[v0 + (size_t)i * BS];
+      else if constexpr (E == 2) e = ((const uint16_t*)vc)[v0 + (size_t)i * BS];
+      else e = vc[v0 + (size_t)i * BS];
+      wv[(i * E) / 4] |= e << (8 * ((i * E) % 4));
+    }
+    vz = u32x4{wv[0], wv[1], wv[2], wv[3]};
+  }
+  *(u32x4*)(k_out + dst) = kz;
+  *(u32x4*)(v_out + dst) = vz;
+}
+
+}  // namespace
+
+int launch_kv_write(const void* key, const void* value, void* kc, void* vc, const int32_t* slots,
+                    int T, int H, int D, int BS, int nb, pkv_dtype src, pkv_dtype cache,
+                    float k_inv, float v_inv, void* stream) {
+  hipStream_t st = (hipStream_t)stream;
+  const int X = 16 / elem_bytes(cache);
+  const long n = (long)T * H * (D / X);
+  if (n == 0) return 0;
+  dim3 grid((unsigned)((n + 255) / 256)), block(256);
+  if (cache == PKV_F32)
+    hipLaunchKernelGGL((kv_write_kernel<PKV_F32, PKV_F32>), grid, block, 0, st, key, value,
+                       (uint8_t*)kc, (uint8_t*)vc, slots, T, H, D, BS, nb, k_inv, v_inv);
+  else if (cache == PKV_BF16)
+    hipLaunchKernelGGL((kv_write_kernel<PKV_BF16, PKV_BF16>), grid, block, 0, st, key, value,
+                       (uint8_t*)kc, (uint8_t*)vc, slots, T, H, D, BS, nb, k_inv, v_inv);
+  else
+    hipLaunchKernelGGL((kv_write_kernel<PKV_BF16, PKV_FP8_E4M3>), grid, block, 0, st, key, value,
+                       (uint8_t*)kc, (uint8_t*)vc, slots, T, H, D, BS, nb, k_inv, v_inv);
+  return (int)hipGetLastError();
+}
+
+int launch_copy_blocks(void* kc, void* vc, const int32_t* pairs, int n, size_t block_bytes, int nb,
+                       void* stream) {
+  if (n == 0) return 0;
+  hipLaunchKernelGGL(copy_blocks_kernel, dim3(n, 2), dim3(256), 0, (hipStream_t)stream,
+                     (uint8_t*)kc, (uint8_t*)vc, pairs, block_bytes, nb);
+  return (int)hipGetLastError();
+}
+
+int launch_gather(void* k_out, void* v_out, const void* kc, const void* vc, const int32_t* tables,
+                  int max_blocks, const int32_t* cu_ctx, int S, int T, int H, int D, int BS,
+                  int nb, pkv_dtype cache, void* stream) {
+  const int X = 16 / elem_bytes(cache);
+  const long n = (long)T * H * (D / X);
+  if (n == 0) return 0;
+  dim3 grid((unsigned)((n + 255) / 256)), block(256);
+  hipStream_t st = (hipStream_t)stream;
+  auto ko = (uint8_t*)k_out, vo = (uint8_t*)v_out;
+  auto kcc = (const uint8_t*)kc, vcc = (const uint8_t*)vc;
+  if (cache == PKV_F32)
+    hipLaunchKernelGGL((gather_kernel<PKV_F32>), grid, block, 0, st, ko, vo, kcc, vcc, tables,
+                       max_blocks, cu_ctx, S, T, H, D, BS, nb);
+  else if (cache == PKV_BF16)
+    hipLaunchKernelGGL((gather_kernel<PKV_BF16>), grid, block, 0, st, ko, vo, kcc, vcc, tables,
+                       max_blocks, cu_ctx, S, T, H, D, BS, nb);
+  else
+    hipLaunchKernelGGL((gather_kernel<PKV_FP8_E4M3>), grid, block, 0, st, ko, vo, kcc, vcc, tables,
+                       max_blocks, cu_ctx, S, T, H, D, BS, nb);
+  return (int)hipGetLastError();
+}
+
+}  // namespace pkv

@@ -1,0 +1,92 @@
+// Device-side helpers for gfx950 (CDNA4, wave64): element conversions and
+// cross-lane reductions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pkv {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+// fp32 -> bf16 bits, round to nearest even; NaN stays a (quiet) NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// Two bf16 from two fp32, packed low = a, high = b (round to nearest even).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16);
+}
+
+// sum of the two bf16 products of a and b, plus c, in fp32 (v_dot2_f32_bf16).
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a),
+                                         __builtin_bit_cast(bf16x2, b), c, false);
+}
+
+// Two E4M3FN codes (bytes 0,1, or 2,3 when HIGH) of w -> two fp32, exact
+// (v_cvt_pk_f32_fp8).
+template <bool HIGH>
+__device__ __forceinline__ f32x2 fp8x2_to_f32(uint32_t w) {
+  return __builtin_amdgcn_cvt_pk_f32_fp8(w, HIGH);
+}
+
+// fp32 -> OCP E4M3FN code: round to nearest, ties to even; |y| >= 448
+// saturates to 448; NaN -> 0x7F.  Bit-level, independent of any hardware
+// conversion mode.
+__device__ __forceinline__ uint32_t f32_to_e4m3(float y) {
+  const uint32_t u = __float_as_uint(y);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t a = u & 0x7fffffffu;
+  if (a > 0x7f800000u) return 0x7fu;              // NaN
+  if (a >= 0x43e00000u) return sign | 0x7eu;      // >= 448 (also inf)
+  if (a >= 0x3c800000u) {                         // >= 2^-6: normal in E4M3
+    const uint32_t r = a + 0x7ffffu + ((a >> 20) & 1u);  // RNE at mantissa bit 20
+    return sign | ((((r >> 23) - 120u) << 3) | ((r >> 20) & 7u));
+  }
+  // subnormal range: the code is round(|y| * 2^9) (k = 8 is the smallest normal)
+  const float k = __builtin_rintf(__uint_as_float(a) * 512.0f);
+  return sign | (uint32_t)k;
+}
+
+// ---- cross-lane helpers (wave64) -------------------------------------------
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xf,
+                                                            0xf, false));
+}
+// DPP controls: quad_perm(1,0,3,2) = 0xB1, quad_perm(2,3,0,1) = 0x4E,
+// row_ror:4 = 0x124, row_ror:8 = 0x128.
+
+// Reductions within each row of 16 lanes (every lane gets the row result).
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, dpp<0xB1>(v));
+  v = fmaxf(v, dpp<0x4E>(v));
+  v = fmaxf(v, dpp<0x124>(v));
+  v = fmaxf(v, dpp<0x128>(v));
+  return v;
+}
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp<0xB1>(v);
+  v += dpp<0x4E>(v);
+  v += dpp<0x124>(v);
+  v += dpp<0x128>(v);
+  return v;
+}
+
+__device__ __forceinline__ float xor_lanes(float v, int mask) { return __shfl_xor(v, mask, 64); }
+
+}  // namespace pkv

@@ -1,0 +1,53 @@
+// Internal declarations shared by the host-side translation units of libpkv.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+
+#include "pkv.h"
+
+namespace pkv {
+
+// Records a thread-local error message and returns `code`.
+int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+void clear_error();
+
+constexpr float kLog2eHost = 1.4426950408889634f;
+
+inline int elem_bytes(pkv_dtype t) { return t == PKV_F32 ? 4 : t == PKV_BF16 ? 2 : 1; }
+
+// Everything the decode kernels need, resolved on the host.
+struct DecodeArgs {
+  void* out;
+  const void* q;
+  const void* kc;
+  const void* vc;
+  const int32_t* tables;
+  const int32_t* lens;
+  const int32_t* part_off;  // null in one-pass mode
+  float* ws;                // partial outputs [total_parts][Hq][D] then (m, l) [total_parts][Hq][2]
+  int max_blocks;
+  int S, Hq, Hkv, D, BS, nb;
+  int partition;            // tokens; 0 = one pass
+  int total_parts;
+  float qk_mult;            // scale * k_scale * log2(e): scores in the log2 domain
+  float v_mult;             // v_scale for fp8, else 1
+  pkv_dtype q_dtype, kv_dtype;
+};
+
+// Kernel launchers (decode.hip, kv_ops.hip).  Return hipError_t as int.
+int launch_decode(const DecodeArgs& a, void* stream);
+int launch_splitk_reduce(void* out, const float* ws, const int32_t* part_off, int S, int Hq, int D,
+                         int total_parts, pkv_dtype out_dtype, void* stream);
+bool decode_supported(pkv_dtype q, pkv_dtype kv, int D, int BS, int G);
+
+int launch_kv_write(const void* key, const void* value, void* kc, void* vc, const int32_t* slots,
+                    int T, int H, int D, int BS, int nb, pkv_dtype src, pkv_dtype cache,
+                    float k_inv, float v_inv, void* stream);
+int launch_copy_blocks(void* kc, void* vc, const int32_t* pairs, int n, size_t block_bytes,
+                       int nb, void* stream);
+int launch_gather(void* k_out, void* v_out, const void* kc, const void* vc, const int32_t* tables,
+                  int max_blocks, const int32_t* cu_ctx, int S, int T, int H, int D, int BS,
+                  int nb, pkv_dtype cache, void* stream);
+
+}  // namespace pkv

@@ -1,0 +1,114 @@
+"""A small paged KV cache manager built on libpkv: block pools on the device,
+the library's host block allocator, and the C ABI's write / copy / decode
+calls.  No arithmetic of the method happens here; it orders the calls.
+
+"Day 6/90 of Inference Engineering" (PagedAttention notes): the manager hands
+out blocks as tokens arrive, shares prefix blocks between prompts, and keeps
+one block table per sequence.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from . import (BlockAllocator, empty_pools, paged_attention_decode, paged_attention_partition_offsets,
+               paged_attention_workspace_bytes, paged_kv_copy_blocks, paged_kv_write)
+
+
+class PagedKVCache:
+    def __init__(self, num_blocks: int, num_kv_heads: int, head_dim: int, block_size: int,
+                 dtype: torch.dtype, device="cuda", free_order=None, k_scale=1.0, v_scale=1.0,
+                 fill_byte: int | None = None):
+        self.num_blocks, self.H, self.D, self.bs = num_blocks, num_kv_heads, head_dim, block_size
+        self.dtype, self.device = dtype, torch.device(device)
+        self.k_scale, self.v_scale = float(k_scale), float(v_scale)
+        self.alloc = BlockAllocator(num_blocks, block_size, free_order)
+        self.key_cache, self.value_cache = empty_pools(num_blocks, num_kv_heads, head_dim,
+                                                       block_size, dtype, device)
+        if fill_byte is not None:
+            self.key_cache.view(torch.uint8).fill_(fill_byte)
+            self.value_cache.view(torch.uint8).fill_(fill_byte)
+        self._ws = None
+
+    # -- allocation and writes ------------------------------------------------
+    def add_seq(self, seq: int):
+        self.alloc.add_seq(seq)
+
+    def fork(self, parent: int, child: int):
+        self.alloc.fork(parent, child)
+
+    def append_many(self, items, stream=None):
+        """items: [(seq, key [n, H, D], value [n, H, D]), ...] (device tensors).
+
+        Allocates every token on the host, applies the copy-on-write block
+        copies, then scatters all rows with one write.  Returns the slot
+        mapping (numpy int32) in item order.
+        """
+        slots, cows, keys, vals = [], [], [], []
+        for seq, k, v in items:
+            s, c = self.alloc.append(seq, int(k.shape[0]))
+            slots.append(s)
+            if len(c):
+                cows.append(c)
+            if k.shape[0]:
+                keys.append(k)
+                vals.append(v)
+        if cows:
+            pairs = torch.from_numpy(np.concatenate(cows).astype(np.int32)).to(self.device)
+            paged_kv_copy_blocks(self.key_cache, self.value_cache, pairs, stream=stream)
+        sl = np.concatenate(slots).astype(np.int32) if slots else np.zeros(0, np.int32)
+        if keys:
+            K = torch.cat(keys) if len(keys) > 1 else keys[0]
+            V = torch.cat(vals) if len(vals) > 1 else vals[0]
+            self.write(K.contiguous(), V.contiguous(), torch.from_numpy(sl).to(self.device), stream)
+        return sl
+
+    def write(self, key, value, slot_mapping, stream=None):
+        paged_kv_write(key, value, self.key_cache, self.value_cache, slot_mapping,
+                       k_scale=self.k_scale, v_scale=self.v_scale, stream=stream)
+
+    # -- tables -----------------------------------------------------------------
+    def seq_lens(self, seqs) -> np.ndarray:
+        return np.array([self.alloc.seq_len(s) for s in seqs], dtype=np.int32)
+
+    def block_tables(self, seqs, width: int | None = None):
+        lens = self.seq_lens(seqs)
+        w = width or max(1, int(-(-lens.max() // self.bs)) if len(lens) else 1)
+        t = self.alloc.fill_tables(seqs, w, pad=-1)
+        return torch.from_numpy(t).to(self.device)
+
+    # -- decode -------------------------------------------------------------------
+    def decode_inputs(self, seqs, partition_tokens: int = 0):
+        """Device tables, lengths and split-K metadata for a decode over seqs."""
+        lens = self.seq_lens(seqs)
+        inp = {"block_tables": self.block_tables(seqs),
+               "context_lens": torch.from_numpy(lens).to(self.device),
+               "partition_tokens": int(partition_tokens), "partition_offsets": None,
+               "total_partitions": 0, "lens_host": lens}
+        if partition_tokens:
+            off, tot = paged_attention_partition_offsets(lens, partition_tokens)
+            inp["partition_offsets"] = torch.from_numpy(off).to(self.device)
+            inp["total_partitions"] = tot
+        return inp
+
+    def workspace(self, total_partitions, num_q_heads, head_dim):
+        """Device scratch for split-K partials (grown on demand, reused)."""
+        need = paged_attention_workspace_bytes(total_partitions, num_q_heads, head_dim)
+        if self._ws is None or self._ws.numel() < need:
+            self._ws = torch.empty(max(need, 16), dtype=torch.uint8, device=self.device)
+        return self._ws
+
+    def decode(self, query, inp, scale, out=None, stream=None):
+        S, Hq, D = query.shape
+        out = torch.empty_like(query) if out is None else out
+        ws = None
+        if inp["partition_tokens"]:
+            ws = self.workspace(inp["total_partitions"], Hq, D)
+        paged_attention_decode(out, query, self.key_cache, self.value_cache, inp["block_tables"],
+                               inp["context_lens"], scale, k_scale=self.k_scale,
+                               v_scale=self.v_scale, partition_tokens=inp["partition_tokens"],
+                               partition_offsets=inp["partition_offsets"],
+                               total_partitions=inp["total_partitions"], workspace=ws,
+                               stream=stream)
+        return out
