@@ -1,0 +1,309 @@
+#!/usr/bin/env python3
+"""PagedAttention decode benchmark on one MI355X.
+
+One step = the decode step of the hot path over one batch: scatter of each
+sequence's new key/value token into its slot (paged_kv_write), the split-K
+decode kernel (paged_attention_decode_partials) and the split-K reduce.  The
+KV cache is prefilled once through the same library; R copies of the pools
+("layers", at least two and at least 2 GB of cache) are cycled so that each
+step reads its KV from HBM, not from the 256 MB Infinity Cache.
+
+Prints ONE JSON line on stdout; details go to stderr.
+
+    python bench.py [--steps K] [--warmup W] [--config 3] [--gpus 1]
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "paged-attn decode µs/step + effective KV GB/s as % of MI355X HBM peak"
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, vendor figure
+ELEM = {"f32": 4, "bf16": 2, "fp8": 1}
+DECODE_SRC = os.path.join(ROOT, "paged_kv_cache_211_amd", "csrc", "decode.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--config", type=int, default=3, help="workload 1..5 (3 = bf16 GQA)")
+    p.add_argument("--partition", type=int, default=None, help="split-K tokens (default: workload's)")
+    p.add_argument("--layers", type=int, default=0, help="pool copies cycled per step (0 = auto)")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-tokens", type=int, default=400_000,
+                   help="token budget of the oracle's timed sample")
+    p.add_argument("--traffic-file", default=None)
+    return p.parse_args()
+
+
+def algorithmic_bytes(wl):
+    c = wl.cfg
+    L = wl.context_lens
+    e, eq = ELEM[c.kv_dtype], ELEM[c.q_dtype]
+    kv = int(L.sum()) * c.H_kv * c.d * 2 * e
+    q = c.S * c.H_q * c.d * eq
+    o = q
+    tbl = int(((L + c.bs - 1) // c.bs).sum()) * 4 + c.S * 4
+    write = c.S * c.H_kv * c.d * 2 * (ELEM[c.src_dtype] + e)
+    return {"kv": kv, "q": q, "o": o, "tables": tbl, "write": write,
+            "decode": kv + q + o + tbl, "step": kv + q + o + tbl + write}
+
+
+def src_sha():
+    h = hashlib.sha256()
+    for f in ("decode.hip", "pkv_device.h"):
+        with open(os.path.join(ROOT, "paged_kv_cache_211_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(path, workload_key, per_launch_alg):
+    """HBM bytes per decode launch from committed rocprofv3 counter runs, or
+    None when absent or taken on a different kernel source."""
+    path = path or os.path.join(ROOT, "profiles", f"traffic_{workload_key}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_src_sha") != src_sha():
+        log(f"traffic file {path} is for another kernel source; traffic = null")
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(wl, token_budget):
+    """Time the oracle (fp64 numpy) on a bounded sample of the same step."""
+    import numpy as np
+
+    from oracle import attention as OA
+    from oracle.layout import write_kv
+    from oracle.replay import OracleState
+
+    c = wl.cfg
+    order = np.random.default_rng([c.seed, 9]).permutation(c.S)
+    sample, tok = [], 0
+    for s in order:
+        if sample and tok + int(wl.context_lens[s]) > token_budget:
+            continue
+        sample.append(int(s))
+        tok += int(wl.context_lens[s])
+    sample.sort()
+    st = OracleState(wl, only_seqs=sample)
+    st.run(wl, wl.prefill)
+    dec = st.run(wl, wl.decode)
+    slots = np.concatenate(dec)
+    ks, vs = zip(*(wl.values(op[3], op[4], 1) for op in wl.decode))
+    K, V = np.concatenate(ks)[sample], np.concatenate(vs)[sample]
+    tables = st.tables(c.S)
+    threads = None
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((i.get("num_threads") or 1) for i in threadpool_info()) if threadpool_info() else 1
+    except Exception:
+        threads = int(os.environ.get("OMP_NUM_THREADS", "1"))
+    t0 = time.perf_counter()
+    write_kv(st.kc, st.vc, K, V, slots[sample], bs=c.bs, src_dtype=c.src_dtype,
+             cache_dtype=c.kv_dtype, k_scale=c.k_scale, v_scale=c.v_scale)
+    OA.paged_decode(wl.q, c.q_dtype, st.kc, st.vc, tables, wl.context_lens, bs=c.bs,
+                    cache_dtype=c.kv_dtype, scale=c.scale, k_scale=c.k_scale, v_scale=c.v_scale,
+                    seqs=sample)
+    dt = time.perf_counter() - t0
+    frac = tok / wl.total_tokens
+    cpu_model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu_model = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), "")
+    except OSError:
+        pass
+    return {"value": round(dt / frac * 1e6, 1), "unit": "us/step", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{len(sample)} of {c.S} sequences, {tok} of {wl.total_tokens} context tokens "
+                      f"({100 * frac:.1f}%), timed {dt:.2f} s, scaled by tokens",
+            "host_cpus": os.cpu_count(), "affinity_cpus": len(os.sched_getaffinity(0)),
+            "cpu_model": cpu_model}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}, "
+              f"WORLD_SIZE {world}); paged decode shards by sequence or kv head with no "
+              "exchange, so per-GPU throughput is the one-GPU figure.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import synth
+    import paged_kv_cache_211_amd as pkv
+    from paged_kv_cache_211_amd import workload as W
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    wl = synth.make(args.config)
+    wl.cache_limit = 0 if not args.no_cpu_baseline else 4
+    c = wl.cfg
+    P = c.partition if args.partition is None else args.partition
+    ab = algorithmic_bytes(wl)
+    log(f"[bench] workload {c.key}: S={c.S} H_q={c.H_q} H_kv={c.H_kv} d={c.d} bs={c.bs} "
+        f"kv={c.kv_dtype} tokens={wl.total_tokens} blocks={wl.num_blocks} partition={P}")
+
+    t0 = time.perf_counter()
+    cache, step = W.build(wl, poison=False, device=dev)
+    torch.cuda.synchronize()
+    log(f"[bench] prefill through the library: {time.perf_counter() - t0:.1f} s")
+
+    pool_bytes = (cache.key_cache.numel() * cache.key_cache.element_size()) * 2
+    R = args.layers or max(2, math.ceil(2e9 / max(ab["kv"], 1)))
+    layers = [(cache.key_cache, cache.value_cache)]
+    for _ in range(R - 1):
+        layers.append((cache.key_cache.clone(), cache.value_cache.clone()))
+    log(f"[bench] {R} pool layers of {pool_bytes / 1e9:.2f} GB")
+
+    inp = cache.decode_inputs(range(c.S), P)
+    q, key, value, slots = step["query"], step["key"], step["value"], step["slots_dev"]
+    out = torch.empty_like(q)
+    ws = cache.workspace(inp["total_partitions"], c.H_q, c.d) if P else None
+    tab, lens = inp["block_tables"], inp["context_lens"]
+
+    def run(i, ev=None):
+        kc, vc = layers[i % R]
+        if ev:
+            ev[0].record()
+        pkv.paged_kv_write(key, value, kc, vc, slots, k_scale=c.k_scale, v_scale=c.v_scale)
+        if ev:
+            ev[1].record()
+        if P:
+            pkv.paged_attention_decode_partials(out, q, kc, vc, tab, lens, c.scale, c.k_scale,
+                                                c.v_scale, P, inp["partition_offsets"],
+                                                inp["total_partitions"], ws)
+            if ev:
+                ev[2].record()
+            pkv.paged_attention_splitk_reduce(out, ws, inp["partition_offsets"],
+                                              inp["total_partitions"])
+        else:
+            pkv.paged_attention_decode(out, q, kc, vc, tab, lens, c.scale, c.k_scale, c.v_scale)
+            if ev:
+                ev[2].record()
+        if ev:
+            ev[3].record()
+
+    # streaming-copy reference (also the known-size kernel for counter scaling)
+    copy_n = 1 << 30
+    src_b = torch.empty(copy_n, dtype=torch.uint8, device=dev)
+    dst_b = torch.empty_like(src_b)
+    dst_b.copy_(src_b)
+    torch.cuda.synchronize()
+    ce0, ce1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ce0.record()
+    for _ in range(5):
+        dst_b.copy_(src_b)
+    ce1.record()
+    torch.cuda.synchronize()
+    copy_gbps = 2 * copy_n * 5 / (ce0.elapsed_time(ce1) * 1e-3) / 1e9
+    del src_b, dst_b
+
+    for i in range(args.warmup):
+        run(i)
+    torch.cuda.synchronize()
+
+    # region 1: the headline, K whole steps bracketed by events
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    e0.record()
+    for i in range(args.steps):
+        run(i)
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms_step = e0.elapsed_time(e1) / args.steps
+
+    # region 2: the same K steps with an event around every kernel launch
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        run(i, evs[i])
+    torch.cuda.synchronize()
+    t_write = np.array([a.elapsed_time(b) for a, b, _, _ in evs]) * 1e3
+    t_dec = np.array([b.elapsed_time(c2) for _, b, c2, _ in evs]) * 1e3
+    t_red = np.array([c2.elapsed_time(d) for _, _, c2, d in evs]) * 1e3
+    dec_us = float(np.mean(t_dec))
+
+    us_step = ms_step * 1e3
+    kv_gbps = ab["kv"] / (us_step * 1e-6) / 1e9
+    achieved = ab["decode"] / (dec_us * 1e-6) / 1e9
+    traffic = load_traffic(args.traffic_file, c.key, ab["decode"])
+    log(f"[bench] step {us_step:.1f} us (wall {wall / args.steps * 1e6:.1f} us); per kernel: "
+        f"write {np.mean(t_write):.1f} us, decode {dec_us:.1f} us "
+        f"[p10 {np.percentile(t_dec, 10):.1f}, p90 {np.percentile(t_dec, 90):.1f}], "
+        f"reduce {np.mean(t_red):.1f} us")
+    log(f"[bench] KV {ab['kv'] / 1e9:.3f} GB/step -> {kv_gbps:.0f} GB/s = "
+        f"{100 * kv_gbps / HBM_PEAK_GBPS:.1f}% of {HBM_PEAK_GBPS:.0f}; decode kernel "
+        f"{achieved:.0f} GB/s; device copy {copy_gbps:.0f} GB/s")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] timing the oracle on a bounded sample ...")
+        cpu = cpu_baseline(wl, args.cpu_tokens)
+        log(f"[bench] oracle: {cpu['value']} us/step est. ({cpu['sample']})")
+
+    dtype = {"f32": "f32", "bf16": "bf16", "fp8": "fp8-kv/bf16-q"}[c.kv_dtype]
+    line = {
+        "metric": METRIC,
+        "value": round(us_step, 2),
+        "unit": "us/step",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": f"{c.key}: {c.S} seqs, {c.H_q}/{c.H_kv} heads, head_dim {c.d}, "
+                        f"block_size {c.bs}, {c.kv_dtype} KV, context {wl.total_tokens} tokens "
+                        f"(seed {c.seed}), split-K {P}, {R} pool layers",
+            "global_batch": c.S,
+            "seq_len": int(wl.context_lens.max()),
+            "mean_context": round(float(wl.context_lens.mean()), 1),
+            "parallelism": "single GPU",
+        },
+        "kv_GBps": round(kv_gbps, 1),
+        "pct_hbm_peak": round(100 * kv_gbps / HBM_PEAK_GBPS, 2),
+        "step_algorithmic_bytes": ab["step"],
+        "kernel_us": {"paged_kv_write": round(float(np.mean(t_write)), 2),
+                      "decode": round(dec_us, 2), "splitk_reduce": round(float(np.mean(t_red)), 2)},
+        "device_copy_GBps": round(copy_gbps, 1),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": traffic, "kernel": "decode (split-K partials)",
+                     "algorithmic_bytes_per_launch": ab["decode"]},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

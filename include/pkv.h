@@ -196,6 +196,15 @@ int paged_kv_gather(void* k_out, void* v_out, const void* key_cache, const void*
                     int num_seqs, int total_tokens, int num_kv_heads, int head_dim, int block_size,
                     int num_blocks, pkv_dtype cache_dtype, void* stream);
 
+/* pkv_hbm_read_probe -- measurement aid: `workgroups` workgroups of 256
+ * lanes stream-read `bytes` (rounded down to 16) of device memory at
+ * `buffer` with 16-byte loads, eight in flight per lane, and store at most
+ * one word to device `sink` (4 bytes).  Timing it gives the attainable HBM
+ * read rate, the ceiling for the decode kernel's key/value stream (an HBM
+ * bound kernel is judged by bytes moved, "Memory Systems" notes, core idea
+ * 1). */
+int pkv_hbm_read_probe(const void* buffer, size_t bytes, void* sink, int workgroups, void* stream);
+
 /* ---------------------------------------------------------------------------
  * Host block allocator ("Day 6/90 of Inference Engineering", PagedAttention
  * notes): hands out one block at a time, takes a new block only when the

@@ -27,7 +27,7 @@ __all__ = [
     "PkvError", "paged_kv_write", "paged_attention_decode", "paged_attention_decode_partials",
     "paged_attention_splitk_reduce", "paged_kv_copy_blocks", "paged_kv_gather",
     "paged_attention_partition_offsets", "paged_attention_workspace_bytes", "BlockAllocator",
-    "empty_pools", "cache_dtype_code",
+    "empty_pools", "cache_dtype_code", "pkv_hbm_read_probe",
 ]
 
 lib()  # fail at import if the library is missing or incomplete
@@ -195,6 +195,14 @@ def paged_kv_gather(k_out, v_out, key_cache, value_cache, block_tables, cu_ctx, 
                                 _ptr(block_tables), block_tables.shape[1], _ptr(cu_ctx), S,
                                 int(total_tokens), H, D, bs, nb, cache_dtype_code(key_cache),
                                 _stream(stream)))
+
+
+def pkv_hbm_read_probe(buffer: torch.Tensor, sink: torch.Tensor, workgroups: int, stream=None):
+    """Stream-read the whole of `buffer` (device); see include/pkv.h."""
+    _need(buffer, "buffer")
+    _need(sink, "sink")
+    check(lib().pkv_hbm_read_probe(_ptr(buffer), buffer.numel() * buffer.element_size(),
+                                   _ptr(sink), int(workgroups), _stream(stream)))
 
 
 class BlockAllocator:

@@ -1,6 +1,6 @@
 """Build libpkv.so in-tree with hipcc for gfx950.
 
-    python -m paged_kv_cache_211_amd.build          # or __graft_entry__.build()
+    python paged_kv_cache_211_amd/build.py          # or __graft_entry__.build()
 
 Every HIP source is compiled with packed fp32 instructions disabled
 (``-Xclang -target-feature -Xclang -packed-fp32-ops``); the host compiler

@@ -270,4 +270,12 @@ int paged_kv_gather(void* k_out, void* v_out, const void* key_cache, const void*
                     "paged_kv_gather launch");
 }
 
+int pkv_hbm_read_probe(const void* buffer, size_t bytes, void* sink, int workgroups,
+                       void* stream) {
+  if (!buffer || !sink || bytes < 16 || workgroups <= 0)
+    return fail(PKV_ERR_INVALID, "bad arguments");
+  return hip_status(launch_read_probe(buffer, bytes, sink, workgroups, stream),
+                    "pkv_hbm_read_probe launch");
+}
+
 }  // extern "C"

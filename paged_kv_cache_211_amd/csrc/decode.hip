@@ -34,6 +34,17 @@
 #include "pkv_device.h"
 #include "pkv_internal.h"
 
+// Launch shape (fixed at build time; -D overrides exist for tuning sweeps).
+#ifndef PKV_DECODE_WAVES
+#define PKV_DECODE_WAVES 4
+#endif
+#ifndef PKV_DECODE_NT
+#define PKV_DECODE_NT 1
+#endif
+#ifndef PKV_DECODE_DEPTH
+#define PKV_DECODE_DEPTH 1
+#endif
+
 namespace pkv {
 namespace {
 
@@ -84,20 +95,35 @@ __device__ __forceinline__ void unpack_pairs(const u32x4 r, uint32_t* p) {
   }
 }
 
+// One 16-byte load of streamed key/value data.
+__device__ __forceinline__ u32x4 load16(const uint8_t* p) {
+#if PKV_DECODE_NT
+  return __builtin_nontemporal_load((const u32x4*)p);
+#else
+  return *(const u32x4*)p;
+#endif
+}
+
 template <int BS>
 __device__ __forceinline__ float tile_max(float v) {
   v = row16_max(v);
-  if constexpr (BS == 32) v = fmaxf(v, xor_lanes(v, 16));
+  if constexpr (BS == 32) v = max_xor16(v);
   return v;
 }
 template <int BS>
 __device__ __forceinline__ float tile_sum(float v) {
   v = row16_sum(v);
-  if constexpr (BS == 32) v += xor_lanes(v, 16);
+  if constexpr (BS == 32) v = sum_xor16(v);
   return v;
 }
+// Sum over the 64/BS lanes that hold the same key token (lanes l, l^BS, ...).
+template <int BS>
+__device__ __forceinline__ float token_sum(float v) {
+  if constexpr (BS == 16) v = sum_xor16(v);
+  return sum_xor32(v);
+}
 
-template <int KV, int D, int BS, int HPW, int NW, bool SPLIT>
+template <int KV, int D, int BS, int HPW, int NW, int NBUF, bool SPLIT>
 __global__ __launch_bounds__(NW * 64) void decode_kernel(const DecodeArgs a) {
   using Gm = Geo<KV, D, BS>;
   constexpr int X = Gm::X, NLOAD = Gm::NLOAD, KL = Gm::KL, RU = Gm::RU, DPI = Gm::DPI;
@@ -178,25 +204,22 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const DecodeArgs a) {
   const int tk = lane % BS;              // this lane's token in a key tile
   const int tv0 = (lane % RU) * X;       // first of this lane's X tokens in a value tile
 
-  int j = t0 / BS + w;
-  u32x4 kr[NLOAD], vr[NLOAD];
+  // tbl_v: block-table entries of the current chunk of this wave's tiles
+  // (lane i holds the entry of the chunk's i-th tile), read with v_readlane.
+  int tbl_v = 0, chunk0 = 0;
   auto load_tile = [&](int jj, u32x4* kdst, u32x4* vdst) {
-    int b = tbl[jj];
+    int b = __builtin_amdgcn_readlane(tbl_v, (jj - chunk0) / NW);
     if ((unsigned)b >= (unsigned)a.nb) { bad = true; b = 0; }
     const uint8_t* kt = kc + (size_t)b * blk_stride + head_off + lane * 16;
     const uint8_t* vt = vc + (size_t)b * blk_stride + head_off + lane * 16;
 #pragma unroll
-    for (int l = 0; l < NLOAD; ++l) kdst[l] = *(const u32x4*)(kt + l * 1024);
+    for (int l = 0; l < NLOAD; ++l) kdst[l] = load16(kt + l * 1024);
 #pragma unroll
-    for (int l = 0; l < NLOAD; ++l) vdst[l] = *(const u32x4*)(vt + l * 1024);
+    for (int l = 0; l < NLOAD; ++l) vdst[l] = load16(vt + l * 1024);
   };
-  if (j < jend) load_tile(j, kr, vr);
 
-  for (; j < jend; j += NW) {
-    u32x4 kn[NLOAD], vn[NLOAD];
-    const int jn = j + NW;
-    if (jn < jend) load_tile(jn, kn, vn);
-
+  // One tile: QK^T for this lane's token, online softmax, PV.
+  auto process = [&](int j, const u32x4* kr, const u32x4* vr) {
     // ---- QK^T for this lane's token, HPW heads ----
     float sc[HPW];
 #pragma unroll
@@ -222,9 +245,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const DecodeArgs a) {
       }
     }
 #pragma unroll
-    for (int hh = 0; hh < HPW; ++hh)
-#pragma unroll
-      for (int msk = BS; msk < 64; msk <<= 1) sc[hh] += xor_lanes(sc[hh], msk);
+    for (int hh = 0; hh < HPW; ++hh) sc[hh] = token_sum<BS>(sc[hh]);
 
     // ---- online softmax over this tile ----
     const int tile_t0 = j * BS;
@@ -237,13 +258,17 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const DecodeArgs a) {
       cfac[hh] = __builtin_amdgcn_exp2f(m_run[hh] - mnew);
       float p = __builtin_amdgcn_exp2f(z - mnew);
       m_run[hh] = mnew;
-      if constexpr (!F32) p = bf16_to_f32(f32_to_bf16(p));
+      uint16_t pb = 0;
+      if constexpr (!F32) {
+        pb = cvt_bf16(p);
+        p = bf16_to_f32(pb);
+      }
       l_run[hh] = l_run[hh] * cfac[hh] + p;
       if (lane < BS) {
         if constexpr (F32)
           p_lds[w][hh][lane] = p;
         else
-          ((uint16_t*)&p_lds[w][hh][0])[lane] = f32_to_bf16(p);
+          ((uint16_t*)&p_lds[w][hh][0])[lane] = pb;
       }
     }
     __builtin_amdgcn_wave_barrier();
@@ -316,12 +341,50 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const DecodeArgs a) {
       }
     }
     __builtin_amdgcn_wave_barrier();
+  };
 
+  // The wave's tiles (jfirst, jfirst + NW, ...) go in chunks of 64: one
+  // vector load fetches a chunk's table entries while nothing else is in
+  // flight, so no tile load ever waits on a table lookup.  Within a chunk a
+  // ring of NBUF register buffers keeps the next tiles in flight while one is
+  // consumed (prefetch of the next pages).  The steady-state loop issues its
+  // prefetches unconditionally, so the compiler's wait counts let exactly the
+  // younger tiles stay outstanding; only the last few tiles of a chunk run
+  // with conditional loads.
+  u32x4 kbuf[NBUF][NLOAD], vbuf[NBUF][NLOAD];
+  const int jfirst = t0 / BS + w;
+  for (chunk0 = jfirst; chunk0 < jend; chunk0 += 64 * NW) {
+    const int n = min(64, (jend - chunk0 + NW - 1) / NW);  // tiles of this wave in the chunk
+    const int jl = chunk0 + lane * NW;
+    tbl_v = lane < n ? tbl[jl] : 0;
+    auto tile = [&](int k) { return chunk0 + k * NW; };
+    int k = 0;
+    if (n >= NBUF) {
 #pragma unroll
-    for (int l = 0; l < NLOAD; ++l) {
-      kr[l] = kn[l];
-      vr[l] = vn[l];
+      for (int b = 0; b < NBUF; ++b) load_tile(tile(b), kbuf[b], vbuf[b]);
+      for (; k + 2 * NBUF <= n; k += NBUF) {
+#pragma unroll
+        for (int b = 0; b < NBUF; ++b) {
+          process(tile(k + b), kbuf[b], vbuf[b]);
+          load_tile(tile(k + NBUF + b), kbuf[b], vbuf[b]);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int b = 0; b < NBUF; ++b)
+        if (b < n) load_tile(tile(b), kbuf[b], vbuf[b]);
     }
+    // buffers hold tiles k .. k+NBUF-1 (those < n); at most 2*NBUF-1 remain
+#pragma unroll
+    for (int b = 0; b < NBUF; ++b) {
+      if (k + b < n) {
+        process(tile(k + b), kbuf[b], vbuf[b]);
+        if (k + NBUF + b < n) load_tile(tile(k + NBUF + b), kbuf[b], vbuf[b]);
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < NBUF; ++b)
+      if (k + NBUF + b < n) process(tile(k + NBUF + b), kbuf[b], vbuf[b]);
   }
 
   // ---- per-wave totals ----
@@ -453,7 +516,8 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(void* __restrict__ o
   }
 }
 
-constexpr int kWaves = 4;
+constexpr int kWaves = PKV_DECODE_WAVES;
+constexpr int kBufs = PKV_DECODE_DEPTH + 1;  // tiles in registers per wave
 
 template <int KV, int D, int BS, int HPW>
 int launch_t(const DecodeArgs& a, hipStream_t st) {
@@ -461,10 +525,10 @@ int launch_t(const DecodeArgs& a, hipStream_t st) {
   dim3 block(kWaves * 64);
   if (a.partition > 0) {
     dim3 grid(a.total_parts, a.Hkv * groups);
-    hipLaunchKernelGGL((decode_kernel<KV, D, BS, HPW, kWaves, true>), grid, block, 0, st, a);
+    hipLaunchKernelGGL((decode_kernel<KV, D, BS, HPW, kWaves, kBufs, true>), grid, block, 0, st, a);
   } else {
     dim3 grid(a.S, a.Hkv * groups);
-    hipLaunchKernelGGL((decode_kernel<KV, D, BS, HPW, kWaves, false>), grid, block, 0, st, a);
+    hipLaunchKernelGGL((decode_kernel<KV, D, BS, HPW, kWaves, kBufs, false>), grid, block, 0, st, a);
   }
   return (int)hipGetLastError();
 }

@@ -193,3 +193,41 @@ int launch_gather(void* k_out, void* v_out, const void* kc, const void* vc, cons
 }
 
 }  // namespace pkv
+
+// ---------------------------------------------------------------------------
+// Streaming-read probe: every lane reads 16-byte units of a buffer with
+// UNROLL loads in flight, folds them into a checksum and stores nothing
+// unless the checksum hits a sentinel.  Measures the attainable HBM read
+// rate of this GPU, the ceiling the decode kernel's KV stream is held to.
+namespace pkv {
+namespace {
+template <int UNROLL>
+__global__ __launch_bounds__(256) void read_probe_kernel(const u32x4* __restrict__ src, size_t n16,
+                                                         uint32_t* __restrict__ sink) {
+  const size_t tid = (size_t)blockIdx.x * 256 + threadIdx.x;
+  const size_t stride = (size_t)gridDim.x * 256;
+  uint32_t acc = 0;
+  size_t i = tid;
+  for (; i + (UNROLL - 1) * stride < n16; i += UNROLL * stride) {
+    u32x4 v[UNROLL];
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) v[u] = __builtin_nontemporal_load(src + i + u * stride);
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+  }
+  for (; i < n16; i += stride) {
+    const u32x4 v = src[i];
+    acc ^= v.x ^ v.y ^ v.z ^ v.w;
+  }
+  if (acc == 0x9e3779b9u) sink[0] = acc;
+}
+}  // namespace
+
+int launch_read_probe(const void* src, size_t bytes, void* sink, int blocks, void* stream) {
+  const size_t n16 = bytes / 16;
+  if (n16 == 0) return 0;
+  hipLaunchKernelGGL((read_probe_kernel<8>), dim3(blocks), dim3(256), 0, (hipStream_t)stream,
+                     (const u32x4*)src, n16, (uint32_t*)sink);
+  return (int)hipGetLastError();
+}
+}  // namespace pkv

@@ -89,4 +89,28 @@ __device__ __forceinline__ float row16_sum(float v) {
 
 __device__ __forceinline__ float xor_lanes(float v, int mask) { return __shfl_xor(v, mask, 64); }
 
+// v[l] + v[l ^ 32] in every lane, without LDS: v_permlane32_swap exchanges the
+// upper half of one register copy with the lower half of the other.
+__device__ __forceinline__ float sum_xor32(float v) {
+  const uint32_t u = __float_as_uint(v);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+// v[l] + v[l ^ 16] (v_permlane16_swap exchanges odd rows with even rows).
+__device__ __forceinline__ float sum_xor16(float v) {
+  const uint32_t u = __float_as_uint(v);
+  const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float max_xor16(float v) {
+  const uint32_t u = __float_as_uint(v);
+  const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+// fp32 -> bf16 bits with the hardware conversion (round to nearest even).
+__device__ __forceinline__ uint16_t cvt_bf16(float f) {
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
+}
+
 }  // namespace pkv

@@ -46,6 +46,7 @@ int launch_kv_write(const void* key, const void* value, void* kc, void* vc, cons
                     float k_inv, float v_inv, void* stream);
 int launch_copy_blocks(void* kc, void* vc, const int32_t* pairs, int n, size_t block_bytes,
                        int nb, void* stream);
+int launch_read_probe(const void* src, size_t bytes, void* sink, int blocks, void* stream);
 int launch_gather(void* k_out, void* v_out, const void* kc, const void* vc, const int32_t* tables,
                   int max_blocks, const int32_t* cu_ctx, int S, int T, int H, int D, int BS,
                   int nb, pkv_dtype cache, void* stream);

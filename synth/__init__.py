@@ -79,7 +79,7 @@ CONFIGS = {
     2: Config("bf16-mha-7b", S=32, H_q=32, H_kv=32, d=128, bs=16, q_dtype="bf16", kv_dtype="bf16",
               scale=_SCALE_D128, partition=512, seed=2, len_range=(128, 2048)),
     3: Config("bf16-gqa", S=64, H_q=32, H_kv=8, d=128, bs=16, q_dtype="bf16", kv_dtype="bf16",
-              scale=_SCALE_D128, partition=512, seed=3, len_range=(512, 8192)),
+              scale=_SCALE_D128, partition=1024, seed=3, len_range=(512, 8192)),
     4: Config("bf16-prefix", S=128, H_q=32, H_kv=8, d=128, bs=16, q_dtype="bf16", kv_dtype="bf16",
               scale=_SCALE_D128, partition=512, seed=4, prefix=1030, suffix_range=(16, 512)),
     5: Config("fp8-skewed", S=256, H_q=64, H_kv=8, d=128, bs=32, q_dtype="bf16", kv_dtype="fp8",
@@ -121,6 +121,7 @@ class Workload:
     prefill: list = field(default_factory=list)
     decode: list = field(default_factory=list)
     _cache: dict = field(default_factory=dict, repr=False)
+    cache_limit: int = 4                # value streams kept in memory (0 = no limit)
 
     # ops are tuples:
     #   ("add", s)  ("fork", parent, child)
@@ -142,7 +143,7 @@ class Workload:
         rng = np.random.default_rng(seed)
         k = _round(rng.standard_normal((n, c.H_kv, c.d), dtype=np.float32), c.src_dtype)
         v = _round(rng.standard_normal((n, c.H_kv, c.d), dtype=np.float32), c.src_dtype)
-        if len(self._cache) >= 4:
+        if self.cache_limit and len(self._cache) >= self.cache_limit:
             self._cache.clear()
         self._cache[stream] = (k, v)
         return k, v
