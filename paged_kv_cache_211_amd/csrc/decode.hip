@@ -44,6 +44,9 @@
 #ifndef PKV_DECODE_DEPTH
 #define PKV_DECODE_DEPTH 1
 #endif
+#ifndef PKV_DECODE_QLDS
+#define PKV_DECODE_QLDS 0
+#endif
 
 namespace pkv {
 namespace {
@@ -167,30 +170,32 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const DecodeArgs a) {
   const size_t head_off = (size_t)hkv * TILE;
   const size_t blk_stride = (size_t)a.Hkv * TILE;
 
-  // ---- query registers: the dims of this lane's key chunks, HPW heads ----
-  const int kchunk0 = lane / BS;  // chunk of load j is j*KL + kchunk0
-  uint32_t qp[F32 ? 1 : HPW][F32 ? 1 : NLOAD][F32 ? 1 : PPC];
-  float qf[F32 ? HPW : 1][F32 ? NLOAD : 1][F32 ? 4 : 1];
+  // ---- query rows of the HPW heads ----
+  // Either held in VGPRs (the dims of this lane's key chunks) or staged once
+  // in LDS for all waves of the workgroup (PKV_DECODE_QLDS).
+  constexpr int QE = F32 ? 4 : 2;              // query element bytes
+  constexpr int QUL = 2 * X * QE / 32;         // 16-byte q units per key load (1 or 2)
+  const int kchunk0 = lane / BS;               // key chunk of load l is l*KL + kchunk0
+  const uint8_t* qsrc = (const uint8_t*)a.q + ((size_t)s * a.Hq + qh0) * D * QE;
+#if PKV_DECODE_QLDS
+  constexpr int QU = HPW * D * QE / 16;
+  __shared__ u32x4 q_lds[QU];
+  for (int u = threadIdx.x; u < QU; u += NW * 64) q_lds[u] = *(const u32x4*)(qsrc + 16 * u);
+  __syncthreads();
+  auto q_unit = [&](int hh, int l, int u) -> u32x4 {
+    return q_lds[(hh * D + (l * KL + kchunk0) * X) * QE / 16 + u];
+  };
+#else
+  u32x4 q_reg[HPW][NLOAD][QUL];
 #pragma unroll
-  for (int hh = 0; hh < HPW; ++hh) {
-    const size_t qrow = ((size_t)s * a.Hq + qh0 + hh) * D;
+  for (int hh = 0; hh < HPW; ++hh)
 #pragma unroll
-    for (int j = 0; j < NLOAD; ++j) {
-      const int dim0 = (j * KL + kchunk0) * X;
-      if constexpr (F32) {
-        const f32x4 v = *(const f32x4*)((const float*)a.q + qrow + dim0);
-        qf[hh][j][0] = v.x; qf[hh][j][1] = v.y; qf[hh][j][2] = v.z; qf[hh][j][3] = v.w;
-      } else {
-        const uint16_t* qb = (const uint16_t*)a.q + qrow + dim0;
+    for (int l = 0; l < NLOAD; ++l)
 #pragma unroll
-        for (int u = 0; u < PPC / 4; ++u) {
-          const u32x4 v = *(const u32x4*)(qb + 8 * u);
-          qp[hh][j][4 * u] = v.x; qp[hh][j][4 * u + 1] = v.y;
-          qp[hh][j][4 * u + 2] = v.z; qp[hh][j][4 * u + 3] = v.w;
-        }
-      }
-    }
-  }
+      for (int u = 0; u < QUL; ++u)
+        q_reg[hh][l][u] = *(const u32x4*)(qsrc + ((size_t)(hh * D + (l * KL + kchunk0) * X) * QE + 16 * u));
+  auto q_unit = [&](int hh, int l, int u) -> u32x4 { return q_reg[hh][l][u]; };
+#endif
 
   float m_run[HPW], l_run[HPW], acc[HPW][NLOAD];
 #pragma unroll
@@ -230,18 +235,26 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const DecodeArgs a) {
         const f32x4 k4 = __builtin_bit_cast(f32x4, kr[l]);
 #pragma unroll
         for (int hh = 0; hh < HPW; ++hh) {
-          sc[hh] = fmaf(qf[hh][l][0], k4.x, sc[hh]);
-          sc[hh] = fmaf(qf[hh][l][1], k4.y, sc[hh]);
-          sc[hh] = fmaf(qf[hh][l][2], k4.z, sc[hh]);
-          sc[hh] = fmaf(qf[hh][l][3], k4.w, sc[hh]);
+          const f32x4 q4 = __builtin_bit_cast(f32x4, q_unit(hh, l, 0));
+          sc[hh] = fmaf(q4.x, k4.x, sc[hh]);
+          sc[hh] = fmaf(q4.y, k4.y, sc[hh]);
+          sc[hh] = fmaf(q4.z, k4.z, sc[hh]);
+          sc[hh] = fmaf(q4.w, k4.w, sc[hh]);
         }
       } else {
         uint32_t kp[PPC];
         unpack_pairs<KV>(kr[l], kp);
 #pragma unroll
-        for (int hh = 0; hh < HPW; ++hh)
+        for (int hh = 0; hh < HPW; ++hh) {
 #pragma unroll
-          for (int k = 0; k < PPC; ++k) sc[hh] = dot2_bf16(qp[hh][l][k], kp[k], sc[hh]);
+          for (int u = 0; u < PPC / 4; ++u) {
+            const u32x4 q4 = q_unit(hh, l, u);
+            sc[hh] = dot2_bf16(q4.x, kp[4 * u], sc[hh]);
+            sc[hh] = dot2_bf16(q4.y, kp[4 * u + 1], sc[hh]);
+            sc[hh] = dot2_bf16(q4.z, kp[4 * u + 2], sc[hh]);
+            sc[hh] = dot2_bf16(q4.w, kp[4 * u + 3], sc[hh]);
+          }
+        }
       }
     }
 #pragma unroll
@@ -534,12 +547,18 @@ int launch_t(const DecodeArgs& a, hipStream_t st) {
 }
 
 // Heads per workgroup: the largest power of two (at most 8) dividing G whose
-// query registers fit in 64 VGPRs.
+// per-head registers fit the budget: the query dims of the lane's key chunks
+// (64 VGPRs in all when q lives in VGPRs), else the accumulators and the
+// probabilities of a value load (48 VGPRs in all).
 template <int KV, int D, int BS>
 constexpr int max_hpw() {
   using Gm = Geo<KV, D, BS>;
-  constexpr int per_head = Gm::F32 ? Gm::NLOAD * 4 : Gm::NLOAD * Gm::PPC;  // q VGPRs per head
-  return 64 / per_head >= 8 ? 8 : 64 / per_head;
+#if PKV_DECODE_QLDS
+  constexpr int per_head = Gm::NLOAD + (Gm::F32 ? 4 : Gm::PPC), budget = 48;
+#else
+  constexpr int per_head = Gm::F32 ? Gm::NLOAD * 4 : Gm::NLOAD * Gm::PPC, budget = 64;
+#endif
+  return budget / per_head >= 8 ? 8 : budget / per_head >= 4 ? 4 : budget / per_head >= 2 ? 2 : 1;
 }
 
 template <int KV, int D, int BS>

@@ -77,11 +77,11 @@ CONFIGS = {
     1: Config("fp32-tiny", S=4, H_q=4, H_kv=4, d=64, bs=16, q_dtype="f32", kv_dtype="f32",
               scale=0.125, partition=0, seed=1, lens=(1, 17, 33, 100), num_blocks=64),
     2: Config("bf16-mha-7b", S=32, H_q=32, H_kv=32, d=128, bs=16, q_dtype="bf16", kv_dtype="bf16",
-              scale=_SCALE_D128, partition=512, seed=2, len_range=(128, 2048)),
+              scale=_SCALE_D128, partition=256, seed=2, len_range=(128, 2048)),
     3: Config("bf16-gqa", S=64, H_q=32, H_kv=8, d=128, bs=16, q_dtype="bf16", kv_dtype="bf16",
               scale=_SCALE_D128, partition=1024, seed=3, len_range=(512, 8192)),
     4: Config("bf16-prefix", S=128, H_q=32, H_kv=8, d=128, bs=16, q_dtype="bf16", kv_dtype="bf16",
-              scale=_SCALE_D128, partition=512, seed=4, prefix=1030, suffix_range=(16, 512)),
+              scale=_SCALE_D128, partition=2048, seed=4, prefix=1030, suffix_range=(16, 512)),
     5: Config("fp8-skewed", S=256, H_q=64, H_kv=8, d=128, bs=32, q_dtype="bf16", kv_dtype="fp8",
               scale=_SCALE_D128, partition=512, seed=5, long=(8, 32768, 131072),
               short=(248, 64, 512), k_scale=FP8_KV_SCALE, v_scale=FP8_KV_SCALE),
