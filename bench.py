@@ -68,7 +68,7 @@ def algorithmic_bytes(wl):
 
 def src_sha():
     h = hashlib.sha256()
-    for f in ("decode.hip", "pkv_device.h"):
+    for f in ("decode.hip", "decode_mfma.hip", "decode_common.h", "pkv_device.h"):
         with open(os.path.join(ROOT, "paged_kv_cache_211_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]

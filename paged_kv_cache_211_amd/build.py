@@ -22,7 +22,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libpkv.so")
 ARCH = "gfx950"
 
-SOURCES = ["api.cpp", "allocator.cpp", "kv_ops.hip", "decode.hip"]
+SOURCES = ["api.cpp", "allocator.cpp", "kv_ops.hip", "decode.hip", "decode_mfma.hip"]
 
 
 def hipcc() -> str:

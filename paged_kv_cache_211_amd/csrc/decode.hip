@@ -31,25 +31,12 @@
 
 #include <cmath>
 
-#include "pkv_device.h"
-#include "pkv_internal.h"
-
-// Launch shape (fixed at build time; -D overrides exist for tuning sweeps).
-#ifndef PKV_DECODE_WAVES
-#define PKV_DECODE_WAVES 4
-#endif
-#ifndef PKV_DECODE_NT
-#define PKV_DECODE_NT 1
-#endif
-#ifndef PKV_DECODE_DEPTH
-#define PKV_DECODE_DEPTH 1
-#endif
-#ifndef PKV_DECODE_QLDS
-#define PKV_DECODE_QLDS 0
-#endif
+#include "decode_common.h"
 
 namespace pkv {
 namespace {
+
+using namespace dec;
 
 template <int KV, int D, int BS>
 struct Geo {
@@ -67,19 +54,6 @@ struct Geo {
   static_assert(RU >= 1 && 64 % RU == 0, "value row must divide the wave");
 };
 
-// Number of i in [1, S] with part_off[i] <= idx, i.e. the sequence owning
-// flat partition idx (part_off is non-decreasing, part_off[0] = 0).
-__device__ __forceinline__ int find_seq(const int32_t* __restrict__ part_off, int S, int idx,
-                                        int lane) {
-  int s = 0;
-  for (int base = 1; base <= S; base += 64) {
-    const int i = base + lane;
-    const bool le = i <= S && part_off[i] <= idx;
-    s += __popcll(__ballot(le));
-  }
-  return s;
-}
-
 // A 16-byte unit of bf16 or fp8 elements -> PPC packed bf16 pairs (exact).
 template <int KV>
 __device__ __forceinline__ void unpack_pairs(const u32x4 r, uint32_t* p) {
@@ -96,15 +70,6 @@ __device__ __forceinline__ void unpack_pairs(const u32x4 r, uint32_t* p) {
       p[2 * i + 1] = __builtin_amdgcn_perm(__float_as_uint(hi.y), __float_as_uint(hi.x), 0x07060302u);
     }
   }
-}
-
-// One 16-byte load of streamed key/value data.
-__device__ __forceinline__ u32x4 load16(const uint8_t* p) {
-#if PKV_DECODE_NT
-  return __builtin_nontemporal_load((const u32x4*)p);
-#else
-  return *(const u32x4*)p;
-#endif
 }
 
 template <int BS>
@@ -141,33 +106,11 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const DecodeArgs a) {
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int G = a.Hq / a.Hkv;
-  const int groups = G / HPW;
-  const int hkv = blockIdx.y / groups;
-  const int qh0 = hkv * G + (blockIdx.y % groups) * HPW;
-
-  int s, nparts, part;
-  if constexpr (SPLIT) {
-    s = __builtin_amdgcn_readfirstlane(find_seq(a.part_off, a.S, blockIdx.x, lane));
-    const int p0 = a.part_off[s];
-    part = blockIdx.x - p0;
-    nparts = a.part_off[s + 1] - p0;
-  } else {
-    s = blockIdx.x;
-    part = 0;
-    nparts = 1;
-  }
-  int L = a.lens[s];
-  bool bad = false;
-  if (L < 0) { L = 0; bad = true; }
-  if (L > a.max_blocks * BS) { L = a.max_blocks * BS; bad = true; }
-  const int t0 = SPLIT ? part * a.partition : 0;
-  const int t1 = SPLIT ? min(L, t0 + a.partition) : L;
-  const int jend = (t1 + BS - 1) / BS;
+  const Work wk = locate<SPLIT, BS>(a, HPW, lane);
+  const int s = wk.s, qh0 = wk.qh0, t1 = wk.t1;
+  bool bad = wk.bad;
   const int32_t* __restrict__ tbl = a.tables + (size_t)s * a.max_blocks;
-  const uint8_t* __restrict__ kc = (const uint8_t*)a.kc;
-  const uint8_t* __restrict__ vc = (const uint8_t*)a.vc;
-  const size_t head_off = (size_t)hkv * TILE;
+  const size_t head_off = (size_t)wk.hkv * TILE;
   const size_t blk_stride = (size_t)a.Hkv * TILE;
 
   // ---- query rows of the HPW heads ----
@@ -208,20 +151,6 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const DecodeArgs a) {
 
   const int tk = lane % BS;              // this lane's token in a key tile
   const int tv0 = (lane % RU) * X;       // first of this lane's X tokens in a value tile
-
-  // tbl_v: block-table entries of the current chunk of this wave's tiles
-  // (lane i holds the entry of the chunk's i-th tile), read with v_readlane.
-  int tbl_v = 0, chunk0 = 0;
-  auto load_tile = [&](int jj, u32x4* kdst, u32x4* vdst) {
-    int b = __builtin_amdgcn_readlane(tbl_v, (jj - chunk0) / NW);
-    if ((unsigned)b >= (unsigned)a.nb) { bad = true; b = 0; }
-    const uint8_t* kt = kc + (size_t)b * blk_stride + head_off + lane * 16;
-    const uint8_t* vt = vc + (size_t)b * blk_stride + head_off + lane * 16;
-#pragma unroll
-    for (int l = 0; l < NLOAD; ++l) kdst[l] = load16(kt + l * 1024);
-#pragma unroll
-    for (int l = 0; l < NLOAD; ++l) vdst[l] = load16(vt + l * 1024);
-  };
 
   // One tile: QK^T for this lane's token, online softmax, PV.
   auto process = [&](int j, const u32x4* kr, const u32x4* vr) {
@@ -356,49 +285,10 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const DecodeArgs a) {
     __builtin_amdgcn_wave_barrier();
   };
 
-  // The wave's tiles (jfirst, jfirst + NW, ...) go in chunks of 64: one
-  // vector load fetches a chunk's table entries while nothing else is in
-  // flight, so no tile load ever waits on a table lookup.  Within a chunk a
-  // ring of NBUF register buffers keeps the next tiles in flight while one is
-  // consumed (prefetch of the next pages).  The steady-state loop issues its
-  // prefetches unconditionally, so the compiler's wait counts let exactly the
-  // younger tiles stay outstanding; only the last few tiles of a chunk run
-  // with conditional loads.
-  u32x4 kbuf[NBUF][NLOAD], vbuf[NBUF][NLOAD];
-  const int jfirst = t0 / BS + w;
-  for (chunk0 = jfirst; chunk0 < jend; chunk0 += 64 * NW) {
-    const int n = min(64, (jend - chunk0 + NW - 1) / NW);  // tiles of this wave in the chunk
-    const int jl = chunk0 + lane * NW;
-    tbl_v = lane < n ? tbl[jl] : 0;
-    auto tile = [&](int k) { return chunk0 + k * NW; };
-    int k = 0;
-    if (n >= NBUF) {
-#pragma unroll
-      for (int b = 0; b < NBUF; ++b) load_tile(tile(b), kbuf[b], vbuf[b]);
-      for (; k + 2 * NBUF <= n; k += NBUF) {
-#pragma unroll
-        for (int b = 0; b < NBUF; ++b) {
-          process(tile(k + b), kbuf[b], vbuf[b]);
-          load_tile(tile(k + NBUF + b), kbuf[b], vbuf[b]);
-        }
-      }
-    } else {
-#pragma unroll
-      for (int b = 0; b < NBUF; ++b)
-        if (b < n) load_tile(tile(b), kbuf[b], vbuf[b]);
-    }
-    // buffers hold tiles k .. k+NBUF-1 (those < n); at most 2*NBUF-1 remain
-#pragma unroll
-    for (int b = 0; b < NBUF; ++b) {
-      if (k + b < n) {
-        process(tile(k + b), kbuf[b], vbuf[b]);
-        if (k + NBUF + b < n) load_tile(tile(k + NBUF + b), kbuf[b], vbuf[b]);
-      }
-    }
-#pragma unroll
-    for (int b = 0; b < NBUF; ++b)
-      if (k + NBUF + b < n) process(tile(k + NBUF + b), kbuf[b], vbuf[b]);
-  }
+  tile_loop<NBUF, NLOAD, NW>(tbl, wk.t0 / BS + w, wk.jend, a.nb,
+                             (const uint8_t*)a.kc + head_off + lane * 16,
+                             (const uint8_t*)a.vc + head_off + lane * 16, blk_stride, lane, bad,
+                             process);
 
   // ---- per-wave totals ----
 #pragma unroll
@@ -420,44 +310,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const DecodeArgs a) {
   __syncthreads();
 
   // ---- merge the waves, then write the output or the partial ----
-  int any_bad = 0;
-#pragma unroll
-  for (int ww = 0; ww < NW; ++ww) any_bad |= bad_lds[ww];
-  const bool final_out = !SPLIT || nparts == 1;
-  float* ws_o = a.ws;
-  float* ws_ml = a.ws + (size_t)a.total_parts * a.Hq * D;
-  for (int i = threadIdx.x; i < HPW * D; i += NW * 64) {
-    const int hh = i / D, dim = i % D;
-    float M = -INFINITY;
-#pragma unroll
-    for (int ww = 0; ww < NW; ++ww) M = fmaxf(M, m_lds[ww][hh]);
-    float Ls = 0.f, O = 0.f;
-    if (M != -INFINITY) {
-#pragma unroll
-      for (int ww = 0; ww < NW; ++ww) {
-        const float f = __builtin_amdgcn_exp2f(m_lds[ww][hh] - M);
-        Ls = fmaf(l_lds[ww][hh], f, Ls);
-        O = fmaf(o_lds[ww][hh][dim], f, O);
-      }
-    }
-    const int qh = qh0 + hh;
-    if (final_out) {
-      float r = Ls > 0.f ? O * a.v_mult / Ls : 0.f;
-      if (any_bad) r = NAN;
-      const size_t oi = ((size_t)s * a.Hq + qh) * D + dim;
-      if constexpr (F32)
-        ((float*)a.out)[oi] = r;
-      else
-        ((uint16_t*)a.out)[oi] = f32_to_bf16(r);
-    } else {
-      const size_t pi = (size_t)blockIdx.x * a.Hq + qh;
-      ws_o[pi * D + dim] = any_bad ? NAN : O * a.v_mult;
-      if (dim == 0) {
-        ws_ml[pi * 2] = M;
-        ws_ml[pi * 2 + 1] = any_bad ? NAN : Ls;
-      }
-    }
-  }
+  merge_store<HPW, D, NW, F32>(a, wk, !SPLIT || wk.nparts == 1, o_lds, m_lds, l_lds, bad_lds);
 }
 
 // Split-K reduce: one workgroup per (sequence, query head) with > 1 partition.
@@ -529,8 +382,6 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(void* __restrict__ o
   }
 }
 
-constexpr int kWaves = PKV_DECODE_WAVES;
-constexpr int kBufs = PKV_DECODE_DEPTH + 1;  // tiles in registers per wave
 
 template <int KV, int D, int BS, int HPW>
 int launch_t(const DecodeArgs& a, hipStream_t st) {
@@ -588,6 +439,7 @@ bool decode_supported(pkv_dtype q, pkv_dtype kv, int D, int BS, int G) {
 }
 
 int launch_decode(const DecodeArgs& a, void* stream) {
+  if (decode_mfma_eligible(a)) return launch_decode_mfma(a, stream);
   hipStream_t st = (hipStream_t)stream;
   switch (a.kv_dtype) {
     case PKV_F32: return launch_d<PKV_F32>(a, st);

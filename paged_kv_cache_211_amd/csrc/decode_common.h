@@ -1,0 +1,205 @@
+// Pieces shared by the decode kernels: locating a workgroup's (sequence,
+// partition, head group), the chunked block-table walk with its prefetch
+// ring of tiles, and the merge of the waves' softmax states.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+
+#include "pkv_device.h"
+#include "pkv_internal.h"
+
+// Launch shape (fixed at build time; -D overrides exist for tuning sweeps).
+#ifndef PKV_DECODE_WAVES
+#define PKV_DECODE_WAVES 4
+#endif
+#ifndef PKV_DECODE_NT
+#define PKV_DECODE_NT 1
+#endif
+#ifndef PKV_DECODE_DEPTH
+#define PKV_DECODE_DEPTH 1
+#endif
+#ifndef PKV_DECODE_QLDS
+#define PKV_DECODE_QLDS 0
+#endif
+
+namespace pkv {
+namespace dec {
+
+constexpr int kWaves = PKV_DECODE_WAVES;
+constexpr int kBufs = PKV_DECODE_DEPTH + 1;  // tiles in registers per wave
+
+// Number of i in [1, S] with part_off[i] <= idx, i.e. the sequence owning
+// flat partition idx (part_off is non-decreasing, part_off[0] = 0).
+__device__ __forceinline__ int find_seq(const int32_t* __restrict__ part_off, int S, int idx,
+                                        int lane) {
+  int s = 0;
+  for (int base = 1; base <= S; base += 64) {
+    const int i = base + lane;
+    const bool le = i <= S && part_off[i] <= idx;
+    s += __popcll(__ballot(le));
+  }
+  return s;
+}
+
+// One 16-byte load of streamed key/value data.
+__device__ __forceinline__ u32x4 load16(const uint8_t* p) {
+#if PKV_DECODE_NT
+  return __builtin_nontemporal_load((const u32x4*)p);
+#else
+  return *(const u32x4*)p;
+#endif
+}
+
+// What one workgroup works on.
+struct Work {
+  int s;       // sequence
+  int nparts;  // partitions of that sequence
+  int t0, t1;  // token range [t0, t1) of this partition
+  int jend;    // one past the last block of the range
+  int hkv;     // kv head
+  int qh0;     // first query head of the group
+  bool bad;    // length out of range: the output becomes NaN
+};
+
+template <bool SPLIT, int BS>
+__device__ __forceinline__ Work locate(const DecodeArgs& a, int hpw, int lane) {
+  Work wk;
+  const int G = a.Hq / a.Hkv;
+  const int groups = G / hpw;
+  wk.hkv = blockIdx.y / groups;
+  wk.qh0 = wk.hkv * G + (blockIdx.y % groups) * hpw;
+  int part;
+  if constexpr (SPLIT) {
+    wk.s = __builtin_amdgcn_readfirstlane(find_seq(a.part_off, a.S, blockIdx.x, lane));
+    const int p0 = a.part_off[wk.s];
+    part = blockIdx.x - p0;
+    wk.nparts = a.part_off[wk.s + 1] - p0;
+  } else {
+    wk.s = blockIdx.x;
+    part = 0;
+    wk.nparts = 1;
+  }
+  int L = a.lens[wk.s];
+  wk.bad = false;
+  if (L < 0) { L = 0; wk.bad = true; }
+  if (L > a.max_blocks * BS) { L = a.max_blocks * BS; wk.bad = true; }
+  wk.t0 = SPLIT ? part * a.partition : 0;
+  wk.t1 = SPLIT ? min(L, wk.t0 + a.partition) : L;
+  wk.jend = (wk.t1 + BS - 1) / BS;
+  return wk;
+}
+
+// Walk this wave's tiles jfirst, jfirst + NW, ... < jend.  Table entries
+// come 64 tiles at a time from one vector load (lane i holds the entry of
+// the chunk's i-th tile, read back with v_readlane) issued while no tile load
+// is in flight, so no tile load waits on a lookup.  Within a chunk a ring of
+// NBUF register buffers keeps the next tiles in flight while one is consumed
+// ("PagedAttention Kernel：大模型推理优化的显存管理革新" §2.2: prefetch the
+// next page while computing the current one).  The steady-state loop issues
+// its prefetches unconditionally, so the compiler's wait counts leave exactly
+// the younger tiles outstanding.  kbase/vbase point at this lane's 16 bytes
+// of load 0 of block 0 (head and lane offsets included); load l of a tile is
+// l KiB further.  A block id outside [0, nb) sets `bad` and reads block 0.
+template <int NBUF, int NLOAD, int NW, class Proc>
+__device__ __forceinline__ void tile_loop(const int32_t* __restrict__ tbl, int jfirst, int jend,
+                                          int nb, const uint8_t* kbase, const uint8_t* vbase,
+                                          size_t blk_stride, int lane, bool& bad, Proc&& process) {
+  u32x4 kbuf[NBUF][NLOAD], vbuf[NBUF][NLOAD];
+  int tbl_v = 0, chunk0 = 0;
+  auto load_tile = [&](int jj, u32x4* kd, u32x4* vd) {
+    int b = __builtin_amdgcn_readlane(tbl_v, (jj - chunk0) / NW);
+    if ((unsigned)b >= (unsigned)nb) { bad = true; b = 0; }
+    const uint8_t* kt = kbase + (size_t)b * blk_stride;
+    const uint8_t* vt = vbase + (size_t)b * blk_stride;
+#pragma unroll
+    for (int l = 0; l < NLOAD; ++l) kd[l] = load16(kt + l * 1024);
+#pragma unroll
+    for (int l = 0; l < NLOAD; ++l) vd[l] = load16(vt + l * 1024);
+  };
+  for (chunk0 = jfirst; chunk0 < jend; chunk0 += 64 * NW) {
+    const int n = min(64, (jend - chunk0 + NW - 1) / NW);  // tiles of this wave in the chunk
+    tbl_v = lane < n ? tbl[chunk0 + lane * NW] : 0;
+    auto tile = [&](int k) { return chunk0 + k * NW; };
+    int k = 0;
+    if (n >= NBUF) {
+#pragma unroll
+      for (int b = 0; b < NBUF; ++b) load_tile(tile(b), kbuf[b], vbuf[b]);
+      for (; k + 2 * NBUF <= n; k += NBUF) {
+#pragma unroll
+        for (int b = 0; b < NBUF; ++b) {
+          process(tile(k + b), kbuf[b], vbuf[b]);
+          load_tile(tile(k + NBUF + b), kbuf[b], vbuf[b]);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int b = 0; b < NBUF; ++b)
+        if (b < n) load_tile(tile(b), kbuf[b], vbuf[b]);
+    }
+    // buffers hold tiles k .. k+NBUF-1 (those < n); at most 2*NBUF-1 remain
+#pragma unroll
+    for (int b = 0; b < NBUF; ++b) {
+      if (k + b < n) {
+        process(tile(k + b), kbuf[b], vbuf[b]);
+        if (k + NBUF + b < n) load_tile(tile(k + NBUF + b), kbuf[b], vbuf[b]);
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < NBUF; ++b)
+      if (k + NBUF + b < n) process(tile(k + NBUF + b), kbuf[b], vbuf[b]);
+  }
+}
+
+// Merge the NW waves' (m, l, o) of HPW heads: M = max m_w, L = sum l_w 2^(m_w - M),
+// O = sum o_w 2^(m_w - M).  A sequence covered by one partition gets its
+// output O / L (times the value scale); otherwise the partial (M, L, O) goes
+// to the workspace for the split-K reduce.
+template <int HPW, int D, int NW, bool F32OUT>
+__device__ __forceinline__ void merge_store(const DecodeArgs& a, const Work& wk, bool final_out,
+                                            const float (&o_lds)[NW][HPW][D],
+                                            const float (&m_lds)[NW][HPW],
+                                            const float (&l_lds)[NW][HPW],
+                                            const int (&bad_lds)[NW]) {
+  int any_bad = 0;
+#pragma unroll
+  for (int ww = 0; ww < NW; ++ww) any_bad |= bad_lds[ww];
+  float* ws_o = a.ws;
+  float* ws_ml = a.ws + (size_t)a.total_parts * a.Hq * D;
+  for (int i = threadIdx.x; i < HPW * D; i += NW * 64) {
+    const int hh = i / D, dim = i % D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int ww = 0; ww < NW; ++ww) M = fmaxf(M, m_lds[ww][hh]);
+    float Ls = 0.f, O = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int ww = 0; ww < NW; ++ww) {
+        const float f = __builtin_amdgcn_exp2f(m_lds[ww][hh] - M);
+        Ls = fmaf(l_lds[ww][hh], f, Ls);
+        O = fmaf(o_lds[ww][hh][dim], f, O);
+      }
+    }
+    const int qh = wk.qh0 + hh;
+    if (final_out) {
+      float r = Ls > 0.f ? O * a.v_mult / Ls : 0.f;
+      if (any_bad) r = NAN;
+      const size_t oi = ((size_t)wk.s * a.Hq + qh) * D + dim;
+      if constexpr (F32OUT)
+        ((float*)a.out)[oi] = r;
+      else
+        ((uint16_t*)a.out)[oi] = f32_to_bf16(r);
+    } else {
+      const size_t pi = (size_t)blockIdx.x * a.Hq + qh;
+      ws_o[pi * D + dim] = any_bad ? NAN : O * a.v_mult;
+      if (dim == 0) {
+        ws_ml[pi * 2] = M;
+        ws_ml[pi * 2 + 1] = any_bad ? NAN : Ls;
+      }
+    }
+  }
+}
+
+}  // namespace dec
+}  // namespace pkv

@@ -37,6 +37,10 @@ struct DecodeArgs {
 
 // Kernel launchers (decode.hip, kv_ops.hip).  Return hipError_t as int.
 int launch_decode(const DecodeArgs& a, void* stream);
+// Matrix-core decode for fp8 key/value tiles with query heads in groups of 8
+// (decode_mfma.hip); launch_decode routes eligible calls there.
+bool decode_mfma_eligible(const DecodeArgs& a);
+int launch_decode_mfma(const DecodeArgs& a, void* stream);
 int launch_splitk_reduce(void* out, const float* ws, const int32_t* part_off, int S, int Hq, int D,
                          int total_parts, pkv_dtype out_dtype, void* stream);
 bool decode_supported(pkv_dtype q, pkv_dtype kv, int D, int BS, int G);
