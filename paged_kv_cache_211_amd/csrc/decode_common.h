@@ -23,12 +23,16 @@
 #ifndef PKV_DECODE_QLDS
 #define PKV_DECODE_QLDS 0
 #endif
+#ifndef PKV_MFMA_DEPTH
+#define PKV_MFMA_DEPTH 0
+#endif
 
 namespace pkv {
 namespace dec {
 
 constexpr int kWaves = PKV_DECODE_WAVES;
-constexpr int kBufs = PKV_DECODE_DEPTH + 1;  // tiles in registers per wave
+constexpr int kBufs = PKV_DECODE_DEPTH + 1;      // tiles in registers per wave (VALU kernel)
+constexpr int kMfmaBufs = PKV_MFMA_DEPTH + 1;    // same, matrix-core kernel
 
 // Number of i in [1, S] with part_off[i] <= idx, i.e. the sequence owning
 // flat partition idx (part_off is non-decreasing, part_off[0] = 0).

@@ -24,6 +24,9 @@
 // assignment of dims/tokens to k slots is free and chosen to match the loads.
 // Score and output rows r = 0..3 of lane l are head 4g + r; rows 8..31 are
 // padding (zero query rows).
+// Work: one wave per (sequence, split-K partition, kv head); the wave keeps
+// its own softmax state and writes its output or partial directly, so no
+// workgroup-wide merge or barrier is needed.
 
 #include <hip/hip_runtime.h>
 
@@ -46,6 +49,9 @@ __device__ __forceinline__ bf16x8 fp8x8_to_bf16(uint32_t w0, uint32_t w1) {
   return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
+// Each wave owns one work item: (sequence, partition) for the kv head of
+// blockIdx.y, flat item blockIdx.x * NW + wave.  Waves never synchronise;
+// a wave writes its own output (one-partition sequence) or partial.
 template <int NW, int NBUF, bool SPLIT>
 __global__ __launch_bounds__(NW * 64) void decode_mfma_fp8_kernel(const DecodeArgs a) {
   constexpr int D = 128, BS = 32, HPW = 8;
@@ -53,19 +59,38 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_fp8_kernel(const DecodeAr
   constexpr int NLOAD = TILE / 1024;    // 4 loads of 16 bytes per lane
 
   __shared__ uint16_t p_lds[NW][HPW][BS];
-  __shared__ float o_lds[NW][HPW][D];
-  __shared__ float m_lds[NW][HPW];
-  __shared__ float l_lds[NW][HPW];
-  __shared__ int bad_lds[NW];
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int col = lane & 31, g = lane >> 5;
-  const Work wk = locate<SPLIT, BS>(a, HPW, lane);
-  const int t1 = wk.t1;
-  bool bad = wk.bad;
-  const int32_t* __restrict__ tbl = a.tables + (size_t)wk.s * a.max_blocks;
-  const size_t head_off = (size_t)wk.hkv * TILE;
+  const int item = blockIdx.x * NW + w;
+  const int n_items = SPLIT ? a.total_parts : a.S;
+  if (item >= n_items) return;
+
+  // ---- locate the work item ----
+  const int G = a.Hq / a.Hkv;
+  const int hkv = blockIdx.y / (G / HPW);
+  const int qh0 = hkv * G + (blockIdx.y % (G / HPW)) * HPW;
+  int s, part, nparts;
+  if constexpr (SPLIT) {
+    s = __builtin_amdgcn_readfirstlane(find_seq(a.part_off, a.S, item, lane));
+    const int p0 = a.part_off[s];
+    part = item - p0;
+    nparts = a.part_off[s + 1] - p0;
+  } else {
+    s = item;
+    part = 0;
+    nparts = 1;
+  }
+  int L = a.lens[s];
+  bool bad = false;
+  if (L < 0) { L = 0; bad = true; }
+  if (L > a.max_blocks * BS) { L = a.max_blocks * BS; bad = true; }
+  const int t0 = SPLIT ? part * a.partition : 0;
+  const int t1 = SPLIT ? min(L, t0 + a.partition) : L;
+  const int jend = (t1 + BS - 1) / BS;
+  const int32_t* __restrict__ tbl = a.tables + (size_t)s * a.max_blocks;
+  const size_t head_off = (size_t)hkv * TILE;
   const size_t blk_stride = (size_t)a.Hkv * TILE;
 
   // Q as the A operand of QK^T: row = head col (rows >= 8 are zero), k slots
@@ -73,7 +98,7 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_fp8_kernel(const DecodeAr
   bf16x8 qa[NLOAD][2];
   {
     const bool valid = col < HPW;
-    const uint16_t* qrow = (const uint16_t*)a.q + ((size_t)wk.s * a.Hq + wk.qh0 + (valid ? col : 0)) * D;
+    const uint16_t* qrow = (const uint16_t*)a.q + ((size_t)s * a.Hq + qh0 + (valid ? col : 0)) * D;
 #pragma unroll
     for (int l = 0; l < NLOAD; ++l)
 #pragma unroll
@@ -106,24 +131,39 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_fp8_kernel(const DecodeAr
       sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[l][1], fp8x8_to_bf16(kr[l].z, kr[l].w), sc, 0, 0, 0);
     }
     // ---- online softmax, rows r = 0..3 (head 4g + r), column = token col ----
+    // Probabilities are taken against a reference max m_run that moves only
+    // when a tile's max exceeds it by more than 2^8 (then l and the
+    // accumulator are rescaled, a rare, wave-uniform branch).  p <= 2^8 stays
+    // exact in range for bf16 and fp32, and the result O / l does not depend
+    // on the reference.
     const int tile_t0 = j * BS;
     const bool valid = tile_t0 + col < t1;
-    float cfac[4];
+    float z[4], tmax[4];
+    bool grow = false;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const float z = valid ? sc[r] * a.qk_mult : -INFINITY;
-      const float mnew = fmaxf(m_run[r], max_xor16(row16_max(z)));
-      cfac[r] = __builtin_amdgcn_exp2f(m_run[r] - mnew);
-      const uint16_t pb = cvt_bf16(__builtin_amdgcn_exp2f(z - mnew));
-      m_run[r] = mnew;
-      l_run[r] = l_run[r] * cfac[r] + bf16_to_f32(pb);
+      z[r] = valid ? sc[r] * a.qk_mult : -INFINITY;
+      tmax[r] = max_xor16(row16_max(z[r]));
+      grow |= tmax[r] > m_run[r] + 8.0f;
+    }
+    if (__ballot(grow)) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const bool up = tmax[r] > m_run[r] + 8.0f;
+        const float c = up ? __builtin_amdgcn_exp2f(m_run[r] - tmax[r]) : 1.0f;
+        m_run[r] = up ? tmax[r] : m_run[r];
+        l_run[r] *= c;
+#pragma unroll
+        for (int m = 0; m < NLOAD; ++m) acc[m][r] *= c;
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const uint16_t pb = cvt_bf16(__builtin_amdgcn_exp2f(z[r] - m_run[r]));
+      l_run[r] += bf16_to_f32(pb);
       p_lds[w][4 * g + r][col] = pb;
     }
     __builtin_amdgcn_wave_barrier();
-#pragma unroll
-    for (int m = 0; m < NLOAD; ++m)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) acc[m][r] *= cfac[r];
     // P as the A operand of PV: row = head col, k slots 8g .. 8g+7 <->
     // tokens 16g + 8*half + (0..7).
     bf16x8 pa[2];
@@ -138,43 +178,57 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_fp8_kernel(const DecodeAr
       pa[1] = __builtin_bit_cast(bf16x8, hi);
     }
     // ---- O[head][dim] += P V; value load m holds dims 32m + col ----
+    // Value codes of tokens past the end of the range become 0 (+0.0) by a
+    // byte mask on the fp8 words (the same tokens in every dim group), so
+    // uninitialised slots never reach the accumulator (0 * NaN).
     const int nvalid = t1 - tile_t0;
-    const bool tail = nvalid < BS;
+    uint32_t vmask[2][2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int keep = min(max(nvalid - (16 * g + 8 * h), 0), 8);  // bytes kept of these 8 tokens
+      const uint64_t m64 = keep >= 8 ? ~0ull : ((1ull << (8 * keep)) - 1ull);
+      vmask[h][0] = (uint32_t)m64;
+      vmask[h][1] = (uint32_t)(m64 >> 32);
+    }
 #pragma unroll
     for (int m = 0; m < NLOAD; ++m) {
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        bf16x8 vb = fp8x8_to_bf16(h ? vr[m].z : vr[m].x, h ? vr[m].w : vr[m].y);
-        if (tail) {
-#pragma unroll
-          for (int e = 0; e < 8; ++e)
-            if (16 * g + 8 * h + e >= nvalid) vb[e] = (__bf16)0.f;
-        }
-        acc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[h], vb, acc[m], 0, 0, 0);
-      }
+      acc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+          pa[0], fp8x8_to_bf16(vr[m].x & vmask[0][0], vr[m].y & vmask[0][1]), acc[m], 0, 0, 0);
+      acc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+          pa[1], fp8x8_to_bf16(vr[m].z & vmask[1][0], vr[m].w & vmask[1][1]), acc[m], 0, 0, 0);
     }
     __builtin_amdgcn_wave_barrier();
   };
 
-  tile_loop<NBUF, NLOAD, NW>(tbl, wk.t0 / BS + w, wk.jend, a.nb,
-                             (const uint8_t*)a.kc + head_off + lane * 16,
-                             (const uint8_t*)a.vc + head_off + col * 32 + g * 16, blk_stride,
-                             lane, bad, process);
+  tile_loop<NBUF, NLOAD, 1>(tbl, t0 / BS, jend, a.nb,
+                            (const uint8_t*)a.kc + head_off + lane * 16,
+                            (const uint8_t*)a.vc + head_off + col * 32 + g * 16, blk_stride,
+                            lane, bad, process);
 
-  // ---- per-wave totals: l over the 32 tokens of each half, o from the MFMA rows ----
+  // ---- epilogue: rows r = 0..3 are head 4g + r; lane holds dims 32m + col ----
+  const bool final_out = !SPLIT || nparts == 1;
+  float* ws_o = a.ws;
+  float* ws_ml = a.ws + (size_t)a.total_parts * a.Hq * D;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const float lt = sum_xor16(row16_sum(l_run[r]));
+    const int qh = qh0 + 4 * g + r;
+    if (final_out) {
+      const float inv = lt > 0.f ? a.v_mult / lt : 0.f;
+      uint16_t* o = (uint16_t*)a.out + ((size_t)s * a.Hq + qh) * D + col;
 #pragma unroll
-    for (int m = 0; m < NLOAD; ++m) o_lds[w][4 * g + r][32 * m + col] = acc[m][r];
-    if (col == 0) {
-      m_lds[w][4 * g + r] = m_run[r];
-      l_lds[w][4 * g + r] = lt;
+      for (int m = 0; m < NLOAD; ++m) o[32 * m] = f32_to_bf16(bad ? NAN : acc[m][r] * inv);
+    } else {
+      const size_t pi = (size_t)item * a.Hq + qh;
+      float* o = ws_o + pi * D + col;
+#pragma unroll
+      for (int m = 0; m < NLOAD; ++m) o[32 * m] = bad ? NAN : acc[m][r] * a.v_mult;
+      if (col == 0) {
+        ws_ml[pi * 2] = m_run[r];
+        ws_ml[pi * 2 + 1] = bad ? NAN : lt;
+      }
     }
   }
-  if (lane == 0) bad_lds[w] = bad ? 1 : 0;
-  __syncthreads();
-  merge_store<HPW, D, NW, false>(a, wk, !SPLIT || wk.nparts == 1, o_lds, m_lds, l_lds, bad_lds);
 }
 
 }  // namespace
@@ -188,13 +242,12 @@ int launch_decode_mfma(const DecodeArgs& a, void* stream) {
   hipStream_t st = (hipStream_t)stream;
   const int groups = a.Hq / a.Hkv / 8;
   dim3 block(kWaves * 64);
-  if (a.partition > 0) {
-    hipLaunchKernelGGL((decode_mfma_fp8_kernel<kWaves, kBufs, true>), dim3(a.total_parts, a.Hkv * groups),
-                       block, 0, st, a);
-  } else {
-    hipLaunchKernelGGL((decode_mfma_fp8_kernel<kWaves, kBufs, false>), dim3(a.S, a.Hkv * groups),
-                       block, 0, st, a);
-  }
+  const int items = a.partition > 0 ? a.total_parts : a.S;
+  dim3 grid((items + kWaves - 1) / kWaves, a.Hkv * groups);
+  if (a.partition > 0)
+    hipLaunchKernelGGL((decode_mfma_fp8_kernel<kWaves, kMfmaBufs, true>), grid, block, 0, st, a);
+  else
+    hipLaunchKernelGGL((decode_mfma_fp8_kernel<kWaves, kMfmaBufs, false>), grid, block, 0, st, a);
   return (int)hipGetLastError();
 }
 
