@@ -1,16 +1,21 @@
 #!/usr/bin/env python3
 """PagedAttention decode benchmark on one MI355X.
 
-One step = the decode step of the hot path over one batch: scatter of each
-sequence's new key/value token into its slot (paged_kv_write), the split-K
-decode kernel (paged_attention_decode_partials) and the split-K reduce.  The
-KV cache is prefilled once through the same library; R copies of the pools
-("layers", at least two and at least 2 GB of cache) are cycled so that each
-step reads its KV from HBM, not from the 256 MB Infinity Cache.
+One step = the decode step of the hot path over one batch: store each
+sequence's new key/value token, split-K decode over the whole context, and
+the split-K reduce.  --mode fused (default) makes it one call of
+paged_attention_decode_step (the store inside the decode launch where the
+shape allows, then the reduce);
+--mode separate makes it paged_kv_write, paged_attention_decode_partials and
+paged_attention_splitk_reduce.  Per-kernel times always come from the
+separate launches.  The KV cache is prefilled once through the same library;
+R copies of the pools ("layers", at least two and at least 2 GB of cache)
+are cycled so that each step reads its KV from HBM, not from the 256 MB
+Infinity Cache.
 
 Prints ONE JSON line on stdout; details go to stderr.
 
-    python bench.py [--steps K] [--warmup W] [--config 3] [--gpus 1]
+    python bench.py [--steps K] [--warmup W] [--config 3] [--gpus 1] [--mode fused]
 """
 
 from __future__ import annotations
@@ -31,7 +36,9 @@ if ROOT not in sys.path:
 METRIC = "paged-attn decode µs/step + effective KV GB/s as % of MI355X HBM peak"
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, vendor figure
 ELEM = {"f32": 4, "bf16": 2, "fp8": 1}
-DECODE_SRC = os.path.join(ROOT, "paged_kv_cache_211_amd", "csrc", "decode.hip")
+# sources of the decode kernels: a counter file taken on other sources is stale
+SRC_FILES = ("decode.hip", "decode_valu.h", "decode_f32.hip", "decode_bf16.hip", "decode_fp8.hip",
+             "decode_mfma.hip", "decode_common.h", "pkv_device.h")
 
 
 def log(*a):
@@ -50,6 +57,7 @@ def parse():
     p.add_argument("--cpu-tokens", type=int, default=400_000,
                    help="token budget of the oracle's timed sample")
     p.add_argument("--traffic-file", default=None)
+    p.add_argument("--mode", choices=("fused", "separate"), default="fused")
     return p.parse_args()
 
 
@@ -68,22 +76,22 @@ def algorithmic_bytes(wl):
 
 def src_sha():
     h = hashlib.sha256()
-    for f in ("decode.hip", "decode_mfma.hip", "decode_common.h", "pkv_device.h"):
+    for f in SRC_FILES:
         with open(os.path.join(ROOT, "paged_kv_cache_211_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def load_traffic(path, workload_key, per_launch_alg):
-    """HBM bytes per decode launch from committed rocprofv3 counter runs, or
-    None when absent or taken on a different kernel source."""
+def load_traffic(path, workload_key, kernel):
+    """HBM bytes per launch of `kernel` from committed rocprofv3 counter runs,
+    or None when absent, for another kernel or taken on other sources."""
     path = path or os.path.join(ROOT, "profiles", f"traffic_{workload_key}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         t = json.load(f)
-    if t.get("kernel_src_sha") != src_sha():
-        log(f"traffic file {path} is for another kernel source; traffic = null")
+    if t.get("kernel_src_sha") != src_sha() or t.get("kernel") != kernel:
+        log(f"traffic file {path} is for another kernel or source; traffic = null")
         return None
     return t.get("hbm_bytes_per_launch")
 
@@ -185,7 +193,20 @@ def main():
     ws = cache.workspace(inp["total_partitions"], c.H_q, c.d) if P else None
     tab, lens = inp["block_tables"], inp["context_lens"]
 
-    def run(i, ev=None):
+    n_launch = pkv.paged_attention_decode_step_launches(c.H_q, c.H_kv, c.d, c.bs, q.dtype,
+                                                        cache.dtype, P)
+
+    def run_fused(i, ev=None):
+        kc, vc = layers[i % R]
+        if ev:
+            ev[0].record()
+        pkv.paged_attention_decode_step(out, q, key, value, kc, vc, tab, lens, c.scale, c.k_scale,
+                                        c.v_scale, P, inp["partition_offsets"],
+                                        inp["total_partitions"], ws)
+        if ev:
+            ev[1].record()
+
+    def run_separate(i, ev=None):
         kc, vc = layers[i % R]
         if ev:
             ev[0].record()
@@ -206,6 +227,8 @@ def main():
                 ev[2].record()
         if ev:
             ev[3].record()
+
+    run = run_fused if args.mode == "fused" else run_separate
 
     # streaming-copy reference (also the known-size kernel for counter scaling)
     copy_n = 1 << 30
@@ -238,27 +261,46 @@ def main():
     wall = time.perf_counter() - w0
     ms_step = e0.elapsed_time(e1) / args.steps
 
-    # region 2: the same K steps with an event around every kernel launch
+    # region 2: the separate launches, an event around each kernel
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    for i in range(args.warmup):
+        run_separate(i)
     torch.cuda.synchronize()
     for i in range(args.steps):
-        run(i, evs[i])
+        run_separate(i, evs[i])
     torch.cuda.synchronize()
     t_write = np.array([a.elapsed_time(b) for a, b, _, _ in evs]) * 1e3
     t_dec = np.array([b.elapsed_time(c2) for _, b, c2, _ in evs]) * 1e3
     t_red = np.array([c2.elapsed_time(d) for _, _, c2, d in evs]) * 1e3
     dec_us = float(np.mean(t_dec))
 
+    # region 3: the step entry alone, events around each call
+    fev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    for i in range(args.warmup):
+        run_fused(i)
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        run_fused(i, fev[i])
+    torch.cuda.synchronize()
+    t_fused = np.array([a.elapsed_time(b) for a, b in fev]) * 1e3
+    fused_us = float(np.mean(t_fused))
+
     us_step = ms_step * 1e3
     kv_gbps = ab["kv"] / (us_step * 1e-6) / 1e9
-    achieved = ab["decode"] / (dec_us * 1e-6) / 1e9
-    traffic = load_traffic(args.traffic_file, c.key, ab["decode"])
-    log(f"[bench] step {us_step:.1f} us (wall {wall / args.steps * 1e6:.1f} us); per kernel: "
+    if n_launch == 1:
+        # the step is one kernel (store inside the decode, no partitions)
+        kernel, kern_us, kern_bytes = "decode step (store + decode)", fused_us, ab["step"]
+    else:
+        kernel, kern_us, kern_bytes = "decode (split-K partials)" if P else "decode", dec_us, ab["decode"]
+    achieved = kern_bytes / (kern_us * 1e-6) / 1e9
+    traffic = load_traffic(args.traffic_file, c.key, kernel)
+    log(f"[bench] mode {args.mode}: step {us_step:.1f} us (wall {wall / args.steps * 1e6:.1f} us); "
+        f"step entry {fused_us:.1f} us in {n_launch} launch(es); separate launches: "
         f"write {np.mean(t_write):.1f} us, decode {dec_us:.1f} us "
         f"[p10 {np.percentile(t_dec, 10):.1f}, p90 {np.percentile(t_dec, 90):.1f}], "
         f"reduce {np.mean(t_red):.1f} us")
     log(f"[bench] KV {ab['kv'] / 1e9:.3f} GB/step -> {kv_gbps:.0f} GB/s = "
-        f"{100 * kv_gbps / HBM_PEAK_GBPS:.1f}% of {HBM_PEAK_GBPS:.0f}; decode kernel "
+        f"{100 * kv_gbps / HBM_PEAK_GBPS:.1f}% of {HBM_PEAK_GBPS:.0f}; {kernel} "
         f"{achieved:.0f} GB/s; device copy {copy_gbps:.0f} GB/s")
 
     cpu = None
@@ -284,22 +326,25 @@ def main():
         "config": {
             "workload": f"{c.key}: {c.S} seqs, {c.H_q}/{c.H_kv} heads, head_dim {c.d}, "
                         f"block_size {c.bs}, {c.kv_dtype} KV, context {wl.total_tokens} tokens "
-                        f"(seed {c.seed}), split-K {P}, {R} pool layers",
+                        f"(seed {c.seed}), split-K {P}, {R} pool layers, {args.mode} step",
             "global_batch": c.S,
             "seq_len": int(wl.context_lens.max()),
             "mean_context": round(float(wl.context_lens.mean()), 1),
             "parallelism": "single GPU",
+            "mode": args.mode,
+            "step_launches": n_launch if args.mode == "fused" else (3 if P else 2),
         },
         "kv_GBps": round(kv_gbps, 1),
         "pct_hbm_peak": round(100 * kv_gbps / HBM_PEAK_GBPS, 2),
         "step_algorithmic_bytes": ab["step"],
         "kernel_us": {"paged_kv_write": round(float(np.mean(t_write)), 2),
-                      "decode": round(dec_us, 2), "splitk_reduce": round(float(np.mean(t_red)), 2)},
+                      "decode": round(dec_us, 2), "splitk_reduce": round(float(np.mean(t_red)), 2),
+                      "decode_step_entry": round(fused_us, 2)},
         "device_copy_GBps": round(copy_gbps, 1),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                     "traffic": traffic, "kernel": "decode (split-K partials)",
-                     "algorithmic_bytes_per_launch": ab["decode"]},
+                     "traffic": traffic, "kernel": kernel,
+                     "algorithmic_bytes_per_launch": kern_bytes},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -163,6 +163,47 @@ int paged_attention_decode_partials(void* out, const void* query, const void* ke
                                     int total_partitions, void* workspace, size_t workspace_bytes,
                                     void* stream);
 
+/* paged_attention_decode_step -- one whole decode step: store each
+ * sequence's new key/value row, then attend over the context that now holds
+ * it ("Day 6/90 of Inference Engineering": a decode step appends its token to
+ * the sequence's last block, then attention reads every block of the table).
+ * The result equals paged_kv_write of the new rows followed by
+ * paged_attention_decode, with these differences:
+ *  new_key, new_value [num_seqs][num_kv_heads][head_dim] of q_dtype (device):
+ *                 row s is the token at position context_lens[s] - 1 of
+ *                 sequence s, stored into the slot that block_tables gives
+ *                 for that position (so the caller has already grown the
+ *                 table); a sequence of length 0, longer than its table or
+ *                 with an out-of-range block id gets no store.  bf16 rows
+ *                 go to an FP8 cache as E4M3FN(fp32(x) / k_scale) (v_scale
+ *                 for values), rounded as paged_kv_write rounds them.
+ *  key_cache, value_cache are written.
+ * When one workgroup reads each (sequence, kv head) partition -- the
+ * vector-ALU kernel with all G query heads of a kv head in one workgroup --
+ * that workgroup stores the new token before it reads the last block, so
+ * store and decode are one launch; otherwise a store launch precedes the
+ * decode.  With partitions the split-K reduce follows, as in
+ * paged_attention_decode.  Returns PKV_ERR_INVALID for a null new_key or
+ * new_value, else as paged_attention_decode. */
+int paged_attention_decode_step(void* out, const void* query, const void* new_key,
+                                const void* new_value, void* key_cache, void* value_cache,
+                                const int32_t* block_tables, int max_blocks_per_seq,
+                                const int32_t* context_lens, int num_seqs, int num_q_heads,
+                                int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                                float scale, pkv_dtype q_dtype, pkv_dtype cache_dtype,
+                                float k_scale, float v_scale, int partition_tokens,
+                                const int32_t* partition_offsets, int total_partitions,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
+/* paged_attention_decode_step_launches -- how many kernel launches
+ * paged_attention_decode_step makes for this shape: 1 (store inside the
+ * decode, no partitions) to 3 (store, decode, split-K reduce).  Returns a
+ * negative PKV_ERR_* for bad or unsupported arguments.  Host only; touches
+ * no device. */
+int paged_attention_decode_step_launches(int num_q_heads, int num_kv_heads, int head_dim,
+                                         int block_size, pkv_dtype q_dtype, pkv_dtype cache_dtype,
+                                         int partition_tokens);
+
 /* paged_attention_splitk_reduce -- combine the partials of every sequence
  * with more than one partition ("PagedAttention Kernel" article §3.2: uneven
  * pages need the work split): with running maxima m_p (log2 domain), sums

@@ -159,6 +159,42 @@ def paged_attention_decode_partials(out, query, key_cache, value_cache, block_ta
     check(lib().paged_attention_decode_partials(*args, _stream(stream)))
 
 
+def paged_attention_decode_step(out, query, new_key, new_value, key_cache, value_cache,
+                                block_tables, context_lens, scale, k_scale=1.0, v_scale=1.0,
+                                partition_tokens=0, partition_offsets=None, total_partitions=0,
+                                workspace=None, stream=None):
+    """Store each sequence's new key/value row (position context_lens[s]-1),
+    then decode, as paged_kv_write followed by paged_attention_decode."""
+    a = _decode_args(out, query, key_cache, value_cache, block_tables, context_lens, scale,
+                     k_scale, v_scale, partition_tokens, partition_offsets, total_partitions,
+                     workspace)
+    S, Hq, D = query.shape
+    H = key_cache.shape[1]
+    for t, n in ((new_key, "new_key"), (new_value, "new_value")):
+        _need(t, n)
+        if tuple(t.shape) != (S, H, D) or t.dtype != query.dtype:
+            raise PkvError(-1, f"{n} must be [S, H_kv, head_dim] of the query dtype")
+    check(lib().paged_attention_decode_step(a[0], a[1], _ptr(new_key), _ptr(new_value), *a[2:],
+                                            _stream(stream)))
+
+
+def paged_attention_decode_step_launches(num_q_heads, num_kv_heads, head_dim, block_size, q_dtype,
+                                         cache_dtype, partition_tokens=0) -> int:
+    """Kernel launches one decode step makes for this shape (1 = store inside the decode).
+    Dtypes are torch dtypes (torch.uint8 for an FP8 cache) or pkv_dtype codes."""
+    def code(t):
+        if isinstance(t, int):
+            return t
+        if t not in _CODES:
+            raise PkvError(-1, f"unsupported dtype {t}")
+        return _CODES[t]
+    n = lib().paged_attention_decode_step_launches(num_q_heads, num_kv_heads, head_dim, block_size,
+                                                   code(q_dtype), code(cache_dtype),
+                                                   int(partition_tokens))
+    check(min(n, 0))
+    return n
+
+
 def paged_attention_splitk_reduce(out, workspace, partition_offsets, total_partitions, stream=None):
     _need(out, "out")
     _need(workspace, "workspace")

@@ -22,7 +22,8 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libpkv.so")
 ARCH = "gfx950"
 
-SOURCES = ["api.cpp", "allocator.cpp", "kv_ops.hip", "decode.hip", "decode_mfma.hip"]
+SOURCES = ["api.cpp", "allocator.cpp", "kv_ops.hip", "decode.hip", "decode_f32.hip",
+           "decode_bf16.hip", "decode_fp8.hip", "decode_mfma.hip"]
 
 
 def hipcc() -> str:
@@ -32,29 +33,39 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (expected /opt/rocm/bin/hipcc)")
 
 
-def compile_cmd(out: str) -> list[str]:
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    return [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
-            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-            "-Wno-unused-command-line-argument",
-            "-I", INCLUDE, "-I", CSRC, *srcs, "-o", out]
+FLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
+         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-Wno-unused-command-line-argument"]
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source into libpkv.so (always recompiles)."""
-    fd, tmp = tempfile.mkstemp(prefix="libpkv.", suffix=".so.tmp", dir=PKG)
-    os.close(fd)
-    cmd = compile_cmd(tmp)
+def compile_cmd(src: str, obj: str) -> list[str]:
+    return [hipcc(), *FLAGS, "-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, src), "-o", obj]
+
+
+def _run(cmd: list[str], verbose: bool) -> None:
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
-        os.unlink(tmp)
-        raise RuntimeError(f"hipcc failed ({r.returncode}):\n{r.stdout}\n{r.stderr}")
+        raise RuntimeError(f"hipcc failed ({r.returncode}): {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
     noise = [l for l in r.stderr.splitlines() if "packed-fp32-ops" not in l and l.strip()]
     if verbose and noise:
         print("\n".join(noise), file=sys.stderr)
-    os.replace(tmp, LIB)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source (in parallel) and link libpkv.so; always recompiles."""
+    from concurrent.futures import ThreadPoolExecutor
+    with tempfile.TemporaryDirectory(prefix="pkv_build.", dir=PKG) as tmpdir:
+        objs = [os.path.join(tmpdir, os.path.splitext(src)[0] + ".o") for src in SOURCES]
+        workers = max(1, min(len(SOURCES), os.cpu_count() or 1, 16))
+        with ThreadPoolExecutor(workers) as pool:
+            for f in [pool.submit(_run, compile_cmd(src, obj), verbose)
+                      for src, obj in zip(SOURCES, objs)]:
+                f.result()
+        tmp = os.path.join(tmpdir, "libpkv.so")
+        _run([hipcc(), *FLAGS, "-shared", *objs, "-o", tmp], verbose)
+        os.replace(tmp, LIB)
     return LIB
 
 

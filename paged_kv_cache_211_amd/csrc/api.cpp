@@ -220,6 +220,68 @@ int paged_attention_decode_partials(void* out, const void* query, const void* ke
   return decode_common(c, false, stream);
 }
 
+int paged_attention_decode_step(void* out, const void* query, const void* new_key,
+                                const void* new_value, void* key_cache, void* value_cache,
+                                const int32_t* block_tables, int max_blocks_per_seq,
+                                const int32_t* context_lens, int num_seqs, int num_q_heads,
+                                int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                                float scale, pkv_dtype q_dtype, pkv_dtype cache_dtype,
+                                float k_scale, float v_scale, int partition_tokens,
+                                const int32_t* partition_offsets, int total_partitions,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  DecodeCall c{out, query, key_cache, value_cache, block_tables, max_blocks_per_seq, context_lens,
+               num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, scale,
+               q_dtype, cache_dtype, k_scale, v_scale, partition_tokens, partition_offsets,
+               total_partitions, workspace, workspace_bytes};
+  DecodeArgs a;
+  int rc = check_decode(c, &a);
+  if (rc) return rc;
+  if (!new_key || !new_value) return fail(PKV_ERR_INVALID, "null pointer argument");
+  if (num_seqs == 0) return PKV_OK;
+  a.new_k = new_key;
+  a.new_v = new_value;
+  if (cache_dtype == PKV_FP8_E4M3) {
+    a.k_inv = 1.f / k_scale;  // the same correctly rounded division as paged_kv_write
+    a.v_inv = 1.f / v_scale;
+  }
+  if (decode_step_stores_in_kernel(a)) {
+    rc = hip_status(launch_decode_step(a, stream), "paged_attention_decode_step launch");
+  } else {
+    // the slots of position context_lens[s] - 1 come from the tables, as in
+    // the one-launch form
+    rc = hip_status(launch_kv_write_tail(new_key, new_value, key_cache, value_cache, block_tables,
+                                         max_blocks_per_seq, context_lens, num_seqs, num_kv_heads,
+                                         head_dim, block_size, num_blocks, cache_dtype, a.k_inv,
+                                         a.v_inv, stream),
+                    "paged_attention_decode_step store launch");
+    if (!rc) rc = hip_status(launch_decode(a, stream), "paged_attention_decode_step launch");
+  }
+  if (rc || partition_tokens == 0) return rc;
+  return hip_status(launch_splitk_reduce(out, a.ws, partition_offsets, num_seqs, num_q_heads,
+                                         head_dim, total_partitions, q_dtype, stream),
+                    "paged_attention_splitk_reduce launch");
+}
+
+int paged_attention_decode_step_launches(int num_q_heads, int num_kv_heads, int head_dim,
+                                         int block_size, pkv_dtype q_dtype, pkv_dtype cache_dtype,
+                                         int partition_tokens) {
+  if (num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0 ||
+      partition_tokens < 0 || !valid_dtype(q_dtype) || !valid_dtype(cache_dtype))
+    return fail(PKV_ERR_INVALID, "bad arguments");
+  if (!decode_supported(q_dtype, cache_dtype, head_dim, block_size, num_q_heads / num_kv_heads))
+    return fail(PKV_ERR_UNSUPPORTED, "unsupported decode shape");
+  DecodeArgs a{};
+  a.Hq = num_q_heads;
+  a.Hkv = num_kv_heads;
+  a.D = head_dim;
+  a.BS = block_size;
+  a.partition = partition_tokens;
+  a.q_dtype = q_dtype;
+  a.kv_dtype = cache_dtype;
+  clear_error();
+  return (decode_step_stores_in_kernel(a) ? 1 : 2) + (partition_tokens > 0 ? 1 : 0);
+}
+
 int paged_attention_splitk_reduce(void* out, const void* workspace, size_t workspace_bytes,
                                   const int32_t* partition_offsets, int num_seqs,
                                   int num_q_heads, int head_dim, int total_partitions,

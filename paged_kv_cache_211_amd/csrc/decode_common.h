@@ -20,6 +20,9 @@
 #ifndef PKV_DECODE_DEPTH
 #define PKV_DECODE_DEPTH 1
 #endif
+#ifndef PKV_DECODE_PER_WAVE
+#define PKV_DECODE_PER_WAVE 0
+#endif
 #ifndef PKV_DECODE_QLDS
 #define PKV_DECODE_QLDS 0
 #endif
@@ -31,6 +34,10 @@ namespace pkv {
 namespace dec {
 
 constexpr int kWaves = PKV_DECODE_WAVES;
+// PKV_DECODE_PER_WAVE = 1: one work item per wave instead of per workgroup
+// (the decode step then stores the new tokens with a launch of its own).
+constexpr bool kPerWave = PKV_DECODE_PER_WAVE;
+
 constexpr int kBufs = PKV_DECODE_DEPTH + 1;      // tiles in registers per wave (VALU kernel)
 constexpr int kMfmaBufs = PKV_MFMA_DEPTH + 1;    // same, matrix-core kernel
 
@@ -62,13 +69,17 @@ struct Work {
   int nparts;  // partitions of that sequence
   int t0, t1;  // token range [t0, t1) of this partition
   int jend;    // one past the last block of the range
+  int L;       // context length (clamped to the table)
+  int p0;      // first flat partition of the sequence (SPLIT)
   int hkv;     // kv head
   int qh0;     // first query head of the group
   bool bad;    // length out of range: the output becomes NaN
 };
 
+// `item` is the flat work index: the split-K partition (SPLIT) or the
+// sequence (one pass).
 template <bool SPLIT, int BS>
-__device__ __forceinline__ Work locate(const DecodeArgs& a, int hpw, int lane) {
+__device__ __forceinline__ Work locate(const DecodeArgs& a, int hpw, int lane, int item) {
   Work wk;
   const int G = a.Hq / a.Hkv;
   const int groups = G / hpw;
@@ -76,12 +87,13 @@ __device__ __forceinline__ Work locate(const DecodeArgs& a, int hpw, int lane) {
   wk.qh0 = wk.hkv * G + (blockIdx.y % groups) * hpw;
   int part;
   if constexpr (SPLIT) {
-    wk.s = __builtin_amdgcn_readfirstlane(find_seq(a.part_off, a.S, blockIdx.x, lane));
-    const int p0 = a.part_off[wk.s];
-    part = blockIdx.x - p0;
-    wk.nparts = a.part_off[wk.s + 1] - p0;
+    wk.s = __builtin_amdgcn_readfirstlane(find_seq(a.part_off, a.S, item, lane));
+    wk.p0 = a.part_off[wk.s];
+    part = item - wk.p0;
+    wk.nparts = a.part_off[wk.s + 1] - wk.p0;
   } else {
-    wk.s = blockIdx.x;
+    wk.s = item;
+    wk.p0 = item;
     part = 0;
     wk.nparts = 1;
   }
@@ -89,6 +101,7 @@ __device__ __forceinline__ Work locate(const DecodeArgs& a, int hpw, int lane) {
   wk.bad = false;
   if (L < 0) { L = 0; wk.bad = true; }
   if (L > a.max_blocks * BS) { L = a.max_blocks * BS; wk.bad = true; }
+  wk.L = L;
   wk.t0 = SPLIT ? part * a.partition : 0;
   wk.t1 = SPLIT ? min(L, wk.t0 + a.partition) : L;
   wk.jend = (wk.t1 + BS - 1) / BS;
@@ -203,6 +216,28 @@ __device__ __forceinline__ void merge_store(const DecodeArgs& a, const Work& wk,
       }
     }
   }
+}
+
+// Decode step: the workgroup that reads the last block of the sequence
+// first stores the sequence's new token, position L - 1, into the slot its
+// table gives for that position.  Only this workgroup reads that block in the
+// launch (one workgroup per kv head), so waiting for the stores to complete
+// and a workgroup barrier order them before every tile load.
+template <int KV, int D, int BS, int NTHREADS>
+__device__ __forceinline__ void store_new_token(const DecodeArgs& a, const Work& wk) {
+  constexpr int X = 16 / (KV == PKV_F32 ? 4 : KV == PKV_BF16 ? 2 : 1);
+  if (!wk.bad && wk.L > 0 && wk.t0 < wk.L && wk.t1 == wk.L) {
+    const int pos = wk.L - 1;
+    const int blk = a.tables[(size_t)wk.s * a.max_blocks + pos / BS];
+    if ((unsigned)blk < (unsigned)a.nb) {
+      const int slot = blk * BS + pos % BS;
+      for (int c = threadIdx.x; c < D / X; c += NTHREADS)
+        write_kv_unit<KV>(a.new_k, a.new_v, (uint8_t*)a.kc, (uint8_t*)a.vc, wk.s, wk.hkv, c, slot,
+                          a.Hkv, D, BS, a.k_inv, a.v_inv);
+      __builtin_amdgcn_s_waitcnt(0);
+    }
+  }
+  __syncthreads();
 }
 
 }  // namespace dec

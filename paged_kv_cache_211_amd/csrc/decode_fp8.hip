@@ -1,0 +1,9 @@
+// Vector-ALU decode kernels for fp8 key/value caches.
+#include "decode_valu.h"
+
+namespace pkv {
+namespace valu {
+template int launch_valu<PKV_FP8_E4M3>(const DecodeArgs&, bool, hipStream_t);
+template int valu_heads_per_wg<PKV_FP8_E4M3>(const DecodeArgs&);
+}  // namespace valu
+}  // namespace pkv

@@ -52,7 +52,10 @@ __device__ __forceinline__ bf16x8 fp8x8_to_bf16(uint32_t w0, uint32_t w1) {
 // Each wave owns one work item: (sequence, partition) for the kv head of
 // blockIdx.y, flat item blockIdx.x * NW + wave.  Waves never synchronise;
 // a wave writes its own output (one-partition sequence) or partial.
-template <int NW, int NBUF, bool SPLIT>
+// STORE (decode step, one group of 8 query heads per kv head): the wave that
+// reads a sequence's last block first stores the sequence's new token there;
+// it is that block's only reader, so waiting for its own stores suffices.
+template <int NW, int NBUF, bool SPLIT, bool STORE = false>
 __global__ __launch_bounds__(NW * 64) void decode_mfma_fp8_kernel(const DecodeArgs a) {
   constexpr int D = 128, BS = 32, HPW = 8;
   constexpr int TILE = BS * D;          // bytes of an fp8 (block, kv head) tile
@@ -90,6 +93,16 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_fp8_kernel(const DecodeAr
   const int t1 = SPLIT ? min(L, t0 + a.partition) : L;
   const int jend = (t1 + BS - 1) / BS;
   const int32_t* __restrict__ tbl = a.tables + (size_t)s * a.max_blocks;
+  if constexpr (STORE) {
+    if (!bad && L > 0 && t0 < L && t1 == L) {
+      const int pos = L - 1;
+      const int blk = tbl[pos / BS];
+      if ((unsigned)blk < (unsigned)a.nb && lane < D / 16)
+        write_kv_unit<PKV_FP8_E4M3>(a.new_k, a.new_v, (uint8_t*)a.kc, (uint8_t*)a.vc, s, hkv, lane,
+                                    blk * BS + pos % BS, a.Hkv, D, BS, a.k_inv, a.v_inv);
+      __builtin_amdgcn_s_waitcnt(0);
+    }
+  }
   const size_t head_off = (size_t)hkv * TILE;
   const size_t blk_stride = (size_t)a.Hkv * TILE;
 
@@ -238,16 +251,24 @@ bool decode_mfma_eligible(const DecodeArgs& a) {
          (a.Hq / a.Hkv) % 8 == 0;
 }
 
-int launch_decode_mfma(const DecodeArgs& a, void* stream) {
+int launch_decode_mfma(const DecodeArgs& a, void* stream, bool store) {
   hipStream_t st = (hipStream_t)stream;
   const int groups = a.Hq / a.Hkv / 8;
+  if (store && groups != 1) return (int)hipErrorInvalidValue;
   dim3 block(kWaves * 64);
   const int items = a.partition > 0 ? a.total_parts : a.S;
   dim3 grid((items + kWaves - 1) / kWaves, a.Hkv * groups);
-  if (a.partition > 0)
-    hipLaunchKernelGGL((decode_mfma_fp8_kernel<kWaves, kMfmaBufs, true>), grid, block, 0, st, a);
-  else
-    hipLaunchKernelGGL((decode_mfma_fp8_kernel<kWaves, kMfmaBufs, false>), grid, block, 0, st, a);
+  if (a.partition > 0) {
+    if (store)
+      hipLaunchKernelGGL((decode_mfma_fp8_kernel<kWaves, kMfmaBufs, true, true>), grid, block, 0, st, a);
+    else
+      hipLaunchKernelGGL((decode_mfma_fp8_kernel<kWaves, kMfmaBufs, true>), grid, block, 0, st, a);
+  } else {
+    if (store)
+      hipLaunchKernelGGL((decode_mfma_fp8_kernel<kWaves, kMfmaBufs, false, true>), grid, block, 0, st, a);
+    else
+      hipLaunchKernelGGL((decode_mfma_fp8_kernel<kWaves, kMfmaBufs, false>), grid, block, 0, st, a);
+  }
   return (int)hipGetLastError();
 }
 

@@ -37,47 +37,36 @@ __global__ __launch_bounds__(256) void kv_write_kernel(const void* __restrict__ 
   const int t = (int)(gid / ((long)units * H));
   const int slot = slots[t];
   if (slot < 0 || slot >= nb * BS) return;
-  const int b = slot / BS, o = slot % BS;
-  const size_t row = ((size_t)t * H + h) * D + (size_t)c * X;   // first source element
-  const size_t kdst = ((((size_t)b * H + h) * (D / X) + c) * BS + o) * 16;
-  const size_t vdst0 = (((size_t)b * H + h) * D + (size_t)c * X) * BS + o;  // element index
+  write_kv_unit<CACHE>(key, value, kc, vc, t, h, c, slot, H, D, BS, k_inv, v_inv);
+}
 
-  if constexpr (CACHE == PKV_F32) {
-    const f32x4 k4 = *(const f32x4*)((const float*)key + row);
-    const f32x4 v4 = *(const f32x4*)((const float*)value + row);
-    *(f32x4*)(kc + kdst) = k4;
-    float* vd = (float*)vc + vdst0;
-    vd[0] = v4.x; vd[BS] = v4.y; vd[2 * BS] = v4.z; vd[3 * BS] = v4.w;
-  } else if constexpr (CACHE == PKV_BF16) {
-    const u32x4 k8 = *(const u32x4*)((const uint16_t*)key + row);
-    const u32x4 v8 = *(const u32x4*)((const uint16_t*)value + row);
-    *(u32x4*)(kc + kdst) = k8;
-    uint16_t* vd = (uint16_t*)vc + vdst0;
-    const uint32_t vw[4] = {v8.x, v8.y, v8.z, v8.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      vd[(2 * i) * BS] = (uint16_t)(vw[i] & 0xffffu);
-      vd[(2 * i + 1) * BS] = (uint16_t)(vw[i] >> 16);
-    }
-  } else {  // bf16 -> fp8 E4M3FN, quantise on write
-    const uint16_t* ks = (const uint16_t*)key + row;
-    const uint16_t* vs = (const uint16_t*)value + row;
-    const u32x4 ka = *(const u32x4*)ks, kb = *(const u32x4*)(ks + 8);
-    const u32x4 va = *(const u32x4*)vs, vb = *(const u32x4*)(vs + 8);
-    const uint32_t kw[8] = {ka.x, ka.y, ka.z, ka.w, kb.x, kb.y, kb.z, kb.w};
-    const uint32_t vw[8] = {va.x, va.y, va.z, va.w, vb.x, vb.y, vb.z, vb.w};
-    uint32_t kout[4] = {0, 0, 0, 0};
-    uint8_t* vd = vc + vdst0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const uint32_t k0 = f32_to_e4m3(bf16_lo(kw[i]) * k_inv);
-      const uint32_t k1 = f32_to_e4m3(bf16_hi(kw[i]) * k_inv);
-      kout[i / 2] |= (k0 | (k1 << 8)) << (16 * (i % 2));
-      vd[(2 * i) * BS] = (uint8_t)f32_to_e4m3(bf16_lo(vw[i]) * v_inv);
-      vd[(2 * i + 1) * BS] = (uint8_t)f32_to_e4m3(bf16_hi(vw[i]) * v_inv);
-    }
-    *(u32x4*)(kc + kdst) = u32x4{kout[0], kout[1], kout[2], kout[3]};
-  }
+// Decode-step scatter: one thread per (sequence, kv head, key unit); row s
+// of key/value is sequence s's new token, stored at position lens[s] - 1 in
+// the slot its block table gives.  Sequences of length 0, beyond the table or
+// with an out-of-range block id are skipped.
+template <int CACHE>
+__global__ __launch_bounds__(256) void kv_write_tail_kernel(const void* __restrict__ key,
+                                                            const void* __restrict__ value,
+                                                            uint8_t* __restrict__ kc,
+                                                            uint8_t* __restrict__ vc,
+                                                            const int32_t* __restrict__ tables,
+                                                            int max_blocks,
+                                                            const int32_t* __restrict__ lens, int S,
+                                                            int H, int D, int BS, int nb,
+                                                            float k_inv, float v_inv) {
+  constexpr int X = 16 / (CACHE == PKV_F32 ? 4 : CACHE == PKV_BF16 ? 2 : 1);
+  const int units = D / X;
+  const long gid = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= (long)S * H * units) return;
+  const int c = (int)(gid % units);
+  const int h = (int)((gid / units) % H);
+  const int s = (int)(gid / ((long)units * H));
+  const int L = lens[s];
+  if (L <= 0 || L > max_blocks * BS) return;
+  const int pos = L - 1;
+  const int blk = tables[(size_t)s * max_blocks + pos / BS];
+  if ((unsigned)blk >= (unsigned)nb) return;
+  write_kv_unit<CACHE>(key, value, kc, vc, s, h, c, blk * BS + pos % BS, H, D, BS, k_inv, v_inv);
 }
 
 // One workgroup per (pair, pool): copies block_bytes from block src to dst.
@@ -159,6 +148,28 @@ int launch_kv_write(const void* key, const void* value, void* kc, void* vc, cons
   else
     hipLaunchKernelGGL((kv_write_kernel<PKV_BF16, PKV_FP8_E4M3>), grid, block, 0, st, key, value,
                        (uint8_t*)kc, (uint8_t*)vc, slots, T, H, D, BS, nb, k_inv, v_inv);
+  return (int)hipGetLastError();
+}
+
+int launch_kv_write_tail(const void* key, const void* value, void* kc, void* vc,
+                         const int32_t* tables, int max_blocks, const int32_t* lens, int S, int H,
+                         int D, int BS, int nb, pkv_dtype cache, float k_inv, float v_inv,
+                         void* stream) {
+  hipStream_t st = (hipStream_t)stream;
+  const int X = 16 / elem_bytes(cache);
+  const long n = (long)S * H * (D / X);
+  if (n == 0) return 0;
+  dim3 grid((unsigned)((n + 255) / 256)), block(256);
+  auto k8 = (uint8_t*)kc, v8 = (uint8_t*)vc;
+  if (cache == PKV_F32)
+    hipLaunchKernelGGL((kv_write_tail_kernel<PKV_F32>), grid, block, 0, st, key, value, k8, v8,
+                       tables, max_blocks, lens, S, H, D, BS, nb, k_inv, v_inv);
+  else if (cache == PKV_BF16)
+    hipLaunchKernelGGL((kv_write_tail_kernel<PKV_BF16>), grid, block, 0, st, key, value, k8, v8,
+                       tables, max_blocks, lens, S, H, D, BS, nb, k_inv, v_inv);
+  else
+    hipLaunchKernelGGL((kv_write_tail_kernel<PKV_FP8_E4M3>), grid, block, 0, st, key, value, k8,
+                       v8, tables, max_blocks, lens, S, H, D, BS, nb, k_inv, v_inv);
   return (int)hipGetLastError();
 }
 

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "pkv.h"
+
 namespace pkv {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -111,6 +113,63 @@ __device__ __forceinline__ float max_xor16(float v) {
 // fp32 -> bf16 bits with the hardware conversion (round to nearest even).
 __device__ __forceinline__ uint16_t cvt_bf16(float f) {
   return __builtin_bit_cast(uint16_t, (__bf16)f);
+}
+
+// ---- slot scatter of one 16-byte key unit and the matching value elements ----
+// Token t's kv head h, key unit c (elements c*X .. c*X+X-1 of the row) goes to
+// slot `slot` = block * BS + offset.  Pool layout: key [NB][H][D/X][BS][X],
+// value [NB][H][D][BS] (X = 16 / element size of the cache).  CACHE selects
+// the stored type; bf16 -> fp8 stores E4M3FN(fp32(x) * inv) (k_inv for keys,
+// v_inv for values).  The caller has checked 0 <= slot < NB * BS.
+template <int CACHE>
+__device__ __forceinline__ void write_kv_unit(const void* __restrict__ key,
+                                              const void* __restrict__ value,
+                                              uint8_t* __restrict__ kc, uint8_t* __restrict__ vc,
+                                              int t, int h, int c, int slot, int H, int D, int BS,
+                                              float k_inv, float v_inv) {
+  constexpr int E = CACHE == PKV_F32 ? 4 : CACHE == PKV_BF16 ? 2 : 1;
+  constexpr int X = 16 / E;
+  const int b = slot / BS, o = slot % BS;
+  const size_t row = ((size_t)t * H + h) * D + (size_t)c * X;   // first source element
+  const size_t kdst = ((((size_t)b * H + h) * (D / X) + c) * BS + o) * 16;
+  const size_t vdst0 = (((size_t)b * H + h) * D + (size_t)c * X) * BS + o;  // element index
+
+  if constexpr (CACHE == PKV_F32) {
+    const f32x4 k4 = *(const f32x4*)((const float*)key + row);
+    const f32x4 v4 = *(const f32x4*)((const float*)value + row);
+    *(f32x4*)(kc + kdst) = k4;
+    float* vd = (float*)vc + vdst0;
+    vd[0] = v4.x; vd[BS] = v4.y; vd[2 * BS] = v4.z; vd[3 * BS] = v4.w;
+  } else if constexpr (CACHE == PKV_BF16) {
+    const u32x4 k8 = *(const u32x4*)((const uint16_t*)key + row);
+    const u32x4 v8 = *(const u32x4*)((const uint16_t*)value + row);
+    *(u32x4*)(kc + kdst) = k8;
+    uint16_t* vd = (uint16_t*)vc + vdst0;
+    const uint32_t vw[4] = {v8.x, v8.y, v8.z, v8.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      vd[(2 * i) * BS] = (uint16_t)(vw[i] & 0xffffu);
+      vd[(2 * i + 1) * BS] = (uint16_t)(vw[i] >> 16);
+    }
+  } else {  // bf16 -> fp8 E4M3FN, quantise on write
+    const uint16_t* ks = (const uint16_t*)key + row;
+    const uint16_t* vs = (const uint16_t*)value + row;
+    const u32x4 ka = *(const u32x4*)ks, kb = *(const u32x4*)(ks + 8);
+    const u32x4 va = *(const u32x4*)vs, vb = *(const u32x4*)(vs + 8);
+    const uint32_t kw[8] = {ka.x, ka.y, ka.z, ka.w, kb.x, kb.y, kb.z, kb.w};
+    const uint32_t vw[8] = {va.x, va.y, va.z, va.w, vb.x, vb.y, vb.z, vb.w};
+    uint32_t kout[4] = {0, 0, 0, 0};
+    uint8_t* vd = vc + vdst0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t k0 = f32_to_e4m3(bf16_lo(kw[i]) * k_inv);
+      const uint32_t k1 = f32_to_e4m3(bf16_hi(kw[i]) * k_inv);
+      kout[i / 2] |= (k0 | (k1 << 8)) << (16 * (i % 2));
+      vd[(2 * i) * BS] = (uint8_t)f32_to_e4m3(bf16_lo(vw[i]) * v_inv);
+      vd[(2 * i + 1) * BS] = (uint8_t)f32_to_e4m3(bf16_hi(vw[i]) * v_inv);
+    }
+    *(u32x4*)(kc + kdst) = u32x4{kout[0], kout[1], kout[2], kout[3]};
+  }
 }
 
 }  // namespace pkv

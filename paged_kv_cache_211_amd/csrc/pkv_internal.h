@@ -33,14 +33,26 @@ struct DecodeArgs {
   float qk_mult;            // scale * k_scale * log2(e): scores in the log2 domain
   float v_mult;             // v_scale for fp8, else 1
   pkv_dtype q_dtype, kv_dtype;
+  // Decode step (paged_attention_decode_step): row s of new_k / new_v is the
+  // new token of sequence s (position lens[s] - 1), stored by the workgroup
+  // that reads the sequence's last block.  Null otherwise.
+  const void* new_k = nullptr;
+  const void* new_v = nullptr;
+  float k_inv = 1.f, v_inv = 1.f;
 };
 
 // Kernel launchers (decode.hip, kv_ops.hip).  Return hipError_t as int.
 int launch_decode(const DecodeArgs& a, void* stream);
+// Decode step (decode.hip): whether the decode launch itself can store the
+// new tokens (one workgroup -- one wave on the matrix-core path -- per kv
+// head and partition), and that launch; otherwise the caller stores them
+// with launch_kv_write_tail first.
+bool decode_step_stores_in_kernel(const DecodeArgs& a);
+int launch_decode_step(const DecodeArgs& a, void* stream);
 // Matrix-core decode for fp8 key/value tiles with query heads in groups of 8
 // (decode_mfma.hip); launch_decode routes eligible calls there.
 bool decode_mfma_eligible(const DecodeArgs& a);
-int launch_decode_mfma(const DecodeArgs& a, void* stream);
+int launch_decode_mfma(const DecodeArgs& a, void* stream, bool store = false);
 int launch_splitk_reduce(void* out, const float* ws, const int32_t* part_off, int S, int Hq, int D,
                          int total_parts, pkv_dtype out_dtype, void* stream);
 bool decode_supported(pkv_dtype q, pkv_dtype kv, int D, int BS, int G);
@@ -48,6 +60,10 @@ bool decode_supported(pkv_dtype q, pkv_dtype kv, int D, int BS, int G);
 int launch_kv_write(const void* key, const void* value, void* kc, void* vc, const int32_t* slots,
                     int T, int H, int D, int BS, int nb, pkv_dtype src, pkv_dtype cache,
                     float k_inv, float v_inv, void* stream);
+int launch_kv_write_tail(const void* key, const void* value, void* kc, void* vc,
+                         const int32_t* tables, int max_blocks, const int32_t* lens, int S, int H,
+                         int D, int BS, int nb, pkv_dtype cache, float k_inv, float v_inv,
+                         void* stream);
 int launch_copy_blocks(void* kc, void* vc, const int32_t* pairs, int n, size_t block_bytes,
                        int nb, void* stream);
 int launch_read_probe(const void* src, size_t bytes, void* sink, int blocks, void* stream);

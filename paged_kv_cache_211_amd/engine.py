@@ -12,8 +12,9 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-from . import (BlockAllocator, empty_pools, paged_attention_decode, paged_attention_partition_offsets,
-               paged_attention_workspace_bytes, paged_kv_copy_blocks, paged_kv_write)
+from . import (BlockAllocator, empty_pools, paged_attention_decode, paged_attention_decode_step,
+               paged_attention_partition_offsets, paged_attention_workspace_bytes,
+               paged_kv_copy_blocks, paged_kv_write)
 
 
 class PagedKVCache:
@@ -38,12 +39,13 @@ class PagedKVCache:
     def fork(self, parent: int, child: int):
         self.alloc.fork(parent, child)
 
-    def append_many(self, items, stream=None):
+    def append_many(self, items, stream=None, write=True):
         """items: [(seq, key [n, H, D], value [n, H, D]), ...] (device tensors).
 
         Allocates every token on the host, applies the copy-on-write block
-        copies, then scatters all rows with one write.  Returns the slot
-        mapping (numpy int32) in item order.
+        copies, then scatters all rows with one write (skipped with
+        write=False: a fused decode step stores them itself).  Returns the
+        slot mapping (numpy int32) in item order.
         """
         slots, cows, keys, vals = [], [], [], []
         for seq, k, v in items:
@@ -58,7 +60,7 @@ class PagedKVCache:
             pairs = torch.from_numpy(np.concatenate(cows).astype(np.int32)).to(self.device)
             paged_kv_copy_blocks(self.key_cache, self.value_cache, pairs, stream=stream)
         sl = np.concatenate(slots).astype(np.int32) if slots else np.zeros(0, np.int32)
-        if keys:
+        if keys and write:
             K = torch.cat(keys) if len(keys) > 1 else keys[0]
             V = torch.cat(vals) if len(vals) > 1 else vals[0]
             self.write(K.contiguous(), V.contiguous(), torch.from_numpy(sl).to(self.device), stream)
@@ -98,6 +100,38 @@ class PagedKVCache:
         if self._ws is None or self._ws.numel() < need:
             self._ws = torch.empty(max(need, 16), dtype=torch.uint8, device=self.device)
         return self._ws
+
+    def reserve_step(self, seqs, stream=None):
+        """Allocate one new token for each sequence (copy-on-write included)
+        without storing it; returns the slots.  decode_step stores the rows."""
+        slots, cows = [], []
+        for seq in seqs:
+            sl, c = self.alloc.append(seq, 1)
+            slots.append(sl)
+            if len(c):
+                cows.append(c)
+        if cows:
+            pairs = torch.from_numpy(np.concatenate(cows).astype(np.int32)).to(self.device)
+            paged_kv_copy_blocks(self.key_cache, self.value_cache, pairs, stream=stream)
+        return np.concatenate(slots).astype(np.int32) if slots else np.zeros(0, np.int32)
+
+    def decode_step(self, query, new_key, new_value, inp, scale, out=None, stream=None):
+        """Store row s of new_key/new_value as the last token of the s-th
+        sequence of inp (already reserved), then decode; the store runs inside
+        the decode launch where the kernel allows."""
+        S, Hq, D = query.shape
+        out = torch.empty_like(query) if out is None else out
+        ws = None
+        if inp["partition_tokens"]:
+            ws = self.workspace(inp["total_partitions"], Hq, D)
+        paged_attention_decode_step(out, query, new_key, new_value, self.key_cache,
+                                    self.value_cache, inp["block_tables"], inp["context_lens"],
+                                    scale, k_scale=self.k_scale, v_scale=self.v_scale,
+                                    partition_tokens=inp["partition_tokens"],
+                                    partition_offsets=inp["partition_offsets"],
+                                    total_partitions=inp["total_partitions"], workspace=ws,
+                                    stream=stream)
+        return out
 
     def decode(self, query, inp, scale, out=None, stream=None):
         S, Hq, D = query.shape

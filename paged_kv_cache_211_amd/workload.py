@@ -62,11 +62,12 @@ def run_ops(cache, wl, ops, device="cuda", flush_tokens=1 << 22):
     _flush(cache, items)
 
 
-def build(wl, poison=True, device="cuda"):
-    """Prefill through the library, then allocate and write the decode step.
+def build(wl, poison=True, device="cuda", write_step=True):
+    """Prefill through the library, then allocate and write the decode step
+    (write_step=False: allocate it only, for a fused step to store).
 
     Returns (cache, step) where step holds the decode-step slot mapping and
-    new key/value rows (device) and the query.
+    new key/value rows (device, row s = sequence s) and the query.
     """
     from .engine import PagedKVCache
     c = wl.cfg
@@ -83,8 +84,9 @@ def build(wl, poison=True, device="cuda"):
         vs.append(v)
     K = to_dev(np.concatenate(ks), c.src_dtype, device)
     V = to_dev(np.concatenate(vs), c.src_dtype, device)
+    assert [op[1] for op in wl.decode] == list(range(len(wl.decode))), "one token per sequence, in order"
     items = [(op[1], K[i:i + 1], V[i:i + 1]) for i, op in enumerate(wl.decode)]
-    slots = cache.append_many(items)
+    slots = cache.append_many(items, write=write_step)
     step = {"slots": slots, "slots_dev": torch.from_numpy(slots).to(device), "key": K, "value": V,
             "query": to_dev(wl.q, c.q_dtype, device)}
     return cache, step
