@@ -58,6 +58,9 @@ def parse():
                    help="token budget of the oracle's timed sample")
     p.add_argument("--traffic-file", default=None)
     p.add_argument("--mode", choices=("fused", "separate"), default="fused")
+    p.add_argument("--schedule", choices=("splitk", "streamk"), default="splitk",
+                   help="split-K partitions of --partition tokens, or stream-K persistent waves")
+    p.add_argument("--workers", type=int, default=0, help="stream-K waves (0 = resident count)")
     return p.parse_args()
 
 
@@ -187,22 +190,38 @@ def main():
         layers.append((cache.key_cache.clone(), cache.value_cache.clone()))
     log(f"[bench] {R} pool layers of {pool_bytes / 1e9:.2f} GB")
 
-    inp = cache.decode_inputs(range(c.S), P)
+    SK = args.schedule == "streamk"
+    if SK:
+        P = 0
+        inp = cache.decode_inputs(range(c.S), streamk=True, num_q_heads=c.H_q,
+                                  q_dtype=W.TORCH_CACHE[c.q_dtype], workers=args.workers or None)
+        ws = cache.streamk_workspace(inp, c.H_q)
+        log(f"[bench] stream-K: {inp['workers']} waves over {inp['total_tiles']} tiles per head group")
+    else:
+        inp = cache.decode_inputs(range(c.S), P)
+        ws = cache.workspace(inp["total_partitions"], c.H_q, c.d) if P else None
     q, key, value, slots = step["query"], step["key"], step["value"], step["slots_dev"]
     out = torch.empty_like(q)
-    ws = cache.workspace(inp["total_partitions"], c.H_q, c.d) if P else None
     tab, lens = inp["block_tables"], inp["context_lens"]
-
-    n_launch = pkv.paged_attention_decode_step_launches(c.H_q, c.H_kv, c.d, c.bs, q.dtype,
-                                                        cache.dtype, P)
+    if SK:
+        n_launch = 2 if pkv.paged_attention_decode_step_launches(c.H_q, c.H_kv, c.d, c.bs, q.dtype,
+                                                                 cache.dtype, 0) == 1 else 3
+    else:
+        n_launch = pkv.paged_attention_decode_step_launches(c.H_q, c.H_kv, c.d, c.bs, q.dtype,
+                                                            cache.dtype, P)
 
     def run_fused(i, ev=None):
         kc, vc = layers[i % R]
         if ev:
             ev[0].record()
-        pkv.paged_attention_decode_step(out, q, key, value, kc, vc, tab, lens, c.scale, c.k_scale,
-                                        c.v_scale, P, inp["partition_offsets"],
-                                        inp["total_partitions"], ws)
+        if SK:
+            pkv.paged_attention_decode_step_streamk(out, q, key, value, kc, vc, tab, lens, c.scale,
+                                                    inp["tile_offsets"], inp["total_tiles"],
+                                                    inp["workers"], ws, c.k_scale, c.v_scale)
+        else:
+            pkv.paged_attention_decode_step(out, q, key, value, kc, vc, tab, lens, c.scale,
+                                            c.k_scale, c.v_scale, P, inp["partition_offsets"],
+                                            inp["total_partitions"], ws)
         if ev:
             ev[1].record()
 
@@ -213,7 +232,15 @@ def main():
         pkv.paged_kv_write(key, value, kc, vc, slots, k_scale=c.k_scale, v_scale=c.v_scale)
         if ev:
             ev[1].record()
-        if P:
+        if SK:
+            pkv.paged_attention_decode_streamk_partials(out, q, kc, vc, tab, lens, c.scale,
+                                                        inp["tile_offsets"], inp["total_tiles"],
+                                                        inp["workers"], ws, c.k_scale, c.v_scale)
+            if ev:
+                ev[2].record()
+            pkv.paged_attention_streamk_reduce(out, ws, inp["tile_offsets"], inp["total_tiles"],
+                                               inp["workers"], c.H_kv, c.bs, cache.dtype)
+        elif P:
             pkv.paged_attention_decode_partials(out, q, kc, vc, tab, lens, c.scale, c.k_scale,
                                                 c.v_scale, P, inp["partition_offsets"],
                                                 inp["total_partitions"], ws)
@@ -243,7 +270,20 @@ def main():
     ce1.record()
     torch.cuda.synchronize()
     copy_gbps = 2 * copy_n * 5 / (ce0.elapsed_time(ce1) * 1e-3) / 1e9
-    del src_b, dst_b
+    del dst_b
+    # attainable streaming-read rate of this GPU: the library's read probe
+    # (16-byte non-temporal loads, 32768 workgroups) over 1 GiB
+    sink = torch.zeros(4, dtype=torch.int32, device=dev)
+    for _ in range(2):
+        pkv.pkv_hbm_read_probe(src_b, sink, 32768)
+    torch.cuda.synchronize()
+    ce0.record()
+    for _ in range(5):
+        pkv.pkv_hbm_read_probe(src_b, sink, 32768)
+    ce1.record()
+    torch.cuda.synchronize()
+    probe_gbps = copy_n * 5 / (ce0.elapsed_time(ce1) * 1e-3) / 1e9
+    del src_b, sink
 
     for i in range(args.warmup):
         run(i)
@@ -291,7 +331,8 @@ def main():
         # the step is one kernel (store inside the decode, no partitions)
         kernel, kern_us, kern_bytes = "decode step (store + decode)", fused_us, ab["step"]
     else:
-        kernel, kern_us, kern_bytes = "decode (split-K partials)" if P else "decode", dec_us, ab["decode"]
+        kernel = ("decode (stream-K)" if SK else "decode (split-K partials)" if P else "decode")
+        kern_us, kern_bytes = dec_us, ab["decode"]
     achieved = kern_bytes / (kern_us * 1e-6) / 1e9
     traffic = load_traffic(args.traffic_file, c.key, kernel)
     log(f"[bench] mode {args.mode}: step {us_step:.1f} us (wall {wall / args.steps * 1e6:.1f} us); "
@@ -301,7 +342,7 @@ def main():
         f"reduce {np.mean(t_red):.1f} us")
     log(f"[bench] KV {ab['kv'] / 1e9:.3f} GB/step -> {kv_gbps:.0f} GB/s = "
         f"{100 * kv_gbps / HBM_PEAK_GBPS:.1f}% of {HBM_PEAK_GBPS:.0f}; {kernel} "
-        f"{achieved:.0f} GB/s; device copy {copy_gbps:.0f} GB/s")
+        f"{achieved:.0f} GB/s; device copy {copy_gbps:.0f} GB/s; read probe {probe_gbps:.0f} GB/s")
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -326,13 +367,16 @@ def main():
         "config": {
             "workload": f"{c.key}: {c.S} seqs, {c.H_q}/{c.H_kv} heads, head_dim {c.d}, "
                         f"block_size {c.bs}, {c.kv_dtype} KV, context {wl.total_tokens} tokens "
-                        f"(seed {c.seed}), split-K {P}, {R} pool layers, {args.mode} step",
+                        f"(seed {c.seed}), "
+                        + (f"stream-K {inp['workers']} waves" if SK else f"split-K {P}")
+                        + f", {R} pool layers, {args.mode} step",
             "global_batch": c.S,
             "seq_len": int(wl.context_lens.max()),
             "mean_context": round(float(wl.context_lens.mean()), 1),
             "parallelism": "single GPU",
             "mode": args.mode,
-            "step_launches": n_launch if args.mode == "fused" else (3 if P else 2),
+            "schedule": args.schedule,
+            "step_launches": n_launch if args.mode == "fused" else (3 if (P or SK) else 2),
         },
         "kv_GBps": round(kv_gbps, 1),
         "pct_hbm_peak": round(100 * kv_gbps / HBM_PEAK_GBPS, 2),
@@ -341,10 +385,12 @@ def main():
                       "decode": round(dec_us, 2), "splitk_reduce": round(float(np.mean(t_red)), 2),
                       "decode_step_entry": round(fused_us, 2)},
         "device_copy_GBps": round(copy_gbps, 1),
+        "hbm_read_probe_GBps": round(probe_gbps, 1),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": traffic, "kernel": kernel,
-                     "algorithmic_bytes_per_launch": kern_bytes},
+                     "algorithmic_bytes_per_launch": kern_bytes,
+                     "frac_of_read_probe": round(achieved / probe_gbps, 4)},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

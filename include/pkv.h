@@ -204,6 +204,86 @@ int paged_attention_decode_step_launches(int num_q_heads, int num_kv_heads, int 
                                          int block_size, pkv_dtype q_dtype, pkv_dtype cache_dtype,
                                          int partition_tokens);
 
+/* ---------------------------------------------------------------------------
+ * Stream-K decode: the same result as paged_attention_decode, scheduled for
+ * uneven lengths ("PagedAttention Kernel：大模型推理优化的显存管理革新" §3.2:
+ * sequences of very different lengths leave workers idle unless the work is
+ * rebalanced).  The (block, kv head) tiles of all sequences are laid end to
+ * end, per group of query heads, and each of `workers` persistent waves takes
+ * an equal contiguous slice; a sequence cut between waves is recombined by a
+ * reduce launch with the split-K rule.  Each wave streams the same number of
+ * tiles whatever the length mix.
+ *
+ *  tile_offsets   [num_seqs + 1] int32 (device): 0, then running sums of
+ *                 ceil(context_lens[s] / block_size)
+ *                 (paged_attention_tile_offsets computes them on the host);
+ *                 a sequence whose entry disagrees with its device length
+ *                 gets a NaN output row
+ *  total_tiles    host copy of tile_offsets[num_seqs]
+ *  workers        waves to launch, > 0; paged_attention_streamk_workers
+ *                 gives the number resident on the current device
+ *  workspace      device scratch of >= paged_attention_streamk_workspace_bytes
+ *                 (workers, ...) bytes (caller-owned; no initialisation)
+ * Other arguments as paged_attention_decode.  Two launches on `stream`
+ * (decode, reduce); the reduce also writes the zero rows of empty sequences.
+ * ------------------------------------------------------------------------- */
+int paged_attention_tile_offsets(const int32_t* context_lens_host, int num_seqs, int block_size,
+                                 int32_t* offsets_host_out, int* total_tiles_out);
+
+/* Waves of the stream-K kernel resident at once on the current device for
+ * this shape (workgroups per CU at full occupancy x CUs x waves per
+ * workgroup); a negative PKV_ERR_* on bad arguments. */
+int paged_attention_streamk_workers(int num_q_heads, int num_kv_heads, int head_dim,
+                                    int block_size, pkv_dtype q_dtype, pkv_dtype cache_dtype);
+
+/* Workspace of the stream-K decode:
+ * (workers * (num_q_heads / num_kv_heads) + num_seqs * num_q_heads)
+ * * (head_dim + 2) * 4 bytes; 0 for bad arguments. */
+size_t paged_attention_streamk_workspace_bytes(int workers, int num_seqs, int num_q_heads,
+                                               int num_kv_heads, int head_dim);
+
+int paged_attention_decode_streamk(void* out, const void* query, const void* key_cache,
+                                   const void* value_cache, const int32_t* block_tables,
+                                   int max_blocks_per_seq, const int32_t* context_lens,
+                                   const int32_t* tile_offsets, int total_tiles, int num_seqs,
+                                   int num_q_heads, int num_kv_heads, int head_dim,
+                                   int block_size, int num_blocks, float scale,
+                                   pkv_dtype q_dtype, pkv_dtype cache_dtype, float k_scale,
+                                   float v_scale, int workers, void* workspace,
+                                   size_t workspace_bytes, void* stream);
+
+/* The two launches of paged_attention_decode_streamk on their own: the
+ * decode writes the outputs of sequences that one wave covered whole and the
+ * partials of the others; the reduce combines those partials and writes the
+ * zero rows of empty sequences.  Arguments as above. */
+int paged_attention_decode_streamk_partials(
+    void* out, const void* query, const void* key_cache, const void* value_cache,
+    const int32_t* block_tables, int max_blocks_per_seq, const int32_t* context_lens,
+    const int32_t* tile_offsets, int total_tiles, int num_seqs, int num_q_heads, int num_kv_heads,
+    int head_dim, int block_size, int num_blocks, float scale, pkv_dtype q_dtype,
+    pkv_dtype cache_dtype, float k_scale, float v_scale, int workers, void* workspace,
+    size_t workspace_bytes, void* stream);
+int paged_attention_streamk_reduce(void* out, const void* workspace, size_t workspace_bytes,
+                                   const int32_t* tile_offsets, int total_tiles, int num_seqs,
+                                   int num_q_heads, int num_kv_heads, int head_dim,
+                                   int block_size, pkv_dtype q_dtype, pkv_dtype cache_dtype,
+                                   int workers, void* stream);
+
+/* paged_attention_decode_step_streamk -- paged_attention_decode_step with the
+ * stream-K schedule: new_key/new_value as there; the wave that reads a
+ * sequence's last block stores the new token first when one wave covers all
+ * query heads of a kv head, else a store launch precedes the decode. */
+int paged_attention_decode_step_streamk(void* out, const void* query, const void* new_key,
+                                        const void* new_value, void* key_cache, void* value_cache,
+                                        const int32_t* block_tables, int max_blocks_per_seq,
+                                        const int32_t* context_lens, const int32_t* tile_offsets,
+                                        int total_tiles, int num_seqs, int num_q_heads,
+                                        int num_kv_heads, int head_dim, int block_size,
+                                        int num_blocks, float scale, pkv_dtype q_dtype,
+                                        pkv_dtype cache_dtype, float k_scale, float v_scale,
+                                        int workers, void* workspace, size_t workspace_bytes,
+                                        void* stream);
+
 /* paged_attention_splitk_reduce -- combine the partials of every sequence
  * with more than one partition ("PagedAttention Kernel" article §3.2: uneven
  * pages need the work split): with running maxima m_p (log2 domain), sums

@@ -182,17 +182,110 @@ def paged_attention_decode_step_launches(num_q_heads, num_kv_heads, head_dim, bl
                                          cache_dtype, partition_tokens=0) -> int:
     """Kernel launches one decode step makes for this shape (1 = store inside the decode).
     Dtypes are torch dtypes (torch.uint8 for an FP8 cache) or pkv_dtype codes."""
-    def code(t):
-        if isinstance(t, int):
-            return t
-        if t not in _CODES:
-            raise PkvError(-1, f"unsupported dtype {t}")
-        return _CODES[t]
     n = lib().paged_attention_decode_step_launches(num_q_heads, num_kv_heads, head_dim, block_size,
-                                                   code(q_dtype), code(cache_dtype),
+                                                   _dtype_code(q_dtype), _dtype_code(cache_dtype),
                                                    int(partition_tokens))
     check(min(n, 0))
     return n
+
+
+def paged_attention_tile_offsets(context_lens_host, block_size: int):
+    """Host-side stream-K tile offsets: (int32 numpy [S+1], total tiles)."""
+    lens = np.ascontiguousarray(np.asarray(context_lens_host, dtype=np.int32))
+    S = lens.size
+    off = np.zeros(S + 1, dtype=np.int32)
+    tot = ctypes.c_int(0)
+    check(lib().paged_attention_tile_offsets(lens.ctypes.data_as(_native.pi32), S, int(block_size),
+                                             off.ctypes.data_as(_native.pi32), ctypes.byref(tot)))
+    return off, tot.value
+
+
+def _dtype_code(t):
+    if isinstance(t, int):
+        return t
+    if t not in _CODES:
+        raise PkvError(-1, f"unsupported dtype {t}")
+    return _CODES[t]
+
+
+def paged_attention_streamk_workers(num_q_heads, num_kv_heads, head_dim, block_size, q_dtype,
+                                    cache_dtype) -> int:
+    n = lib().paged_attention_streamk_workers(num_q_heads, num_kv_heads, head_dim, block_size,
+                                              _dtype_code(q_dtype), _dtype_code(cache_dtype))
+    check(min(n, 0))
+    return n
+
+
+def paged_attention_streamk_workspace_bytes(workers, num_seqs, num_q_heads, num_kv_heads,
+                                            head_dim) -> int:
+    return int(lib().paged_attention_streamk_workspace_bytes(workers, num_seqs, num_q_heads,
+                                                             num_kv_heads, head_dim))
+
+
+def _streamk_args(query, key_cache, block_tables, context_lens, tile_offsets, total_tiles, workers,
+                  workspace):
+    _need(tile_offsets, "tile_offsets", torch.int32)
+    _need(workspace, "workspace")
+    S = query.shape[0]
+    if tile_offsets.numel() != S + 1:
+        raise PkvError(-1, "tile_offsets must have S + 1 entries")
+    return (_ptr(tile_offsets), int(total_tiles)), (int(workers), _ptr(workspace),
+                                                    workspace.numel() * workspace.element_size())
+
+
+def paged_attention_decode_streamk(out, query, key_cache, value_cache, block_tables, context_lens,
+                                   scale, tile_offsets, total_tiles, workers, workspace,
+                                   k_scale=1.0, v_scale=1.0, stream=None):
+    a = _decode_args(out, query, key_cache, value_cache, block_tables, context_lens, scale,
+                     k_scale, v_scale, 0, None, 0, None)
+    mid, tail = _streamk_args(query, key_cache, block_tables, context_lens, tile_offsets,
+                              total_tiles, workers, workspace)
+    # a = (out, q, kc, vc, tables, max_blocks, lens, S, Hq, Hkv, D, bs, nb, scale, qdt, cdt,
+    #      k_scale, v_scale, partition, part_off, total_parts, ws, ws_bytes)
+    check(lib().paged_attention_decode_streamk(*a[:7], *mid, *a[7:18], *tail, _stream(stream)))
+
+
+def paged_attention_decode_streamk_partials(out, query, key_cache, value_cache, block_tables,
+                                            context_lens, scale, tile_offsets, total_tiles,
+                                            workers, workspace, k_scale=1.0, v_scale=1.0,
+                                            stream=None):
+    a = _decode_args(out, query, key_cache, value_cache, block_tables, context_lens, scale,
+                     k_scale, v_scale, 0, None, 0, None)
+    mid, tail = _streamk_args(query, key_cache, block_tables, context_lens, tile_offsets,
+                              total_tiles, workers, workspace)
+    check(lib().paged_attention_decode_streamk_partials(*a[:7], *mid, *a[7:18], *tail,
+                                                        _stream(stream)))
+
+
+def paged_attention_streamk_reduce(out, workspace, tile_offsets, total_tiles, workers,
+                                   num_kv_heads, block_size, cache_dtype, stream=None):
+    _need(out, "out")
+    _need(workspace, "workspace")
+    _need(tile_offsets, "tile_offsets", torch.int32)
+    S, Hq, D = out.shape
+    check(lib().paged_attention_streamk_reduce(
+        _ptr(out), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _ptr(tile_offsets), int(total_tiles), S, Hq, int(num_kv_heads), D, int(block_size),
+        cache_dtype_code(out), _dtype_code(cache_dtype), int(workers), _stream(stream)))
+
+
+def paged_attention_decode_step_streamk(out, query, new_key, new_value, key_cache, value_cache,
+                                        block_tables, context_lens, scale, tile_offsets,
+                                        total_tiles, workers, workspace, k_scale=1.0, v_scale=1.0,
+                                        stream=None):
+    a = _decode_args(out, query, key_cache, value_cache, block_tables, context_lens, scale,
+                     k_scale, v_scale, 0, None, 0, None)
+    S, Hq, D = query.shape
+    H = key_cache.shape[1]
+    for t, n in ((new_key, "new_key"), (new_value, "new_value")):
+        _need(t, n)
+        if tuple(t.shape) != (S, H, D) or t.dtype != query.dtype:
+            raise PkvError(-1, f"{n} must be [S, H_kv, head_dim] of the query dtype")
+    mid, tail = _streamk_args(query, key_cache, block_tables, context_lens, tile_offsets,
+                              total_tiles, workers, workspace)
+    check(lib().paged_attention_decode_step_streamk(a[0], a[1], _ptr(new_key), _ptr(new_value),
+                                                    *a[2:7], *mid, *a[7:18], *tail,
+                                                    _stream(stream)))
 
 
 def paged_attention_splitk_reduce(out, workspace, partition_offsets, total_partitions, stream=None):

@@ -45,6 +45,20 @@ SIGNATURES = {
                                           i32, i32, i32, f32, i32, i32, f32, f32, i32, vp, i32,
                                           vp, sz, vp]),
     "paged_attention_decode_step_launches": (i32, [i32, i32, i32, i32, i32, i32, i32]),
+    "paged_attention_tile_offsets": (i32, [pi32, i32, i32, pi32, ctypes.POINTER(i32)]),
+    "paged_attention_streamk_workers": (i32, [i32, i32, i32, i32, i32, i32]),
+    "paged_attention_streamk_workspace_bytes": (sz, [i32, i32, i32, i32, i32]),
+    "paged_attention_decode_streamk": (i32, [vp, vp, vp, vp, vp, i32, vp, vp, i32, i32, i32, i32,
+                                             i32, i32, i32, f32, i32, i32, f32, f32, i32, vp, sz,
+                                             vp]),
+    "paged_attention_decode_streamk_partials": (i32, [vp, vp, vp, vp, vp, i32, vp, vp, i32, i32,
+                                                      i32, i32, i32, i32, i32, f32, i32, i32, f32,
+                                                      f32, i32, vp, sz, vp]),
+    "paged_attention_streamk_reduce": (i32, [vp, vp, sz, vp, i32, i32, i32, i32, i32, i32, i32,
+                                             i32, i32, vp]),
+    "paged_attention_decode_step_streamk": (i32, [vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, i32,
+                                                  i32, i32, i32, i32, i32, i32, f32, i32, i32, f32,
+                                                  f32, i32, vp, sz, vp]),
     "paged_attention_splitk_reduce": (i32, [vp, vp, sz, vp, i32, i32, i32, i32, i32, vp]),
     "paged_kv_copy_blocks": (i32, [vp, vp, vp, i32, sz, i32, vp]),
     "paged_kv_gather": (i32, [vp, vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, i32, i32, i32, vp]),

@@ -282,6 +282,179 @@ int paged_attention_decode_step_launches(int num_q_heads, int num_kv_heads, int 
   return (decode_step_stores_in_kernel(a) ? 1 : 2) + (partition_tokens > 0 ? 1 : 0);
 }
 
+int paged_attention_tile_offsets(const int32_t* context_lens_host, int num_seqs, int block_size,
+                                 int32_t* offsets_host_out, int* total_tiles_out) {
+  if (num_seqs < 0 || block_size <= 0 || !offsets_host_out || (num_seqs > 0 && !context_lens_host))
+    return fail(PKV_ERR_INVALID, "bad arguments");
+  int64_t acc = 0;
+  offsets_host_out[0] = 0;
+  for (int s = 0; s < num_seqs; ++s) {
+    const int64_t L = context_lens_host[s];
+    if (L < 0) return fail(PKV_ERR_INVALID, "negative context length at %d", s);
+    acc += (L + block_size - 1) / block_size;
+    if (acc > INT32_MAX) return fail(PKV_ERR_INVALID, "too many tiles");
+    offsets_host_out[s + 1] = (int32_t)acc;
+  }
+  if (total_tiles_out) *total_tiles_out = (int)acc;
+  clear_error();
+  return PKV_OK;
+}
+
+static bool shape_args(int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                       pkv_dtype q_dtype, pkv_dtype cache_dtype, DecodeArgs* a) {
+  if (num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0 ||
+      !valid_dtype(q_dtype) || !valid_dtype(cache_dtype)) {
+    fail(PKV_ERR_INVALID, "bad arguments");
+    return false;
+  }
+  if (!decode_supported(q_dtype, cache_dtype, head_dim, block_size, num_q_heads / num_kv_heads)) {
+    fail(PKV_ERR_UNSUPPORTED, "unsupported decode shape");
+    return false;
+  }
+  *a = DecodeArgs{};
+  a->Hq = num_q_heads;
+  a->Hkv = num_kv_heads;
+  a->D = head_dim;
+  a->BS = block_size;
+  a->q_dtype = q_dtype;
+  a->kv_dtype = cache_dtype;
+  return true;
+}
+
+int paged_attention_streamk_workers(int num_q_heads, int num_kv_heads, int head_dim,
+                                    int block_size, pkv_dtype q_dtype, pkv_dtype cache_dtype) {
+  DecodeArgs a;
+  if (!shape_args(num_q_heads, num_kv_heads, head_dim, block_size, q_dtype, cache_dtype, &a))
+    return PKV_ERR_INVALID;
+  const int r = decode_sk_workers(a);
+  if (r <= 0) return fail(PKV_ERR_HIP, "occupancy query failed");
+  clear_error();
+  return r;
+}
+
+size_t paged_attention_streamk_workspace_bytes(int workers, int num_seqs, int num_q_heads,
+                                               int num_kv_heads, int head_dim) {
+  if (workers <= 0 || num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+      num_q_heads % num_kv_heads != 0)
+    return 0;
+  const size_t G = (size_t)(num_q_heads / num_kv_heads);
+  return ((size_t)workers * G + (size_t)num_seqs * num_q_heads) * (head_dim + 2) * sizeof(float);
+}
+
+static int streamk_common(const DecodeCall& c, const void* new_key, const void* new_value,
+                          const int32_t* tile_offsets, int total_tiles, int workers,
+                          bool reduce, void* stream) {
+  DecodeArgs a;
+  int rc = check_decode(c, &a);
+  if (rc) return rc;
+  const bool step = new_key || new_value;
+  if (step && !(new_key && new_value)) return fail(PKV_ERR_INVALID, "null pointer argument");
+  if (!tile_offsets || total_tiles < 0) return fail(PKV_ERR_INVALID, "bad tile offsets");
+  if (workers <= 0) return fail(PKV_ERR_INVALID, "workers must be > 0");
+  const size_t need = paged_attention_streamk_workspace_bytes(workers, c.num_seqs, c.num_q_heads,
+                                                              c.num_kv_heads, c.head_dim);
+  if (!c.workspace || c.workspace_bytes < need)
+    return fail(PKV_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", need, c.workspace_bytes);
+  if (c.num_seqs == 0) return PKV_OK;
+  a.ws = (float*)c.workspace;
+  a.tile_off = tile_offsets;
+  a.sk_cu = total_tiles;
+  a.sk_workers = workers;
+  if (step) {
+    a.new_k = new_key;
+    a.new_v = new_value;
+    if (c.cache_dtype == PKV_FP8_E4M3) {
+      a.k_inv = 1.f / c.k_scale;  // the same correctly rounded division as paged_kv_write
+      a.v_inv = 1.f / c.v_scale;
+    }
+  }
+  const bool store_in_kernel = step && decode_sk_heads_per_wave(a) == c.num_q_heads / c.num_kv_heads;
+  if (step && !store_in_kernel) {
+    rc = hip_status(launch_kv_write_tail(new_key, new_value, (void*)c.key_cache,
+                                         (void*)c.value_cache, c.block_tables,
+                                         c.max_blocks_per_seq, c.context_lens, c.num_seqs,
+                                         c.num_kv_heads, c.head_dim, c.block_size, c.num_blocks,
+                                         c.cache_dtype, a.k_inv, a.v_inv, stream),
+                    "paged_attention_decode_step_streamk store launch");
+    if (rc) return rc;
+  }
+  if (total_tiles > 0) {
+    rc = hip_status(launch_decode_sk(a, store_in_kernel, stream), "stream-K decode launch");
+    if (rc) return rc;
+  }
+  if (!reduce) return PKV_OK;
+  return hip_status(launch_sk_reduce(a, stream), "stream-K reduce launch");
+}
+
+int paged_attention_decode_streamk(void* out, const void* query, const void* key_cache,
+                                   const void* value_cache, const int32_t* block_tables,
+                                   int max_blocks_per_seq, const int32_t* context_lens,
+                                   const int32_t* tile_offsets, int total_tiles, int num_seqs,
+                                   int num_q_heads, int num_kv_heads, int head_dim,
+                                   int block_size, int num_blocks, float scale,
+                                   pkv_dtype q_dtype, pkv_dtype cache_dtype, float k_scale,
+                                   float v_scale, int workers, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+  DecodeCall c{out, query, key_cache, value_cache, block_tables, max_blocks_per_seq, context_lens,
+               num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, scale,
+               q_dtype, cache_dtype, k_scale, v_scale, 0, nullptr, 0, workspace, workspace_bytes};
+  return streamk_common(c, nullptr, nullptr, tile_offsets, total_tiles, workers, true, stream);
+}
+
+int paged_attention_decode_streamk_partials(
+    void* out, const void* query, const void* key_cache, const void* value_cache,
+    const int32_t* block_tables, int max_blocks_per_seq, const int32_t* context_lens,
+    const int32_t* tile_offsets, int total_tiles, int num_seqs, int num_q_heads, int num_kv_heads,
+    int head_dim, int block_size, int num_blocks, float scale, pkv_dtype q_dtype,
+    pkv_dtype cache_dtype, float k_scale, float v_scale, int workers, void* workspace,
+    size_t workspace_bytes, void* stream) {
+  DecodeCall c{out, query, key_cache, value_cache, block_tables, max_blocks_per_seq, context_lens,
+               num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, scale,
+               q_dtype, cache_dtype, k_scale, v_scale, 0, nullptr, 0, workspace, workspace_bytes};
+  return streamk_common(c, nullptr, nullptr, tile_offsets, total_tiles, workers, false, stream);
+}
+
+int paged_attention_streamk_reduce(void* out, const void* workspace, size_t workspace_bytes,
+                                   const int32_t* tile_offsets, int total_tiles, int num_seqs,
+                                   int num_q_heads, int num_kv_heads, int head_dim,
+                                   int block_size, pkv_dtype q_dtype, pkv_dtype cache_dtype,
+                                   int workers, void* stream) {
+  DecodeArgs a;
+  if (!shape_args(num_q_heads, num_kv_heads, head_dim, block_size, q_dtype, cache_dtype, &a))
+    return PKV_ERR_INVALID;
+  if (!out || !workspace || !tile_offsets) return fail(PKV_ERR_INVALID, "null pointer argument");
+  if (num_seqs < 0 || total_tiles < 0 || workers <= 0) return fail(PKV_ERR_INVALID, "bad sizes");
+  const size_t need = paged_attention_streamk_workspace_bytes(workers, num_seqs, num_q_heads,
+                                                              num_kv_heads, head_dim);
+  if (workspace_bytes < need)
+    return fail(PKV_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", need, workspace_bytes);
+  if (num_seqs == 0) return PKV_OK;
+  a.out = out;
+  a.ws = (float*)workspace;
+  a.S = num_seqs;
+  a.tile_off = tile_offsets;
+  a.sk_cu = total_tiles;
+  a.sk_workers = workers;
+  return hip_status(launch_sk_reduce(a, stream), "stream-K reduce launch");
+}
+
+int paged_attention_decode_step_streamk(void* out, const void* query, const void* new_key,
+                                        const void* new_value, void* key_cache, void* value_cache,
+                                        const int32_t* block_tables, int max_blocks_per_seq,
+                                        const int32_t* context_lens, const int32_t* tile_offsets,
+                                        int total_tiles, int num_seqs, int num_q_heads,
+                                        int num_kv_heads, int head_dim, int block_size,
+                                        int num_blocks, float scale, pkv_dtype q_dtype,
+                                        pkv_dtype cache_dtype, float k_scale, float v_scale,
+                                        int workers, void* workspace, size_t workspace_bytes,
+                                        void* stream) {
+  if (!new_key || !new_value) return fail(PKV_ERR_INVALID, "null pointer argument");
+  DecodeCall c{out, query, key_cache, value_cache, block_tables, max_blocks_per_seq, context_lens,
+               num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, scale,
+               q_dtype, cache_dtype, k_scale, v_scale, 0, nullptr, 0, workspace, workspace_bytes};
+  return streamk_common(c, new_key, new_value, tile_offsets, total_tiles, workers, true, stream);
+}
+
 int paged_attention_splitk_reduce(void* out, const void* workspace, size_t workspace_bytes,
                                   const int32_t* partition_offsets, int num_seqs,
                                   int num_q_heads, int head_dim, int total_partitions,

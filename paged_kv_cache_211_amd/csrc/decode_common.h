@@ -20,8 +20,8 @@
 #ifndef PKV_DECODE_DEPTH
 #define PKV_DECODE_DEPTH 1
 #endif
-#ifndef PKV_DECODE_PER_WAVE
-#define PKV_DECODE_PER_WAVE 0
+#ifndef PKV_SK_WAVES
+#define PKV_SK_WAVES 4
 #endif
 #ifndef PKV_DECODE_QLDS
 #define PKV_DECODE_QLDS 0
@@ -34,9 +34,8 @@ namespace pkv {
 namespace dec {
 
 constexpr int kWaves = PKV_DECODE_WAVES;
-// PKV_DECODE_PER_WAVE = 1: one work item per wave instead of per workgroup
-// (the decode step then stores the new tokens with a launch of its own).
-constexpr bool kPerWave = PKV_DECODE_PER_WAVE;
+constexpr int kSkWaves = PKV_SK_WAVES;            // waves per workgroup, stream-K kernels
+constexpr bool kQLds = PKV_DECODE_QLDS;           // vector-ALU kernels: query rows in LDS
 
 constexpr int kBufs = PKV_DECODE_DEPTH + 1;      // tiles in registers per wave (VALU kernel)
 constexpr int kMfmaBufs = PKV_MFMA_DEPTH + 1;    // same, matrix-core kernel

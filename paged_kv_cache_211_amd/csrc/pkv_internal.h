@@ -39,6 +39,10 @@ struct DecodeArgs {
   const void* new_k = nullptr;
   const void* new_v = nullptr;
   float k_inv = 1.f, v_inv = 1.f;
+  // Stream-K schedule: tile_off [S+1] prefix sums of ceil(lens/BS) (device),
+  // sk_cu = tile_off[S] (host copy), sk_workers = waves launched.
+  const int32_t* tile_off = nullptr;
+  int sk_cu = 0, sk_workers = 0;
 };
 
 // Kernel launchers (decode.hip, kv_ops.hip).  Return hipError_t as int.
@@ -49,6 +53,13 @@ int launch_decode(const DecodeArgs& a, void* stream);
 // with launch_kv_write_tail first.
 bool decode_step_stores_in_kernel(const DecodeArgs& a);
 int launch_decode_step(const DecodeArgs& a, void* stream);
+// Stream-K decode (decode.hip): resident waves for this shape on the current
+// device (< 0 on error), the decode launch (store: also the decode step's
+// new-token store, when decode_step_stores_in_kernel) and its reduce.
+int decode_sk_workers(const DecodeArgs& a);
+int decode_sk_heads_per_wave(const DecodeArgs& a);
+int launch_decode_sk(const DecodeArgs& a, bool store, void* stream);
+int launch_sk_reduce(const DecodeArgs& a, void* stream);
 // Matrix-core decode for fp8 key/value tiles with query heads in groups of 8
 // (decode_mfma.hip); launch_decode routes eligible calls there.
 bool decode_mfma_eligible(const DecodeArgs& a);

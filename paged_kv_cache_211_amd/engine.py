@@ -13,8 +13,10 @@ import numpy as np
 import torch
 
 from . import (BlockAllocator, empty_pools, paged_attention_decode, paged_attention_decode_step,
-               paged_attention_partition_offsets, paged_attention_workspace_bytes,
-               paged_kv_copy_blocks, paged_kv_write)
+               paged_attention_decode_step_streamk, paged_attention_decode_streamk,
+               paged_attention_partition_offsets, paged_attention_streamk_workers,
+               paged_attention_streamk_workspace_bytes, paged_attention_tile_offsets,
+               paged_attention_workspace_bytes, paged_kv_copy_blocks, paged_kv_write)
 
 
 class PagedKVCache:
@@ -81,25 +83,43 @@ class PagedKVCache:
         return torch.from_numpy(t).to(self.device)
 
     # -- decode -------------------------------------------------------------------
-    def decode_inputs(self, seqs, partition_tokens: int = 0):
-        """Device tables, lengths and split-K metadata for a decode over seqs."""
+    def decode_inputs(self, seqs, partition_tokens: int = 0, streamk: bool = False,
+                      num_q_heads: int | None = None, q_dtype=None, workers: int | None = None):
+        """Device tables, lengths and schedule metadata for a decode over seqs:
+        split-K partitions of partition_tokens (0 = one pass), or with
+        streamk=True the tile offsets and wave count of the stream-K schedule
+        (num_q_heads and q_dtype needed; workers defaults to the resident
+        waves of this device)."""
         lens = self.seq_lens(seqs)
         inp = {"block_tables": self.block_tables(seqs),
                "context_lens": torch.from_numpy(lens).to(self.device),
                "partition_tokens": int(partition_tokens), "partition_offsets": None,
-               "total_partitions": 0, "lens_host": lens}
-        if partition_tokens:
+               "total_partitions": 0, "lens_host": lens, "streamk": bool(streamk)}
+        if streamk:
+            off, tot = paged_attention_tile_offsets(lens, self.bs)
+            inp["tile_offsets"] = torch.from_numpy(off).to(self.device)
+            inp["total_tiles"] = tot
+            inp["workers"] = workers or paged_attention_streamk_workers(
+                num_q_heads, self.H, self.D, self.bs, q_dtype, self.dtype)
+        elif partition_tokens:
             off, tot = paged_attention_partition_offsets(lens, partition_tokens)
             inp["partition_offsets"] = torch.from_numpy(off).to(self.device)
             inp["total_partitions"] = tot
         return inp
 
-    def workspace(self, total_partitions, num_q_heads, head_dim):
-        """Device scratch for split-K partials (grown on demand, reused)."""
-        need = paged_attention_workspace_bytes(total_partitions, num_q_heads, head_dim)
+    def _scratch(self, need):
         if self._ws is None or self._ws.numel() < need:
             self._ws = torch.empty(max(need, 16), dtype=torch.uint8, device=self.device)
         return self._ws
+
+    def workspace(self, total_partitions, num_q_heads, head_dim):
+        """Device scratch for split-K partials (grown on demand, reused)."""
+        return self._scratch(paged_attention_workspace_bytes(total_partitions, num_q_heads, head_dim))
+
+    def streamk_workspace(self, inp, num_q_heads):
+        S = len(inp["lens_host"])
+        return self._scratch(paged_attention_streamk_workspace_bytes(inp["workers"], S, num_q_heads,
+                                                                     self.H, self.D))
 
     def reserve_step(self, seqs, stream=None):
         """Allocate one new token for each sequence (copy-on-write included)
@@ -121,6 +141,13 @@ class PagedKVCache:
         the decode launch where the kernel allows."""
         S, Hq, D = query.shape
         out = torch.empty_like(query) if out is None else out
+        if inp["streamk"]:
+            paged_attention_decode_step_streamk(
+                out, query, new_key, new_value, self.key_cache, self.value_cache,
+                inp["block_tables"], inp["context_lens"], scale, inp["tile_offsets"],
+                inp["total_tiles"], inp["workers"], self.streamk_workspace(inp, Hq),
+                k_scale=self.k_scale, v_scale=self.v_scale, stream=stream)
+            return out
         ws = None
         if inp["partition_tokens"]:
             ws = self.workspace(inp["total_partitions"], Hq, D)
@@ -136,6 +163,13 @@ class PagedKVCache:
     def decode(self, query, inp, scale, out=None, stream=None):
         S, Hq, D = query.shape
         out = torch.empty_like(query) if out is None else out
+        if inp["streamk"]:
+            paged_attention_decode_streamk(out, query, self.key_cache, self.value_cache,
+                                           inp["block_tables"], inp["context_lens"], scale,
+                                           inp["tile_offsets"], inp["total_tiles"], inp["workers"],
+                                           self.streamk_workspace(inp, Hq), k_scale=self.k_scale,
+                                           v_scale=self.v_scale, stream=stream)
+            return out
         ws = None
         if inp["partition_tokens"]:
             ws = self.workspace(inp["total_partitions"], Hq, D)
