@@ -4,7 +4,9 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
+#include <type_traits>
 
 #include "decode_common.h"
 
@@ -37,120 +39,148 @@ namespace {
 
 using namespace dec;
 
-// Combine n partials of one (sequence, query head) into output row `oi`:
-// partial p is row row0 + p*stride of o (D floats each) and of (m, l) (2
+// Combine the n partials of HG query heads of one sequence: partial p of head
+// hh is row row0 + p*pstride + hh of o (D floats each) and of (m, l) (2
 // floats each); out = sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p with
-// M = max_p m_p.  All 256 threads of the workgroup take part.
-template <int D, bool F32OUT>
-__device__ __forceinline__ void merge_partials(void* __restrict__ out, size_t oi,
-                                               const float* __restrict__ ws_o,
-                                               const float* __restrict__ ws_ml, size_t row0,
-                                               size_t stride, int n) {
-  constexpr int DQ = D / 4;      // float4 columns of a row
-  constexpr int PL = 256 / DQ;   // partials handled in parallel
-  __shared__ f32x4 o_red[PL][DQ];
-  __shared__ float l_red[PL];
-  __shared__ float mx_red[256];
-  const int tid = threadIdx.x;
+// M = max_p m_p, written to out rows oi0 + hh*D.  The 256 threads first take
+// (piece, head) pairs for the maxima and the weights (kept in LDS, a chunk
+// of pieces at a time); then PL piece lanes each sum every PL-th piece over
+// the NV = HG*D/4 float4 columns, four pieces' loads in flight, and LDS adds
+// the lanes.
+template <int D, bool F32OUT, int HG>
+__device__ __forceinline__ void merge_heads(void* __restrict__ out, size_t oi0,
+                                            const float* __restrict__ ws_o,
+                                            const float* __restrict__ ws_ml, size_t row0,
+                                            size_t pstride, int n) {
+  constexpr int NT = 256, PSTEP = NT / HG, PCH = 2048 / HG, NV = HG * D / 4, PL = NT / NV;
+  static_assert(NV * PL == NT, "thread layout");
+  __shared__ float red[NT];
+  __shared__ float w_lds[PCH][HG];
+  __shared__ float m_s[HG], l_s[HG];
+  __shared__ f32x4 part[PL][NV];
+  const int tid = threadIdx.x, hh_t = tid % HG, p_t = tid / HG;
 
   float mx = -INFINITY;
-  for (int p = tid; p < n; p += 256) mx = fmaxf(mx, ws_ml[(row0 + p * stride) * 2]);
-  mx_red[tid] = mx;
+  for (int p = p_t; p < n; p += PSTEP) mx = fmaxf(mx, ws_ml[(row0 + p * pstride + hh_t) * 2]);
+  red[tid] = mx;
   __syncthreads();
-  for (int k = 128; k > 0; k >>= 1) {
-    if (tid < k) mx_red[tid] = fmaxf(mx_red[tid], mx_red[tid + k]);
+  for (int k = NT / 2; k >= HG; k >>= 1) {
+    if (tid < k) red[tid] = fmaxf(red[tid], red[tid + k]);
     __syncthreads();
   }
-  const float M = mx_red[0];
+  if (tid < HG) m_s[tid] = red[tid];
+  __syncthreads();
+  const float M_t = m_s[hh_t];
 
-  const int dq = tid % DQ, pl = tid / DQ;
-  f32x4 o = {0.f, 0.f, 0.f, 0.f};
-  float l = 0.f;
-  if (M != -INFINITY) {
-    for (int p = pl; p < n; p += PL) {
-      const size_t pi = row0 + p * stride;
-      const float f = __builtin_amdgcn_exp2f(ws_ml[pi * 2] - M);
-      l = fmaf(ws_ml[pi * 2 + 1], f, l);
-      const f32x4 v = *(const f32x4*)(ws_o + pi * D + dq * 4);
-      o.x = fmaf(v.x, f, o.x);
-      o.y = fmaf(v.y, f, o.y);
-      o.z = fmaf(v.z, f, o.z);
-      o.w = fmaf(v.w, f, o.w);
+  const int pl = tid / NV, e = tid % NV;
+  const int hh_e = e * 4 / D, d4 = e * 4 % D;   // this thread's float4 column
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  float lsum = 0.f;
+  for (int pc = 0; pc < n; pc += PCH) {
+    const int np = min(PCH, n - pc);
+    for (int p = p_t; p < np; p += PSTEP) {
+      const float* ml = ws_ml + (row0 + (size_t)(pc + p) * pstride + hh_t) * 2;
+      const float w = M_t == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ml[0] - M_t);
+      w_lds[p][hh_t] = w;
+      lsum = fmaf(ml[1], w, lsum);
     }
+    __syncthreads();
+    const float* op = ws_o + (row0 + (size_t)pc * pstride + hh_e) * D + d4;
+    const size_t ps = pstride * D;
+    int p = pl;
+    for (; p + 3 * PL < np; p += 4 * PL) {
+      f32x4 v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v[u] = *(const f32x4*)(op + (size_t)(p + u * PL) * ps);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float w = w_lds[p + u * PL][hh_e];
+        acc.x = fmaf(v[u].x, w, acc.x);
+        acc.y = fmaf(v[u].y, w, acc.y);
+        acc.z = fmaf(v[u].z, w, acc.z);
+        acc.w = fmaf(v[u].w, w, acc.w);
+      }
+    }
+    for (; p < np; p += PL) {
+      const f32x4 v = *(const f32x4*)(op + (size_t)p * ps);
+      const float w = w_lds[p][hh_e];
+      acc.x = fmaf(v.x, w, acc.x);
+      acc.y = fmaf(v.y, w, acc.y);
+      acc.z = fmaf(v.z, w, acc.z);
+      acc.w = fmaf(v.w, w, acc.w);
+    }
+    __syncthreads();
   }
-  o_red[pl][dq] = o;
-  if (dq == 0) l_red[pl] = l;
+  part[pl][e] = acc;
+  red[tid] = lsum;
+  __syncthreads();
+  for (int k = NT / 2; k >= HG; k >>= 1) {
+    if (tid < k) red[tid] += red[tid + k];
+    __syncthreads();
+  }
+  if (tid < HG) l_s[tid] = red[tid];
   __syncthreads();
   if (pl == 0) {
-    f32x4 t = o_red[0][dq];
-    float lt = l_red[0];
-    for (int r = 1; r < PL; ++r) {
-      const f32x4 u = o_red[r][dq];
-      t.x += u.x; t.y += u.y; t.z += u.z; t.w += u.w;
-      lt += l_red[r];
+#pragma unroll
+    for (int q = 1; q < PL; ++q) {
+      const f32x4 u = part[q][e];
+      acc.x += u.x; acc.y += u.y; acc.z += u.z; acc.w += u.w;
     }
-    const float inv = lt > 0.f ? 1.f / lt : 0.f;   // a NaN partial stays NaN through t
-    const size_t o4 = oi + dq * 4;
-    const float r0 = t.x * inv, r1 = t.y * inv, r2 = t.z * inv, r3 = t.w * inv;
+    const float L = l_s[hh_e];
+    const float inv = L > 0.f ? 1.f / L : 0.f;   // a NaN partial stays NaN through acc
+    const float r0 = acc.x * inv, r1 = acc.y * inv, r2 = acc.z * inv, r3 = acc.w * inv;
+    const size_t o4 = oi0 + (size_t)hh_e * D + d4;
     if constexpr (F32OUT) {
       *(f32x4*)((float*)out + o4) = f32x4{r0, r1, r2, r3};
     } else {
       uint16_t* o16 = (uint16_t*)out + o4;
-      const uint32_t lo = pack_bf16x2(r0, r1), hi = pack_bf16x2(r2, r3);
-      *(uint2*)o16 = make_uint2(lo, hi);
+      *(uint2*)o16 = make_uint2(pack_bf16x2(r0, r1), pack_bf16x2(r2, r3));
     }
   }
 }
 
-// Split-K reduce: one workgroup per (sequence, query head) with > 1 partition.
-template <int D, bool F32OUT>
+// Split-K reduce: one workgroup per (sequence, group of HG query heads);
+// sequences with one partition are left alone.
+template <int D, bool F32OUT, int HG>
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(void* __restrict__ out,
                                                             const float* __restrict__ ws,
                                                             const int32_t* __restrict__ part_off,
                                                             int Hq, int total_parts) {
-  const int s = blockIdx.x, qh = blockIdx.y;
+  const int s = blockIdx.x, qh0 = blockIdx.y * HG;
   const int p0 = part_off[s];
   const int n = part_off[s + 1] - p0;
   if (n <= 1) return;
-  merge_partials<D, F32OUT>(out, ((size_t)s * Hq + qh) * D, ws, ws + (size_t)total_parts * Hq * D,
-                            (size_t)p0 * Hq + qh, Hq, n);
+  merge_heads<D, F32OUT, HG>(out, ((size_t)s * Hq + qh0) * D, ws, ws + (size_t)total_parts * Hq * D,
+                             (size_t)p0 * Hq + qh0, Hq, n);
 }
 
-// Stream-K reduce: one workgroup per (sequence, query head).  The item's
-// tiles [start, start + n) of the T laid out end to end went to waves
-// r(start) .. r(start + n - 1), r(x) = floor(((x + 1) R - 1) / T) being the
-// wave whose slice [floor(r T / R), floor((r + 1) T / R)) holds tile x; with
-// one wave the output is already written, with several their partials sit in
-// consecutive slots r + hg*S + s.  A sequence without tiles gets zeros.
-template <int D, bool F32OUT>
+// Stream-K reduce: one workgroup per (sequence, HG query heads of one head
+// group hg of hpw).  The item's tiles [start, start + n) of the T laid out end to
+// end went to waves r(start) .. r(start + n - 1), r(x) = floor(((x + 1) R -
+// 1) / T) being the wave whose slice [floor(r T / R), floor((r + 1) T / R))
+// holds tile x; with one wave the output is already written, with several
+// their partials sit in consecutive slots r + hg*S + s.  A sequence without
+// tiles gets zeros; offsets that are not running sums ending at CU, NaN.
+template <int D, bool F32OUT, int HG>
 __global__ __launch_bounds__(256) void sk_reduce_kernel(void* __restrict__ out,
                                                         const float* __restrict__ ws,
                                                         const int32_t* __restrict__ tile_off,
                                                         int S, int Hq, int Hkv, int hpw, int R,
                                                         int CU) {
-  const int s = blockIdx.x, qh = blockIdx.y;
+  const int s = blockIdx.x, qh0 = blockIdx.y * HG;   // heads qh0 .. qh0 + HG - 1
   const int G = Hq / Hkv, groups = G / hpw;
-  const int hkv = qh / G, g = (qh % G) / hpw, hh = qh % hpw;
-  const int hg = hkv * groups + g;
+  const int hkv = qh0 / G, hg = hkv * groups + (qh0 % G) / hpw, hh0 = qh0 % hpw;
   const int n = tile_off[s + 1] - tile_off[s];
-  const size_t oi = ((size_t)s * Hq + qh) * D;
-  if (n <= 0) {
-    for (int i = threadIdx.x; i < D; i += 256) {
-      if constexpr (F32OUT)
-        ((float*)out)[oi + i] = 0.f;
-      else
-        ((uint16_t*)out)[oi + i] = 0;
-    }
-    return;
-  }
+  const size_t oi0 = ((size_t)s * Hq + qh0) * D;
   const int64_t T = (int64_t)CU * Hkv * groups;
   const int64_t start = (int64_t)hg * CU + tile_off[s], last = start + n - 1;
-  if (start < 0 || last >= T) {   // offsets that are not running sums ending at CU
-    for (int i = threadIdx.x; i < D; i += 256) {
+  if (n <= 0 || start < 0 || last >= T) {
+    const bool zero = n == 0;
+    for (int i = threadIdx.x; i < HG * D; i += 256) {
       if constexpr (F32OUT)
-        ((float*)out)[oi + i] = NAN;
+        ((float*)out)[oi0 + i] = zero ? 0.f : NAN;
       else
-        ((uint16_t*)out)[oi + i] = 0x7fc0;
+        ((uint16_t*)out)[oi0 + i] = zero ? 0 : 0x7fc0;
     }
     return;
   }
@@ -158,7 +188,8 @@ __global__ __launch_bounds__(256) void sk_reduce_kernel(void* __restrict__ out,
   if (r0 == r1) return;
   const size_t slots = (size_t)R + (size_t)Hkv * groups * S;
   const size_t slot0 = (size_t)r0 + (size_t)hg * S + s;
-  merge_partials<D, F32OUT>(out, oi, ws, ws + slots * hpw * D, slot0 * hpw + hh, hpw, r1 - r0 + 1);
+  merge_heads<D, F32OUT, HG>(out, oi0, ws, ws + slots * hpw * D, slot0 * hpw + hh0, hpw,
+                             r1 - r0 + 1);
 }
 
 int launch_valu_any(const DecodeArgs& a, bool store, hipStream_t st) {
@@ -199,6 +230,7 @@ int launch_decode_step(const DecodeArgs& a, void* stream) {
 }
 
 int decode_sk_workers(const DecodeArgs& a) {
+  if (decode_mfma_eligible(a)) return decode_mfma_sk_workers();
   switch (a.kv_dtype) {
     case PKV_F32: return valu::valu_sk_workers<PKV_F32>(a);
     case PKV_BF16: return valu::valu_sk_workers<PKV_BF16>(a);
@@ -207,6 +239,7 @@ int decode_sk_workers(const DecodeArgs& a) {
 }
 
 int decode_sk_heads_per_wave(const DecodeArgs& a) {
+  if (decode_mfma_eligible(a)) return 8;
   switch (a.kv_dtype) {
     case PKV_F32: return valu::valu_heads_per_wg<PKV_F32>(a);
     case PKV_BF16: return valu::valu_heads_per_wg<PKV_BF16>(a);
@@ -226,6 +259,7 @@ static DecodeArgs clamp_workers(const DecodeArgs& a) {
 
 int launch_decode_sk(const DecodeArgs& a0, bool store, void* stream) {
   const DecodeArgs a = clamp_workers(a0);
+  if (decode_mfma_eligible(a)) return launch_decode_mfma_sk(a, stream, store);
   hipStream_t st = (hipStream_t)stream;
   switch (a.kv_dtype) {
     case PKV_F32: return valu::launch_valu_sk<PKV_F32>(a, store, st);
@@ -234,40 +268,56 @@ int launch_decode_sk(const DecodeArgs& a0, bool store, void* stream) {
   }
 }
 
+// Calls f(integral_constant<int, HG>) for HG in {1, 2, 4, 8}.
+template <class F>
+int with_hg(int hg, F&& f) {
+  switch (hg) {
+    case 8: return f(std::integral_constant<int, 8>());
+    case 4: return f(std::integral_constant<int, 4>());
+    case 2: return f(std::integral_constant<int, 2>());
+    default: return f(std::integral_constant<int, 1>());
+  }
+}
+
 int launch_sk_reduce(const DecodeArgs& a0, void* stream) {
   const DecodeArgs a = clamp_workers(a0);
   hipStream_t st = (hipStream_t)stream;
   const int hpw = decode_sk_heads_per_wave(a);
-  dim3 grid(a.S, a.Hq), block(256);
+  const int hgs = std::min(hpw, 256 / a.D);   // heads per reduce workgroup
+  dim3 grid(a.S, a.Hq / hgs), block(256);
   const bool f32 = a.q_dtype == PKV_F32;
-  auto go = [&](auto kern) {
-    hipLaunchKernelGGL(kern, grid, block, 0, st, a.out, (const float*)a.ws, a.tile_off, a.S, a.Hq,
-                       a.Hkv, hpw, a.sk_workers, a.sk_cu);
-  };
-  if (a.D == 64)
-    f32 ? go(sk_reduce_kernel<64, true>) : go(sk_reduce_kernel<64, false>);
-  else
-    f32 ? go(sk_reduce_kernel<128, true>) : go(sk_reduce_kernel<128, false>);
-  return (int)hipGetLastError();
+  return with_hg(hgs, [&](auto hg) {
+    constexpr int HG = decltype(hg)::value;
+    auto go = [&](auto kern) {
+      hipLaunchKernelGGL(kern, grid, block, 0, st, a.out, (const float*)a.ws, a.tile_off, a.S,
+                         a.Hq, a.Hkv, hpw, a.sk_workers, a.sk_cu);
+    };
+    if (a.D == 64)
+      f32 ? go(sk_reduce_kernel<64, true, HG>) : go(sk_reduce_kernel<64, false, HG>);
+    else
+      f32 ? go(sk_reduce_kernel<128, true, HG>) : go(sk_reduce_kernel<128, false, HG>);
+    return (int)hipGetLastError();
+  });
 }
 
 int launch_splitk_reduce(void* out, const float* ws, const int32_t* part_off, int S, int Hq, int D,
                          int total_parts, pkv_dtype out_dtype, void* stream) {
   hipStream_t st = (hipStream_t)stream;
-  dim3 grid(S, Hq), block(256);
+  const int cap = 256 / D;   // heads per workgroup: 64 float4 columns at most
+  const int hgs = Hq % cap == 0 ? cap : Hq % 2 == 0 ? 2 : 1;
+  dim3 grid(S, Hq / hgs), block(256);
   const bool f32 = out_dtype == PKV_F32;
-  if (D == 64) {
-    if (f32)
-      hipLaunchKernelGGL((splitk_reduce_kernel<64, true>), grid, block, 0, st, out, ws, part_off, Hq, total_parts);
+  return with_hg(hgs, [&](auto hg) {
+    constexpr int HG = decltype(hg)::value;
+    auto go = [&](auto kern) {
+      hipLaunchKernelGGL(kern, grid, block, 0, st, out, ws, part_off, Hq, total_parts);
+    };
+    if (D == 64)
+      f32 ? go(splitk_reduce_kernel<64, true, HG>) : go(splitk_reduce_kernel<64, false, HG>);
     else
-      hipLaunchKernelGGL((splitk_reduce_kernel<64, false>), grid, block, 0, st, out, ws, part_off, Hq, total_parts);
-  } else {
-    if (f32)
-      hipLaunchKernelGGL((splitk_reduce_kernel<128, true>), grid, block, 0, st, out, ws, part_off, Hq, total_parts);
-    else
-      hipLaunchKernelGGL((splitk_reduce_kernel<128, false>), grid, block, 0, st, out, ws, part_off, Hq, total_parts);
-  }
-  return (int)hipGetLastError();
+      f32 ? go(splitk_reduce_kernel<128, true, HG>) : go(splitk_reduce_kernel<128, false, HG>);
+    return (int)hipGetLastError();
+  });
 }
 
 }  // namespace pkv

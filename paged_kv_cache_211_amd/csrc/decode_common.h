@@ -118,13 +118,17 @@ __device__ __forceinline__ Work locate(const DecodeArgs& a, int hpw, int lane, i
 // the younger tiles outstanding.  kbase/vbase point at this lane's 16 bytes
 // of load 0 of block 0 (head and lane offsets included); load l of a tile is
 // l KiB further.  A block id outside [0, nb) sets `bad` and reads block 0.
+// j_sync >= 0: every earlier memory operation of the wave (a store into that
+// tile, say) completes before tile j_sync is loaded.
 template <int NBUF, int NLOAD, int NW, class Proc>
 __device__ __forceinline__ void tile_loop(const int32_t* __restrict__ tbl, int jfirst, int jend,
                                           int nb, const uint8_t* kbase, const uint8_t* vbase,
-                                          size_t blk_stride, int lane, bool& bad, Proc&& process) {
+                                          size_t blk_stride, int lane, bool& bad, Proc&& process,
+                                          int j_sync = -1) {
   u32x4 kbuf[NBUF][NLOAD], vbuf[NBUF][NLOAD];
   int tbl_v = 0, chunk0 = 0;
   auto load_tile = [&](int jj, u32x4* kd, u32x4* vd) {
+    if (jj == j_sync) __builtin_amdgcn_s_waitcnt(0);
     int b = __builtin_amdgcn_readlane(tbl_v, (jj - chunk0) / NW);
     if ((unsigned)b >= (unsigned)nb) { bad = true; b = 0; }
     const uint8_t* kt = kbase + (size_t)b * blk_stride;

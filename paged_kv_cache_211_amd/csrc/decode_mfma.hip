@@ -24,9 +24,9 @@
 // assignment of dims/tokens to k slots is free and chosen to match the loads.
 // Score and output rows r = 0..3 of lane l are head 4g + r; rows 8..31 are
 // padding (zero query rows).
-// Work: one wave per (sequence, split-K partition, kv head); the wave keeps
-// its own softmax state and writes its output or partial directly, so no
-// workgroup-wide merge or barrier is needed.
+// Work: one wave per (sequence, split-K partition, kv head), or per piece of
+// a stream-K slice; the wave keeps its own softmax state and writes its
+// output or partial directly, so no workgroup-wide merge or barrier is needed.
 
 #include <hip/hip_runtime.h>
 
@@ -49,60 +49,22 @@ __device__ __forceinline__ bf16x8 fp8x8_to_bf16(uint32_t w0, uint32_t w1) {
   return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
-// Each wave owns one work item: (sequence, partition) for the kv head of
-// blockIdx.y, flat item blockIdx.x * NW + wave.  Waves never synchronise;
-// a wave writes its own output (one-partition sequence) or partial.
-// STORE (decode step, one group of 8 query heads per kv head): the wave that
-// reads a sequence's last block first stores the sequence's new token there;
-// it is that block's only reader, so waiting for its own stores suffices.
-template <int NW, int NBUF, bool SPLIT, bool STORE = false>
-__global__ __launch_bounds__(NW * 64) void decode_mfma_fp8_kernel(const DecodeArgs a) {
-  constexpr int D = 128, BS = 32, HPW = 8;
-  constexpr int TILE = BS * D;          // bytes of an fp8 (block, kv head) tile
-  constexpr int NLOAD = TILE / 1024;    // 4 loads of 16 bytes per lane
+constexpr int kD = 128, kBS = 32, kHPW = 8;
+constexpr int kTile = kBS * kD;         // bytes of an fp8 (block, kv head) tile
+constexpr int kNLoad = kTile / 1024;    // 4 loads of 16 bytes per lane
 
-  __shared__ uint16_t p_lds[NW][HPW][BS];
-
-  const int lane = threadIdx.x & 63;
-  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+// One wave's work on tiles [jfirst, jend) of sequence s (tokens end at t1)
+// for the 8 query heads qh0 .. qh0+7 of kv head hkv: QK^T and PV on matrix
+// cores, online softmax, then the output rows (final_out) or the partial
+// rows prow0 + h (h = 0..7) of ws_o / ws_ml.  prow: this wave's LDS rows.
+__device__ __forceinline__ void mfma_item(const DecodeArgs& a, int s, int hkv, int qh0, int jfirst,
+                                          int jend, int t1, bool bad, bool final_out, size_t prow0,
+                                          float* ws_o, float* ws_ml, uint16_t (*prow)[kBS],
+                                          int lane, int j_sync = -1) {
+  constexpr int D = kD, BS = kBS, HPW = kHPW, TILE = kTile, NLOAD = kNLoad;
+  constexpr int NBUF = kMfmaBufs;
   const int col = lane & 31, g = lane >> 5;
-  const int item = blockIdx.x * NW + w;
-  const int n_items = SPLIT ? a.total_parts : a.S;
-  if (item >= n_items) return;
-
-  // ---- locate the work item ----
-  const int G = a.Hq / a.Hkv;
-  const int hkv = blockIdx.y / (G / HPW);
-  const int qh0 = hkv * G + (blockIdx.y % (G / HPW)) * HPW;
-  int s, part, nparts;
-  if constexpr (SPLIT) {
-    s = __builtin_amdgcn_readfirstlane(find_seq(a.part_off, a.S, item, lane));
-    const int p0 = a.part_off[s];
-    part = item - p0;
-    nparts = a.part_off[s + 1] - p0;
-  } else {
-    s = item;
-    part = 0;
-    nparts = 1;
-  }
-  int L = a.lens[s];
-  bool bad = false;
-  if (L < 0) { L = 0; bad = true; }
-  if (L > a.max_blocks * BS) { L = a.max_blocks * BS; bad = true; }
-  const int t0 = SPLIT ? part * a.partition : 0;
-  const int t1 = SPLIT ? min(L, t0 + a.partition) : L;
-  const int jend = (t1 + BS - 1) / BS;
   const int32_t* __restrict__ tbl = a.tables + (size_t)s * a.max_blocks;
-  if constexpr (STORE) {
-    if (!bad && L > 0 && t0 < L && t1 == L) {
-      const int pos = L - 1;
-      const int blk = tbl[pos / BS];
-      if ((unsigned)blk < (unsigned)a.nb && lane < D / 16)
-        write_kv_unit<PKV_FP8_E4M3>(a.new_k, a.new_v, (uint8_t*)a.kc, (uint8_t*)a.vc, s, hkv, lane,
-                                    blk * BS + pos % BS, a.Hkv, D, BS, a.k_inv, a.v_inv);
-      __builtin_amdgcn_s_waitcnt(0);
-    }
-  }
   const size_t head_off = (size_t)hkv * TILE;
   const size_t blk_stride = (size_t)a.Hkv * TILE;
 
@@ -174,7 +136,7 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_fp8_kernel(const DecodeAr
     for (int r = 0; r < 4; ++r) {
       const uint16_t pb = cvt_bf16(__builtin_amdgcn_exp2f(z[r] - m_run[r]));
       l_run[r] += bf16_to_f32(pb);
-      p_lds[w][4 * g + r][col] = pb;
+      prow[4 * g + r][col] = pb;
     }
     __builtin_amdgcn_wave_barrier();
     // P as the A operand of PV: row = head col, k slots 8g .. 8g+7 <->
@@ -183,7 +145,7 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_fp8_kernel(const DecodeAr
     {
       u32x4 lo = {0, 0, 0, 0}, hi = {0, 0, 0, 0};
       if (col < HPW) {
-        const u32x4* src = (const u32x4*)&p_lds[w][col][16 * g];
+        const u32x4* src = (const u32x4*)&prow[col][16 * g];
         lo = src[0];
         hi = src[1];
       }
@@ -213,26 +175,22 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_fp8_kernel(const DecodeAr
     __builtin_amdgcn_wave_barrier();
   };
 
-  tile_loop<NBUF, NLOAD, 1>(tbl, t0 / BS, jend, a.nb,
-                            (const uint8_t*)a.kc + head_off + lane * 16,
+  tile_loop<NBUF, NLOAD, 1>(tbl, jfirst, jend, a.nb, (const uint8_t*)a.kc + head_off + lane * 16,
                             (const uint8_t*)a.vc + head_off + col * 32 + g * 16, blk_stride,
-                            lane, bad, process);
+                            lane, bad, process, j_sync);
 
   // ---- epilogue: rows r = 0..3 are head 4g + r; lane holds dims 32m + col ----
-  const bool final_out = !SPLIT || nparts == 1;
-  float* ws_o = a.ws;
-  float* ws_ml = a.ws + (size_t)a.total_parts * a.Hq * D;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const float lt = sum_xor16(row16_sum(l_run[r]));
-    const int qh = qh0 + 4 * g + r;
+    const int hh = 4 * g + r;
     if (final_out) {
       const float inv = lt > 0.f ? a.v_mult / lt : 0.f;
-      uint16_t* o = (uint16_t*)a.out + ((size_t)s * a.Hq + qh) * D + col;
+      uint16_t* o = (uint16_t*)a.out + ((size_t)s * a.Hq + qh0 + hh) * D + col;
 #pragma unroll
       for (int m = 0; m < NLOAD; ++m) o[32 * m] = f32_to_bf16(bad ? NAN : acc[m][r] * inv);
     } else {
-      const size_t pi = (size_t)item * a.Hq + qh;
+      const size_t pi = prow0 + hh;
       float* o = ws_o + pi * D + col;
 #pragma unroll
       for (int m = 0; m < NLOAD; ++m) o[32 * m] = bad ? NAN : acc[m][r] * a.v_mult;
@@ -241,6 +199,125 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_fp8_kernel(const DecodeAr
         ws_ml[pi * 2 + 1] = bad ? NAN : lt;
       }
     }
+  }
+}
+
+// The decode step's store of sequence s's new token (position L - 1) into
+// the slot its table gives, by the wave that will read that block; the wave
+// must wait for it (s_waitcnt) before loading the block.  Returns whether a
+// store was issued.
+__device__ __forceinline__ bool mfma_store_new_token(const DecodeArgs& a, int s, int hkv, int L,
+                                                     int lane) {
+  const int pos = L - 1;
+  const int blk = a.tables[(size_t)s * a.max_blocks + pos / kBS];
+  if ((unsigned)blk >= (unsigned)a.nb) return false;
+  if (lane < kD / 16)
+    write_kv_unit<PKV_FP8_E4M3>(a.new_k, a.new_v, (uint8_t*)a.kc, (uint8_t*)a.vc, s, hkv, lane,
+                                blk * kBS + pos % kBS, a.Hkv, kD, kBS, a.k_inv, a.v_inv);
+  return true;
+}
+
+// Split-K schedule: each wave owns one work item, (sequence, partition) for
+// the kv head of blockIdx.y, flat item blockIdx.x * NW + wave; it writes its
+// own output (one-partition sequence) or partial.  STORE (decode step, one
+// group of 8 query heads per kv head): the wave that reads a sequence's last
+// block first stores the sequence's new token; it is that block's only reader.
+template <int NW, bool SPLIT, bool STORE = false>
+__global__ __launch_bounds__(NW * 64) void decode_mfma_fp8_kernel(const DecodeArgs a) {
+  constexpr int BS = kBS, HPW = kHPW, D = kD;
+  __shared__ uint16_t p_lds[NW][HPW][BS];
+
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int item = blockIdx.x * NW + w;
+  const int n_items = SPLIT ? a.total_parts : a.S;
+  if (item >= n_items) return;
+
+  // ---- locate the work item ----
+  const int G = a.Hq / a.Hkv;
+  const int hkv = blockIdx.y / (G / HPW);
+  const int qh0 = hkv * G + (blockIdx.y % (G / HPW)) * HPW;
+  int s, part, nparts;
+  if constexpr (SPLIT) {
+    s = __builtin_amdgcn_readfirstlane(find_seq(a.part_off, a.S, item, lane));
+    const int p0 = a.part_off[s];
+    part = item - p0;
+    nparts = a.part_off[s + 1] - p0;
+  } else {
+    s = item;
+    part = 0;
+    nparts = 1;
+  }
+  int L = a.lens[s];
+  bool bad = false;
+  if (L < 0) { L = 0; bad = true; }
+  if (L > a.max_blocks * BS) { L = a.max_blocks * BS; bad = true; }
+  const int t0 = SPLIT ? part * a.partition : 0;
+  const int t1 = SPLIT ? min(L, t0 + a.partition) : L;
+  const int jend = (t1 + BS - 1) / BS;
+  if constexpr (STORE) {
+    if (!bad && L > 0 && t0 < L && t1 == L && mfma_store_new_token(a, s, hkv, L, lane))
+      __builtin_amdgcn_s_waitcnt(0);
+  }
+  mfma_item(a, s, hkv, qh0, t0 / BS, jend, t1, bad, !SPLIT || nparts == 1,
+            (size_t)item * a.Hq + qh0, a.ws, a.ws + (size_t)a.total_parts * a.Hq * D, p_lds[w],
+            lane);
+}
+
+// Stream-K schedule (see the vector-ALU stream-K kernel): wave gw of
+// R = a.sk_workers takes tiles [floor(gw*T/R), floor((gw+1)*T/R)) of the
+// T = CU * H_kv * groups tiles laid out as (head group hg, sequence s, tile)
+// and writes each piece as the output (whole item) or as the partial rows
+// [slot][8] of slot gw + hg*S + s.
+template <int NW, bool STORE>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
+void decode_mfma_sk_kernel(const DecodeArgs a) {
+  constexpr int BS = kBS, HPW = kHPW, D = kD;
+  __shared__ uint16_t p_lds[NW][HPW][BS];
+
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int gw = blockIdx.x * NW + w;
+  const int R = a.sk_workers;
+  if (gw >= R) return;
+  const int G = a.Hq / a.Hkv, groups = G / HPW;
+  const int64_t CU = a.sk_cu;
+  const int64_t T = CU * a.Hkv * groups;
+  int64_t x = (int64_t)gw * T / R;
+  const int64_t x1 = (int64_t)(gw + 1) * T / R;
+  const size_t slots = (size_t)R + (size_t)a.Hkv * groups * a.S;
+  float* ws_ml = a.ws + slots * HPW * D;
+
+  while (x < x1) {
+    const int hg = (int)(x / CU);
+    const int rem = (int)(x - (int64_t)hg * CU);
+    const int s = min(__builtin_amdgcn_readfirstlane(find_seq(a.tile_off, a.S, rem, lane)), a.S - 1);
+    const int off = a.tile_off[s];
+    const int n_s = a.tile_off[s + 1] - off;
+    const int j0 = rem - off;
+    const int jn = (int)min((int64_t)n_s, (int64_t)j0 + (x1 - x));
+    if (j0 < 0 || jn <= j0) break;   // offsets are not running sums ending at sk_cu
+    x += jn - j0;
+
+    int L = a.lens[s];
+    bool bad = false;
+    if (L < 0) { L = 0; bad = true; }
+    if (L > a.max_blocks * BS) { L = a.max_blocks * BS; bad = true; }
+    const int nt = (L + BS - 1) / BS;
+    if (nt != n_s) bad = true;               // tile offsets disagree with the length
+    const int jend = min(jn, nt), jfirst = min(j0, jend);
+    const int hkv = hg / groups;
+    const int qh0 = hkv * G + (hg % groups) * HPW;
+    // STORE: the wait for the store comes just before the item's last tile
+    // is loaded, not once per item at its start.
+    int j_sync = -1;
+    if constexpr (STORE) {
+      if (!bad && L > 0 && jend == nt && jfirst < jend && mfma_store_new_token(a, s, hkv, L, lane))
+        j_sync = nt - 1;
+    }
+    const size_t slot = (size_t)gw + (size_t)hg * a.S + s;
+    mfma_item(a, s, hkv, qh0, jfirst, jend, L, bad, j0 == 0 && jn == n_s, slot * HPW, a.ws, ws_ml,
+              p_lds[w], lane, j_sync);
   }
 }
 
@@ -260,16 +337,38 @@ int launch_decode_mfma(const DecodeArgs& a, void* stream, bool store) {
   dim3 grid((items + kWaves - 1) / kWaves, a.Hkv * groups);
   if (a.partition > 0) {
     if (store)
-      hipLaunchKernelGGL((decode_mfma_fp8_kernel<kWaves, kMfmaBufs, true, true>), grid, block, 0, st, a);
+      hipLaunchKernelGGL((decode_mfma_fp8_kernel<kWaves, true, true>), grid, block, 0, st, a);
     else
-      hipLaunchKernelGGL((decode_mfma_fp8_kernel<kWaves, kMfmaBufs, true>), grid, block, 0, st, a);
+      hipLaunchKernelGGL((decode_mfma_fp8_kernel<kWaves, true>), grid, block, 0, st, a);
   } else {
     if (store)
-      hipLaunchKernelGGL((decode_mfma_fp8_kernel<kWaves, kMfmaBufs, false, true>), grid, block, 0, st, a);
+      hipLaunchKernelGGL((decode_mfma_fp8_kernel<kWaves, false, true>), grid, block, 0, st, a);
     else
-      hipLaunchKernelGGL((decode_mfma_fp8_kernel<kWaves, kMfmaBufs, false>), grid, block, 0, st, a);
+      hipLaunchKernelGGL((decode_mfma_fp8_kernel<kWaves, false>), grid, block, 0, st, a);
   }
   return (int)hipGetLastError();
+}
+
+int launch_decode_mfma_sk(const DecodeArgs& a, void* stream, bool store) {
+  hipStream_t st = (hipStream_t)stream;
+  if (store && a.Hq / a.Hkv != 8) return (int)hipErrorInvalidValue;
+  dim3 block(kSkWaves * 64), grid((a.sk_workers + kSkWaves - 1) / kSkWaves);
+  if (store)
+    hipLaunchKernelGGL((decode_mfma_sk_kernel<kSkWaves, true>), grid, block, 0, st, a);
+  else
+    hipLaunchKernelGGL((decode_mfma_sk_kernel<kSkWaves, false>), grid, block, 0, st, a);
+  return (int)hipGetLastError();
+}
+
+int decode_mfma_sk_workers() {
+  int dev = 0, cus = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return -1;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return -1;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+          &per_cu, reinterpret_cast<const void*>(&decode_mfma_sk_kernel<kSkWaves, false>),
+          kSkWaves * 64, 0) != hipSuccess)
+    return -1;
+  return (per_cu > 1 ? per_cu : 1) * cus * kSkWaves;
 }
 
 }  // namespace pkv

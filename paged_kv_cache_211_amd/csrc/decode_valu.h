@@ -429,6 +429,10 @@ __global__ __launch_bounds__(NW * 64) void decode_sk_kernel(const DecodeArgs a) 
     const int qh0 = hkv * G + (hg % groups) * HPW;
     const int32_t* __restrict__ tbl = a.tables + (size_t)s * a.max_blocks;
 
+    // STORE: the new token goes to the item's last tile; the wait for the
+    // store comes just before that tile is loaded, so a wave holding many
+    // short items does not wait once per item at its start.
+    int j_sync = -1;
     if constexpr (STORE) {
       if (!bad && L > 0 && jend == nt && jfirst < jend) {
         const int pos = L - 1;
@@ -437,7 +441,7 @@ __global__ __launch_bounds__(NW * 64) void decode_sk_kernel(const DecodeArgs a) 
           for (int c = lane; c < D / X; c += 64)
             write_kv_unit<KV>(a.new_k, a.new_v, (uint8_t*)a.kc, (uint8_t*)a.vc, s, hkv, c,
                               blk * BS + pos % BS, a.Hkv, D, BS, a.k_inv, a.v_inv);
-          __builtin_amdgcn_s_waitcnt(0);
+          j_sync = nt - 1;
         }
       }
     }
@@ -456,7 +460,8 @@ __global__ __launch_bounds__(NW * 64) void decode_sk_kernel(const DecodeArgs a) 
                               (const uint8_t*)a.vc + head_off + lane * 16, blk_stride, lane, bad,
                               [&](int j, const u32x4* kr, const u32x4* vr) {
                                 st.tile(a.qk_mult, j, L, kr, vr, p_lds[w], lane);
-                              });
+                              },
+                              j_sync);
 
     // ---- this piece: the output when it is the whole item, else a partial ----
     const bool whole = j0 == 0 && jn == n_s;

@@ -64,6 +64,8 @@ int launch_sk_reduce(const DecodeArgs& a, void* stream);
 // (decode_mfma.hip); launch_decode routes eligible calls there.
 bool decode_mfma_eligible(const DecodeArgs& a);
 int launch_decode_mfma(const DecodeArgs& a, void* stream, bool store = false);
+int launch_decode_mfma_sk(const DecodeArgs& a, void* stream, bool store);
+int decode_mfma_sk_workers();
 int launch_splitk_reduce(void* out, const float* ws, const int32_t* part_off, int S, int Hq, int D,
                          int total_parts, pkv_dtype out_dtype, void* stream);
 bool decode_supported(pkv_dtype q, pkv_dtype kv, int D, int BS, int G);

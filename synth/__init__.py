@@ -83,7 +83,7 @@ CONFIGS = {
     4: Config("bf16-prefix", S=128, H_q=32, H_kv=8, d=128, bs=16, q_dtype="bf16", kv_dtype="bf16",
               scale=_SCALE_D128, partition=2048, seed=4, prefix=1030, suffix_range=(16, 512)),
     5: Config("fp8-skewed", S=256, H_q=64, H_kv=8, d=128, bs=32, q_dtype="bf16", kv_dtype="fp8",
-              scale=_SCALE_D128, partition=512, seed=5, long=(8, 32768, 131072),
+              scale=_SCALE_D128, partition=1024, seed=5, long=(8, 32768, 131072),
               short=(248, 64, 512), k_scale=FP8_KV_SCALE, v_scale=FP8_KV_SCALE),
 }
 
