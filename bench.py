@@ -325,6 +325,31 @@ def main():
     t_fused = np.array([a.elapsed_time(b) for a, b in fev]) * 1e3
     fused_us = float(np.mean(t_fused))
 
+    # region 4: the roofline kernel alone, K back-to-back launches between two
+    # events on its stream (cycling the pool layers): its average launch time
+    def run_decode_only(i):
+        kc, vc = layers[i % R]
+        if SK:
+            pkv.paged_attention_decode_streamk_partials(out, q, kc, vc, tab, lens, c.scale,
+                                                        inp["tile_offsets"], inp["total_tiles"],
+                                                        inp["workers"], ws, c.k_scale, c.v_scale)
+        elif P:
+            pkv.paged_attention_decode_partials(out, q, kc, vc, tab, lens, c.scale, c.k_scale,
+                                                c.v_scale, P, inp["partition_offsets"],
+                                                inp["total_partitions"], ws)
+        else:
+            pkv.paged_attention_decode(out, q, kc, vc, tab, lens, c.scale, c.k_scale, c.v_scale)
+
+    for i in range(args.warmup):
+        run_decode_only(i)
+    torch.cuda.synchronize()
+    e0.record()
+    for i in range(args.steps):
+        run_decode_only(i)
+    e1.record()
+    torch.cuda.synchronize()
+    dec_only_us = e0.elapsed_time(e1) / args.steps * 1e3
+
     us_step = ms_step * 1e3
     kv_gbps = ab["kv"] / (us_step * 1e-6) / 1e9
     if n_launch == 1:
@@ -332,14 +357,14 @@ def main():
         kernel, kern_us, kern_bytes = "decode step (store + decode)", fused_us, ab["step"]
     else:
         kernel = ("decode (stream-K)" if SK else "decode (split-K partials)" if P else "decode")
-        kern_us, kern_bytes = dec_us, ab["decode"]
+        kern_us, kern_bytes = dec_only_us, ab["decode"]
     achieved = kern_bytes / (kern_us * 1e-6) / 1e9
     traffic = load_traffic(args.traffic_file, c.key, kernel)
     log(f"[bench] mode {args.mode}: step {us_step:.1f} us (wall {wall / args.steps * 1e6:.1f} us); "
         f"step entry {fused_us:.1f} us in {n_launch} launch(es); separate launches: "
         f"write {np.mean(t_write):.1f} us, decode {dec_us:.1f} us "
         f"[p10 {np.percentile(t_dec, 10):.1f}, p90 {np.percentile(t_dec, 90):.1f}], "
-        f"reduce {np.mean(t_red):.1f} us")
+        f"reduce {np.mean(t_red):.1f} us; decode back to back {dec_only_us:.1f} us")
     log(f"[bench] KV {ab['kv'] / 1e9:.3f} GB/step -> {kv_gbps:.0f} GB/s = "
         f"{100 * kv_gbps / HBM_PEAK_GBPS:.1f}% of {HBM_PEAK_GBPS:.0f}; {kernel} "
         f"{achieved:.0f} GB/s; device copy {copy_gbps:.0f} GB/s; read probe {probe_gbps:.0f} GB/s")
@@ -383,7 +408,8 @@ def main():
         "step_algorithmic_bytes": ab["step"],
         "kernel_us": {"paged_kv_write": round(float(np.mean(t_write)), 2),
                       "decode": round(dec_us, 2), "splitk_reduce": round(float(np.mean(t_red)), 2),
-                      "decode_step_entry": round(fused_us, 2)},
+                      "decode_step_entry": round(fused_us, 2),
+                      "decode_back_to_back": round(dec_only_us, 2)},
         "device_copy_GBps": round(copy_gbps, 1),
         "hbm_read_probe_GBps": round(probe_gbps, 1),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,

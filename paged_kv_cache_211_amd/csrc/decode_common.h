@@ -118,13 +118,20 @@ __device__ __forceinline__ Work locate(const DecodeArgs& a, int hpw, int lane, i
 // the younger tiles outstanding.  kbase/vbase point at this lane's 16 bytes
 // of load 0 of block 0 (head and lane offsets included); load l of a tile is
 // l KiB further.  A block id outside [0, nb) sets `bad` and reads block 0.
-// j_sync >= 0: every earlier memory operation of the wave (a store into that
-// tile, say) completes before tile j_sync is loaded.
-template <int NBUF, int NLOAD, int NW, class Proc>
+// start() runs once, after the first chunk's table load is issued and before
+// any tile load (so memory operations it issues share the table load's wait
+// and precede every tile load); j_sync >= 0: every earlier memory operation
+// of the wave (a store into that tile, say) completes before tile j_sync is
+// loaded.
+struct NoStart {
+  __device__ __forceinline__ void operator()() const {}
+};
+
+template <int NBUF, int NLOAD, int NW, class Proc, class Start = NoStart>
 __device__ __forceinline__ void tile_loop(const int32_t* __restrict__ tbl, int jfirst, int jend,
                                           int nb, const uint8_t* kbase, const uint8_t* vbase,
                                           size_t blk_stride, int lane, bool& bad, Proc&& process,
-                                          int j_sync = -1) {
+                                          int j_sync = -1, Start&& start = Start()) {
   u32x4 kbuf[NBUF][NLOAD], vbuf[NBUF][NLOAD];
   int tbl_v = 0, chunk0 = 0;
   auto load_tile = [&](int jj, u32x4* kd, u32x4* vd) {
@@ -141,6 +148,7 @@ __device__ __forceinline__ void tile_loop(const int32_t* __restrict__ tbl, int j
   for (chunk0 = jfirst; chunk0 < jend; chunk0 += 64 * NW) {
     const int n = min(64, (jend - chunk0 + NW - 1) / NW);  // tiles of this wave in the chunk
     tbl_v = lane < n ? tbl[chunk0 + lane * NW] : 0;
+    if (chunk0 == jfirst) start();
     auto tile = [&](int k) { return chunk0 + k * NW; };
     int k = 0;
     if (n >= NBUF) {
@@ -221,26 +229,22 @@ __device__ __forceinline__ void merge_store(const DecodeArgs& a, const Work& wk,
   }
 }
 
-// Decode step: the workgroup that reads the last block of the sequence
-// first stores the sequence's new token, position L - 1, into the slot its
-// table gives for that position.  Only this workgroup reads that block in the
-// launch (one workgroup per kv head), so waiting for the stores to complete
-// and a workgroup barrier order them before every tile load.
-template <int KV, int D, int BS, int NTHREADS>
-__device__ __forceinline__ void store_new_token(const DecodeArgs& a, const Work& wk) {
+// Decode step: stores sequence s's new token (position L - 1; kv head hkv)
+// into the slot its table gives, from the lanes of the one wave that will
+// read that block; returns the block's tile index (the wave's j_sync) or -1
+// when there is nothing to store.  Called from tile_loop's start hook, so
+// the new row's loads share the table load's wait and the stores precede
+// every tile load of the wave.
+template <int KV, int D, int BS>
+__device__ __forceinline__ void store_new_token(const DecodeArgs& a, int s, int hkv, int L,
+                                                int lane) {
   constexpr int X = 16 / (KV == PKV_F32 ? 4 : KV == PKV_BF16 ? 2 : 1);
-  if (!wk.bad && wk.L > 0 && wk.t0 < wk.L && wk.t1 == wk.L) {
-    const int pos = wk.L - 1;
-    const int blk = a.tables[(size_t)wk.s * a.max_blocks + pos / BS];
-    if ((unsigned)blk < (unsigned)a.nb) {
-      const int slot = blk * BS + pos % BS;
-      for (int c = threadIdx.x; c < D / X; c += NTHREADS)
-        write_kv_unit<KV>(a.new_k, a.new_v, (uint8_t*)a.kc, (uint8_t*)a.vc, wk.s, wk.hkv, c, slot,
-                          a.Hkv, D, BS, a.k_inv, a.v_inv);
-      __builtin_amdgcn_s_waitcnt(0);
-    }
-  }
-  __syncthreads();
+  const int pos = L - 1;
+  const int blk = a.tables[(size_t)s * a.max_blocks + pos / BS];
+  if ((unsigned)blk >= (unsigned)a.nb) return;
+  for (int c = lane; c < D / X; c += 64)
+    write_kv_unit<KV>(a.new_k, a.new_v, (uint8_t*)a.kc, (uint8_t*)a.vc, s, hkv, c,
+                      blk * BS + pos % BS, a.Hkv, D, BS, a.k_inv, a.v_inv);
 }
 
 }  // namespace dec

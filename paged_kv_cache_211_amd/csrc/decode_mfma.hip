@@ -60,7 +60,7 @@ constexpr int kNLoad = kTile / 1024;    // 4 loads of 16 bytes per lane
 __device__ __forceinline__ void mfma_item(const DecodeArgs& a, int s, int hkv, int qh0, int jfirst,
                                           int jend, int t1, bool bad, bool final_out, size_t prow0,
                                           float* ws_o, float* ws_ml, uint16_t (*prow)[kBS],
-                                          int lane, int j_sync = -1) {
+                                          int lane, bool store_new = false, int L = 0) {
   constexpr int D = kD, BS = kBS, HPW = kHPW, TILE = kTile, NLOAD = kNLoad;
   constexpr int NBUF = kMfmaBufs;
   const int col = lane & 31, g = lane >> 5;
@@ -177,7 +177,9 @@ __device__ __forceinline__ void mfma_item(const DecodeArgs& a, int s, int hkv, i
 
   tile_loop<NBUF, NLOAD, 1>(tbl, jfirst, jend, a.nb, (const uint8_t*)a.kc + head_off + lane * 16,
                             (const uint8_t*)a.vc + head_off + col * 32 + g * 16, blk_stride,
-                            lane, bad, process, j_sync);
+                            lane, bad, process, store_new ? jend - 1 : -1, [&] {
+                              if (store_new) store_new_token<PKV_FP8_E4M3, D, BS>(a, s, hkv, L, lane);
+                            });
 
   // ---- epilogue: rows r = 0..3 are head 4g + r; lane holds dims 32m + col ----
 #pragma unroll
@@ -200,21 +202,6 @@ __device__ __forceinline__ void mfma_item(const DecodeArgs& a, int s, int hkv, i
       }
     }
   }
-}
-
-// The decode step's store of sequence s's new token (position L - 1) into
-// the slot its table gives, by the wave that will read that block; the wave
-// must wait for it (s_waitcnt) before loading the block.  Returns whether a
-// store was issued.
-__device__ __forceinline__ bool mfma_store_new_token(const DecodeArgs& a, int s, int hkv, int L,
-                                                     int lane) {
-  const int pos = L - 1;
-  const int blk = a.tables[(size_t)s * a.max_blocks + pos / kBS];
-  if ((unsigned)blk >= (unsigned)a.nb) return false;
-  if (lane < kD / 16)
-    write_kv_unit<PKV_FP8_E4M3>(a.new_k, a.new_v, (uint8_t*)a.kc, (uint8_t*)a.vc, s, hkv, lane,
-                                blk * kBS + pos % kBS, a.Hkv, kD, kBS, a.k_inv, a.v_inv);
-  return true;
 }
 
 // Split-K schedule: each wave owns one work item, (sequence, partition) for
@@ -255,13 +242,9 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_fp8_kernel(const DecodeAr
   const int t0 = SPLIT ? part * a.partition : 0;
   const int t1 = SPLIT ? min(L, t0 + a.partition) : L;
   const int jend = (t1 + BS - 1) / BS;
-  if constexpr (STORE) {
-    if (!bad && L > 0 && t0 < L && t1 == L && mfma_store_new_token(a, s, hkv, L, lane))
-      __builtin_amdgcn_s_waitcnt(0);
-  }
   mfma_item(a, s, hkv, qh0, t0 / BS, jend, t1, bad, !SPLIT || nparts == 1,
             (size_t)item * a.Hq + qh0, a.ws, a.ws + (size_t)a.total_parts * a.Hq * D, p_lds[w],
-            lane);
+            lane, STORE && !bad && L > 0 && t0 < L && t1 == L, L);
 }
 
 // Stream-K schedule (see the vector-ALU stream-K kernel): wave gw of
@@ -308,16 +291,9 @@ void decode_mfma_sk_kernel(const DecodeArgs a) {
     const int jend = min(jn, nt), jfirst = min(j0, jend);
     const int hkv = hg / groups;
     const int qh0 = hkv * G + (hg % groups) * HPW;
-    // STORE: the wait for the store comes just before the item's last tile
-    // is loaded, not once per item at its start.
-    int j_sync = -1;
-    if constexpr (STORE) {
-      if (!bad && L > 0 && jend == nt && jfirst < jend && mfma_store_new_token(a, s, hkv, L, lane))
-        j_sync = nt - 1;
-    }
     const size_t slot = (size_t)gw + (size_t)hg * a.S + s;
     mfma_item(a, s, hkv, qh0, jfirst, jend, L, bad, j0 == 0 && jn == n_s, slot * HPW, a.ws, ws_ml,
-              p_lds[w], lane, j_sync);
+              p_lds[w], lane, STORE && !bad && L > 0 && jend == nt && jfirst < jend, L);
   }
 }
 

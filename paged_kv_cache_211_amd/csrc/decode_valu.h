@@ -328,7 +328,6 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const DecodeArgs a) {
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const Work wk = locate<SPLIT, BS>(a, HPW, lane, blockIdx.x);
-  if constexpr (STORE) store_new_token<KV, D, BS, NW * 64>(a, wk);
   bool bad = wk.bad;
   const int32_t* __restrict__ tbl = a.tables + (size_t)wk.s * a.max_blocks;
   const size_t head_off = (size_t)wk.hkv * TILE;
@@ -345,11 +344,23 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const DecodeArgs a) {
   }
   st.reset();
   const int t1 = wk.t1;
+  // STORE: the wave that reads the last block stores the new token into it
+  // (waves take tiles t0/BS + w, + NW, ...), then waits for the store only
+  // before loading that block.
+  const int jlast = wk.jend - 1;
+  const bool my_store = STORE && !wk.bad && wk.L > 0 && wk.t0 < wk.L && wk.t1 == wk.L &&
+                        (jlast - wk.t0 / BS) % NW == w;
   tile_loop<NBUF, NLOAD, NW>(tbl, wk.t0 / BS + w, wk.jend, a.nb,
                              (const uint8_t*)a.kc + head_off + lane * 16,
                              (const uint8_t*)a.vc + head_off + lane * 16, blk_stride, lane, bad,
                              [&](int j, const u32x4* kr, const u32x4* vr) {
                                st.tile(a.qk_mult, j, t1, kr, vr, p_lds[w], lane);
+                             },
+                             my_store ? jlast : -1,
+                             [&] {
+                               if constexpr (STORE) {
+                                 if (my_store) store_new_token<KV, D, BS>(a, wk.s, wk.hkv, wk.L, lane);
+                               }
                              });
 
   // ---- per-wave totals ----
@@ -385,7 +396,6 @@ template <int KV, int D, int BS, int HPW, int NW, int NBUF, bool STORE>
 __global__ __launch_bounds__(NW * 64) void decode_sk_kernel(const DecodeArgs a) {
   using St = ValuHeads<KV, D, BS, HPW, kQLds>;
   constexpr int NLOAD = St::NLOAD, RU = St::RU, DPI = St::DPI, TILE = Geo<KV, D, BS>::TILE;
-  constexpr int X = St::X;
 
   __shared__ float p_lds[NW][HPW][BS];
   __shared__ u32x4 q_lds[kQLds ? NW : 1][kQLds ? St::QU : 1];
@@ -429,22 +439,9 @@ __global__ __launch_bounds__(NW * 64) void decode_sk_kernel(const DecodeArgs a) 
     const int qh0 = hkv * G + (hg % groups) * HPW;
     const int32_t* __restrict__ tbl = a.tables + (size_t)s * a.max_blocks;
 
-    // STORE: the new token goes to the item's last tile; the wait for the
-    // store comes just before that tile is loaded, so a wave holding many
-    // short items does not wait once per item at its start.
-    int j_sync = -1;
-    if constexpr (STORE) {
-      if (!bad && L > 0 && jend == nt && jfirst < jend) {
-        const int pos = L - 1;
-        const int blk = tbl[pos / BS];
-        if ((unsigned)blk < (unsigned)a.nb) {
-          for (int c = lane; c < D / X; c += 64)
-            write_kv_unit<KV>(a.new_k, a.new_v, (uint8_t*)a.kc, (uint8_t*)a.vc, s, hkv, c,
-                              blk * BS + pos % BS, a.Hkv, D, BS, a.k_inv, a.v_inv);
-          j_sync = nt - 1;
-        }
-      }
-    }
+    // STORE: the new token goes to the item's last tile, stored from the
+    // start hook and waited for just before that tile is loaded.
+    const bool my_store = STORE && !bad && L > 0 && jend == nt && jfirst < jend;
 
     if constexpr (kQLds) {
       __builtin_amdgcn_wave_barrier();   // the previous item's reads of q_lds come first
@@ -461,7 +458,12 @@ __global__ __launch_bounds__(NW * 64) void decode_sk_kernel(const DecodeArgs a) 
                               [&](int j, const u32x4* kr, const u32x4* vr) {
                                 st.tile(a.qk_mult, j, L, kr, vr, p_lds[w], lane);
                               },
-                              j_sync);
+                              my_store ? nt - 1 : -1,
+                              [&] {
+                                if constexpr (STORE) {
+                                  if (my_store) store_new_token<KV, D, BS>(a, s, hkv, L, lane);
+                                }
+                              });
 
     // ---- this piece: the output when it is the whole item, else a partial ----
     const bool whole = j0 == 0 && jn == n_s;
