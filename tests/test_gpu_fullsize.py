@@ -1,12 +1,16 @@
 """Parity at the full workload sizes, in the launch configuration bench.py
-times (each workload's split-K partition).
+times: the decode step (new-token store inside the decode launch, then the
+split-K reduce) at each workload's split-K partition, and then the plain
+decode over the same cache.
 
-The device runs the whole batch; the oracle recomputes sampled sequences one
-by one (the first and last, the longest and shortest, and a few seeded
-others): their tables, slots and cache bits must match exactly and their
-outputs within tolerance.  For every sequence, properties that hold at any
-size are checked: outputs are finite and lie within the range of the values
-attended over (softmax weights are a convex combination).
+The device runs the whole batch with the decode token allocated but not yet
+stored (its slot holds the NaN poison until the step stores it); the oracle
+recomputes sampled sequences one by one (the first and last, the longest and
+shortest, and a few seeded others): their tables, slots and cache bits must
+match exactly and their outputs within tolerance.  For every sequence,
+properties that hold at any size are checked: outputs are finite and lie
+within the range of the values attended over (softmax weights are a convex
+combination).
 """
 
 import numpy as np
@@ -39,20 +43,27 @@ def test_full_size_sampled(cfg_id):
     seqs = sorted({0, c.S - 1, int(L.argmax()), int(L.argmin()),
                    *[int(s) for s in rng.choice(c.S, size=min(3, c.S), replace=False)]})
     st, oslots = replay.build(wl, only_seqs=seqs)
-    cache, step = H.build(wl, poison=True)
+    cache, step = H.build(wl, poison=True, write_step=False)
     torch.cuda.synchronize()
     assert np.array_equal(step["slots"].astype(np.int64), oslots)
     for s in range(c.S):
         assert list(cache.alloc.block_table(s)) == st.model.table(s), f"table of seq {s}"
-    check_cache_bits(cache, st, wl, np.array(seqs))
-    got = gpu_decode(cache, step, wl, c.partition)
-    assert np.isfinite(got).all()
-    vmax = 8.0 if c.kv_dtype == "fp8" else 7.0   # |N(0,1)| draws stay far below 7 sigma here
-    assert np.abs(got).max() <= vmax
     ref, wsum = OA.paged_decode(wl.q, c.q_dtype, st.kc, st.vc, st.tables(c.S), L, bs=c.bs,
                                 cache_dtype=c.kv_dtype, scale=c.scale, k_scale=c.k_scale,
                                 v_scale=c.v_scale, seqs=seqs)
-    err = np.abs(got[seqs] - ref[seqs]).max()
-    print(f"  sampled seqs {seqs}: max abs err {err:.3e} (tol {H.TOL[c.kv_dtype]})", flush=True)
-    assert err <= H.TOL[c.kv_dtype]
     assert np.abs(wsum[seqs] - 1).max() < 1e-12
+    vmax = 8.0 if c.kv_dtype == "fp8" else 7.0   # |N(0,1)| draws stay far below 7 sigma here
+    # the decode step as bench.py times it, then the plain decode over the stored cache
+    inp = cache.decode_inputs(range(c.S), c.partition)
+    out = torch.full_like(step["query"], float("nan"))
+    cache.decode_step(step["query"], step["key"], step["value"], inp, c.scale, out=out)
+    torch.cuda.synchronize()
+    check_cache_bits(cache, st, wl, np.array(seqs))
+    for name, got in (("decode step", out.double().cpu().numpy()),
+                      ("decode", gpu_decode(cache, step, wl, c.partition))):
+        assert np.isfinite(got).all(), name
+        assert np.abs(got).max() <= vmax, name
+        err = np.abs(got[seqs] - ref[seqs]).max()
+        print(f"  {name}, sampled seqs {seqs}: max abs err {err:.3e} (tol {H.TOL[c.kv_dtype]})",
+              flush=True)
+        assert err <= H.TOL[c.kv_dtype], name
