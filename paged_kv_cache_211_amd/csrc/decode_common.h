@@ -72,18 +72,20 @@ struct Work {
   int p0;      // first flat partition of the sequence (SPLIT)
   int hkv;     // kv head
   int qh0;     // first query head of the group
+  int item;    // flat work index (partial row of the workspace)
   bool bad;    // length out of range: the output becomes NaN
 };
 
 // `item` is the flat work index: the split-K partition (SPLIT) or the
-// sequence (one pass).
+// sequence (one pass); `hg` the head group (kv head * groups + group).
 template <bool SPLIT, int BS>
-__device__ __forceinline__ Work locate(const DecodeArgs& a, int hpw, int lane, int item) {
+__device__ __forceinline__ Work locate(const DecodeArgs& a, int hpw, int lane, int item, int hg) {
   Work wk;
   const int G = a.Hq / a.Hkv;
   const int groups = G / hpw;
-  wk.hkv = blockIdx.y / groups;
-  wk.qh0 = wk.hkv * G + (blockIdx.y % groups) * hpw;
+  wk.hkv = hg / groups;
+  wk.qh0 = wk.hkv * G + (hg % groups) * hpw;
+  wk.item = item;
   int part;
   if constexpr (SPLIT) {
     wk.s = __builtin_amdgcn_readfirstlane(find_seq(a.part_off, a.S, item, lane));
@@ -219,7 +221,7 @@ __device__ __forceinline__ void merge_store(const DecodeArgs& a, const Work& wk,
       else
         ((uint16_t*)a.out)[oi] = f32_to_bf16(r);
     } else {
-      const size_t pi = (size_t)blockIdx.x * a.Hq + qh;
+      const size_t pi = (size_t)wk.item * a.Hq + qh;
       ws_o[pi * D + dim] = any_bad ? NAN : O * a.v_mult;
       if (dim == 0) {
         ws_ml[pi * 2] = M;

@@ -216,14 +216,19 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_fp8_kernel(const DecodeAr
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int item = blockIdx.x * NW + w;
+  // XCD-aware order (workgroup ids go round-robin to the 8 XCDs): the head
+  // group is the id's low part, so with 8 head groups every XCD serves one
+  // kv head.
+  const int G = a.Hq / a.Hkv;
+  const int nhg = a.Hkv * (G / HPW);
+  const int hg = blockIdx.x % nhg;
+  const int item = (blockIdx.x / nhg) * NW + w;
   const int n_items = SPLIT ? a.total_parts : a.S;
   if (item >= n_items) return;
 
   // ---- locate the work item ----
-  const int G = a.Hq / a.Hkv;
-  const int hkv = blockIdx.y / (G / HPW);
-  const int qh0 = hkv * G + (blockIdx.y % (G / HPW)) * HPW;
+  const int hkv = hg / (G / HPW);
+  const int qh0 = hkv * G + (hg % (G / HPW)) * HPW;
   int s, part, nparts;
   if constexpr (SPLIT) {
     s = __builtin_amdgcn_readfirstlane(find_seq(a.part_off, a.S, item, lane));
@@ -310,7 +315,7 @@ int launch_decode_mfma(const DecodeArgs& a, void* stream, bool store) {
   if (store && groups != 1) return (int)hipErrorInvalidValue;
   dim3 block(kWaves * 64);
   const int items = a.partition > 0 ? a.total_parts : a.S;
-  dim3 grid((items + kWaves - 1) / kWaves, a.Hkv * groups);
+  dim3 grid((items + kWaves - 1) / kWaves * a.Hkv * groups);
   if (a.partition > 0) {
     if (store)
       hipLaunchKernelGGL((decode_mfma_fp8_kernel<kWaves, true, true>), grid, block, 0, st, a);

@@ -327,7 +327,12 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const DecodeArgs a) {
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const Work wk = locate<SPLIT, BS>(a, HPW, lane, blockIdx.x);
+  // XCD-aware order: workgroup ids go round-robin to the 8 XCDs (each with
+  // its own L2), so the head group is the id's low part: with 8 head groups
+  // every XCD serves one kv head, and blocks that several sequences share
+  // stay in that XCD's L2.
+  const int nhg = a.Hkv * (a.Hq / a.Hkv / HPW);
+  const Work wk = locate<SPLIT, BS>(a, HPW, lane, blockIdx.x / nhg, blockIdx.x % nhg);
   bool bad = wk.bad;
   const int32_t* __restrict__ tbl = a.tables + (size_t)wk.s * a.max_blocks;
   const size_t head_off = (size_t)wk.hkv * TILE;
@@ -525,7 +530,7 @@ int launch_t(const DecodeArgs& a, bool store, hipStream_t st) {
   const int groups = a.Hq / a.Hkv / HPW;
   if (store && groups != 1) return (int)hipErrorInvalidValue;
   dim3 block(kWaves * 64);
-  dim3 grid(a.partition > 0 ? a.total_parts : a.S, a.Hkv * groups);
+  dim3 grid((a.partition > 0 ? a.total_parts : a.S) * a.Hkv * groups);
   if (a.partition > 0) {
     if (store)
       hipLaunchKernelGGL((decode_kernel<KV, D, BS, HPW, kWaves, kBufs, true, true>), grid, block, 0, st, a);
