@@ -58,8 +58,9 @@ def parse():
                    help="token budget of the oracle's timed sample")
     p.add_argument("--traffic-file", default=None)
     p.add_argument("--mode", choices=("fused", "separate"), default="fused")
-    p.add_argument("--schedule", choices=("splitk", "streamk"), default="splitk",
-                   help="split-K partitions of --partition tokens, or stream-K persistent waves")
+    p.add_argument("--schedule", choices=("splitk", "streamk", "prefix"), default="splitk",
+                   help="split-K partitions of --partition tokens, stream-K persistent waves, or "
+                        "the shared-prefix decode (shared blocks read once per 32 query rows)")
     p.add_argument("--workers", type=int, default=0, help="stream-K waves (0 = resident count)")
     return p.parse_args()
 
@@ -73,8 +74,12 @@ def algorithmic_bytes(wl):
     o = q
     tbl = int(((L + c.bs - 1) // c.bs).sum()) * 4 + c.S * 4
     write = c.S * c.H_kv * c.d * 2 * (ELEM[c.src_dtype] + e)
-    return {"kv": kv, "q": q, "o": o, "tables": tbl, "write": write,
-            "decode": kv + q + o + tbl, "step": kv + q + o + tbl + write}
+    # unique KV bytes: a shared prefix's full blocks counted once
+    shared = (c.prefix // c.bs) * c.bs if c.prefix else 0
+    kv_unique = (shared + int((L - shared).sum())) * c.H_kv * c.d * 2 * e if shared else kv
+    return {"kv": kv, "kv_unique": kv_unique, "q": q, "o": o, "tables": tbl, "write": write,
+            "decode": kv + q + o + tbl, "decode_unique": kv_unique + q + o + tbl,
+            "step": kv + q + o + tbl + write}
 
 
 def src_sha():
@@ -191,7 +196,14 @@ def main():
     log(f"[bench] {R} pool layers of {pool_bytes / 1e9:.2f} GB")
 
     SK = args.schedule == "streamk"
-    if SK:
+    PF = args.schedule == "prefix"
+    if PF:
+        inp = cache.decode_inputs(range(c.S), P, prefix=True, num_q_heads=c.H_q)
+        ws = cache.workspace(inp["prefix_totals"][0], c.H_q, c.d)
+        log(f"[bench] shared prefix: groups {inp['prefix']['group_offsets'].cpu().tolist()} "
+            f"prefix blocks {inp['prefix']['group_prefix_blocks'].cpu().tolist()} "
+            f"plan totals {inp['prefix_totals']}")
+    elif SK:
         P = 0
         inp = cache.decode_inputs(range(c.S), streamk=True, num_q_heads=c.H_q,
                                   q_dtype=W.TORCH_CACHE[c.q_dtype], workers=args.workers or None)
@@ -203,18 +215,27 @@ def main():
     q, key, value, slots = step["query"], step["key"], step["value"], step["slots_dev"]
     out = torch.empty_like(q)
     tab, lens = inp["block_tables"], inp["context_lens"]
-    if SK:
+    if PF:
+        n_launch = 4
+    elif SK:
         n_launch = 2 if pkv.paged_attention_decode_step_launches(c.H_q, c.H_kv, c.d, c.bs, q.dtype,
                                                                  cache.dtype, 0) == 1 else 3
     else:
         n_launch = pkv.paged_attention_decode_step_launches(c.H_q, c.H_kv, c.d, c.bs, q.dtype,
                                                             cache.dtype, P)
 
+    def run_prefix(kc, vc):
+        pkv.paged_attention_decode_prefix(out, q, kc, vc, tab, lens, c.scale, P, inp["prefix"],
+                                          inp["prefix_totals"], ws, c.k_scale, c.v_scale)
+
     def run_fused(i, ev=None):
         kc, vc = layers[i % R]
         if ev:
             ev[0].record()
-        if SK:
+        if PF:   # no in-kernel store on this schedule: the store, then the decode
+            pkv.paged_kv_write(key, value, kc, vc, slots, k_scale=c.k_scale, v_scale=c.v_scale)
+            run_prefix(kc, vc)
+        elif SK:
             pkv.paged_attention_decode_step_streamk(out, q, key, value, kc, vc, tab, lens, c.scale,
                                                     inp["tile_offsets"], inp["total_tiles"],
                                                     inp["workers"], ws, c.k_scale, c.v_scale)
@@ -232,7 +253,11 @@ def main():
         pkv.paged_kv_write(key, value, kc, vc, slots, k_scale=c.k_scale, v_scale=c.v_scale)
         if ev:
             ev[1].record()
-        if SK:
+        if PF:
+            run_prefix(kc, vc)
+            if ev:
+                ev[2].record()
+        elif SK:
             pkv.paged_attention_decode_streamk_partials(out, q, kc, vc, tab, lens, c.scale,
                                                         inp["tile_offsets"], inp["total_tiles"],
                                                         inp["workers"], ws, c.k_scale, c.v_scale)
@@ -329,7 +354,9 @@ def main():
     # events on its stream (cycling the pool layers): its average launch time
     def run_decode_only(i):
         kc, vc = layers[i % R]
-        if SK:
+        if PF:
+            run_prefix(kc, vc)
+        elif SK:
             pkv.paged_attention_decode_streamk_partials(out, q, kc, vc, tab, lens, c.scale,
                                                         inp["tile_offsets"], inp["total_tiles"],
                                                         inp["workers"], ws, c.k_scale, c.v_scale)
@@ -355,6 +382,9 @@ def main():
     if n_launch == 1:
         # the step is one kernel (store inside the decode, no partitions)
         kernel, kern_us, kern_bytes = "decode step (store + decode)", fused_us, ab["step"]
+    elif PF:
+        # the three launches of the shared-prefix decode, over the unique bytes
+        kernel, kern_us, kern_bytes = "decode (shared prefix + suffix + reduce)", dec_only_us, ab["decode_unique"]
     else:
         kernel = ("decode (stream-K)" if SK else "decode (split-K partials)" if P else "decode")
         kern_us, kern_bytes = dec_only_us, ab["decode"]

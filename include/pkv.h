@@ -284,6 +284,60 @@ int paged_attention_decode_step_streamk(void* out, const void* query, const void
                                         int workers, void* workspace, size_t workspace_bytes,
                                         void* stream);
 
+/* ---------------------------------------------------------------------------
+ * Shared-prefix decode ("Day 6/90 of Inference Engineering": prompts that
+ * begin alike share their prefix blocks by reference and continue in blocks
+ * of their own).  The same result as paged_attention_decode, scheduled so
+ * that the blocks a group of sequences shares are read once per 32 query
+ * rows ((sequence, query head) pairs of a kv head) instead of once per
+ * sequence: a matrix-core pass over each group's shared blocks leaves
+ * partials, the split-K decode covers every sequence's own tokens from the
+ * end of its group's prefix, and the split-K reduce combines both.
+ * bf16 query and cache, head_dim 128, block_size 16 (else
+ * PKV_ERR_UNSUPPORTED).
+ *
+ * paged_attention_prefix_plan (host only): groups are runs of consecutive
+ * sequences, group g = sequences group_offsets[g] .. group_offsets[g+1]-1
+ * (group_offsets[0] = 0, group_offsets[num_groups] = num_seqs), whose tables
+ * all begin with the same group_prefix_blocks[g] block ids (0 = nothing
+ * shared).  Every member must be at least that many blocks long.  Outputs
+ * (caller-owned host arrays): row_offsets_out [num_seqs+1] (partial rows of
+ * each sequence: its suffix partitions, then one row per 8 prefix blocks),
+ * suffix_offsets_out [num_seqs+1] (suffix partitions), token_start_out
+ * [num_seqs] (first own token), prefix_item_offsets_out [num_groups+1]
+ * (waves of the prefix pass), totals_out [3] = (rows, suffix partitions,
+ * prefix waves).  PKV_ERR_INVALID on inconsistent groups.
+ *
+ * paged_attention_decode_prefix: the usual decode arguments, then
+ * partition_tokens (> 0) and the plan's arrays uploaded to the device
+ * (group_offsets, group_prefix_blocks, row_offsets, suffix_offsets,
+ * token_start, prefix_item_offsets) with its three totals; workspace of
+ * paged_attention_workspace_bytes(total_rows, num_q_heads, head_dim) bytes.
+ * Three launches on `stream`.  A block id out of range in a group's prefix
+ * makes every member's output NaN.
+ * ------------------------------------------------------------------------- */
+int paged_attention_prefix_plan(const int32_t* context_lens_host, int num_seqs,
+                                const int32_t* group_offsets_host,
+                                const int32_t* group_prefix_blocks_host, int num_groups,
+                                int block_size, int partition_tokens, int num_q_heads,
+                                int num_kv_heads, int32_t* row_offsets_out,
+                                int32_t* suffix_offsets_out, int32_t* token_start_out,
+                                int32_t* prefix_item_offsets_out, int32_t* totals_out);
+
+int paged_attention_decode_prefix(void* out, const void* query, const void* key_cache,
+                                  const void* value_cache, const int32_t* block_tables,
+                                  int max_blocks_per_seq, const int32_t* context_lens,
+                                  int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                                  int block_size, int num_blocks, float scale, pkv_dtype q_dtype,
+                                  pkv_dtype cache_dtype, float k_scale, float v_scale,
+                                  int partition_tokens, const int32_t* group_offsets,
+                                  const int32_t* group_prefix_blocks, int num_groups,
+                                  const int32_t* row_offsets, const int32_t* suffix_offsets,
+                                  const int32_t* token_start, const int32_t* prefix_item_offsets,
+                                  int total_rows, int total_suffix_partitions,
+                                  int total_prefix_items, void* workspace,
+                                  size_t workspace_bytes, void* stream);
+
 /* paged_attention_splitk_reduce -- combine the partials of every sequence
  * with more than one partition ("PagedAttention Kernel" article §3.2: uneven
  * pages need the work split): with running maxima m_p (log2 domain), sums

@@ -288,6 +288,57 @@ def paged_attention_decode_step_streamk(out, query, new_key, new_value, key_cach
                                                     _stream(stream)))
 
 
+def paged_attention_prefix_plan(context_lens_host, group_offsets, group_prefix_blocks, block_size,
+                                partition_tokens, num_q_heads, num_kv_heads):
+    """Host plan of the shared-prefix decode: groups of consecutive sequences
+    group_offsets[g] .. group_offsets[g+1] share their first
+    group_prefix_blocks[g] blocks.  Returns a dict of int32 numpy arrays
+    (row_offsets, suffix_offsets, token_start, prefix_item_offsets) and the
+    totals (rows, suffix_partitions, prefix_items)."""
+    lens = np.ascontiguousarray(np.asarray(context_lens_host, dtype=np.int32))
+    go = np.ascontiguousarray(np.asarray(group_offsets, dtype=np.int32))
+    gb = np.ascontiguousarray(np.asarray(group_prefix_blocks, dtype=np.int32))
+    S, G = lens.size, gb.size
+    if go.size != G + 1:
+        raise PkvError(-1, "group_offsets must have one entry more than group_prefix_blocks")
+    row = np.zeros(S + 1, np.int32)
+    suf = np.zeros(S + 1, np.int32)
+    ts = np.zeros(max(S, 1), np.int32)
+    pre = np.zeros(G + 1, np.int32)
+    tot = np.zeros(3, np.int32)
+    P = lambda x: x.ctypes.data_as(_native.pi32)
+    check(lib().paged_attention_prefix_plan(P(lens), S, P(go), P(gb), G, int(block_size),
+                                            int(partition_tokens), int(num_q_heads),
+                                            int(num_kv_heads), P(row), P(suf), P(ts), P(pre),
+                                            P(tot)))
+    return {"row_offsets": row, "suffix_offsets": suf, "token_start": ts[:S],
+            "prefix_item_offsets": pre, "group_offsets": go, "group_prefix_blocks": gb,
+            "totals": tuple(int(t) for t in tot)}
+
+
+def paged_attention_decode_prefix(out, query, key_cache, value_cache, block_tables, context_lens,
+                                  scale, partition_tokens, plan_dev, totals, workspace,
+                                  k_scale=1.0, v_scale=1.0, stream=None):
+    """Decode with each group's shared prefix blocks read once per 32 query
+    rows.  plan_dev: device int32 tensors of the plan (group_offsets,
+    group_prefix_blocks, row_offsets, suffix_offsets, token_start,
+    prefix_item_offsets); totals: the plan's host totals."""
+    a = _decode_args(out, query, key_cache, value_cache, block_tables, context_lens, scale,
+                     k_scale, v_scale, 0, None, 0, None)
+    names = ("group_offsets", "group_prefix_blocks", "row_offsets", "suffix_offsets",
+             "token_start", "prefix_item_offsets")
+    for n in names:
+        _need(plan_dev[n], n, torch.int32)
+    _need(workspace, "workspace")
+    d = {n: _ptr(plan_dev[n]) for n in names}
+    n_groups = plan_dev["group_prefix_blocks"].numel()
+    check(lib().paged_attention_decode_prefix(
+        *a[:18], int(partition_tokens), d["group_offsets"], d["group_prefix_blocks"], n_groups,
+        d["row_offsets"], d["suffix_offsets"], d["token_start"], d["prefix_item_offsets"],
+        int(totals[0]), int(totals[1]), int(totals[2]), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
 def paged_attention_splitk_reduce(out, workspace, partition_offsets, total_partitions, stream=None):
     _need(out, "out")
     _need(workspace, "workspace")

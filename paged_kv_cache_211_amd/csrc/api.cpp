@@ -455,6 +455,114 @@ int paged_attention_decode_step_streamk(void* out, const void* query, const void
   return streamk_common(c, new_key, new_value, tile_offsets, total_tiles, workers, true, stream);
 }
 
+int paged_attention_prefix_plan(const int32_t* context_lens_host, int num_seqs,
+                                const int32_t* group_offsets_host,
+                                const int32_t* group_prefix_blocks_host, int num_groups,
+                                int block_size, int partition_tokens, int num_q_heads,
+                                int num_kv_heads, int32_t* row_offsets_out,
+                                int32_t* suffix_offsets_out, int32_t* token_start_out,
+                                int32_t* prefix_item_offsets_out, int32_t* totals_out) {
+  if (num_seqs < 0 || num_groups < 0 || block_size <= 0 || partition_tokens <= 0 ||
+      partition_tokens % block_size != 0 || num_q_heads <= 0 || num_kv_heads <= 0 ||
+      num_q_heads % num_kv_heads != 0 || !row_offsets_out || !suffix_offsets_out ||
+      !prefix_item_offsets_out || !totals_out || (num_seqs > 0 && (!context_lens_host || !token_start_out)) ||
+      !group_offsets_host || (num_groups > 0 && !group_prefix_blocks_host))
+    return fail(PKV_ERR_INVALID, "bad arguments");
+  if (group_offsets_host[0] != 0 || group_offsets_host[num_groups] != num_seqs)
+    return fail(PKV_ERR_INVALID, "group offsets must run from 0 to num_seqs");
+  const int G = num_q_heads / num_kv_heads;
+  int64_t rows = 0, suf = 0, items = 0;
+  row_offsets_out[0] = 0;
+  suffix_offsets_out[0] = 0;
+  prefix_item_offsets_out[0] = 0;
+  for (int g = 0; g < num_groups; ++g) {
+    const int a0 = group_offsets_host[g], a1 = group_offsets_host[g + 1];
+    const int pb = group_prefix_blocks_host[g];
+    if (a1 < a0 || pb < 0) return fail(PKV_ERR_INVALID, "bad group %d", g);
+    const int64_t pt = (int64_t)pb * block_size;
+    const int npre = (pb + kPrefixPieceBlocks - 1) / kPrefixPieceBlocks;
+    for (int s = a0; s < a1; ++s) {
+      const int64_t L = context_lens_host[s];
+      if (L < pt) return fail(PKV_ERR_INVALID, "sequence %d is shorter than its group's prefix", s);
+      int64_t nsuf = (L - pt + partition_tokens - 1) / partition_tokens;
+      if (nsuf + npre == 0) nsuf = 1;   // an empty sequence still gets its (zero) row
+      suf += nsuf;
+      rows += nsuf + npre;
+      if (rows > INT32_MAX) return fail(PKV_ERR_INVALID, "too many rows");
+      suffix_offsets_out[s + 1] = (int32_t)suf;
+      row_offsets_out[s + 1] = (int32_t)rows;
+      token_start_out[s] = (int32_t)pt;
+    }
+    const int64_t rb = ((int64_t)(a1 - a0) * G + 31) / 32;
+    items += (int64_t)num_kv_heads * rb * npre;
+    if (items > INT32_MAX) return fail(PKV_ERR_INVALID, "too many prefix items");
+    prefix_item_offsets_out[g + 1] = (int32_t)items;
+  }
+  totals_out[0] = (int32_t)rows;
+  totals_out[1] = (int32_t)suf;
+  totals_out[2] = (int32_t)items;
+  clear_error();
+  return PKV_OK;
+}
+
+int paged_attention_decode_prefix(void* out, const void* query, const void* key_cache,
+                                  const void* value_cache, const int32_t* block_tables,
+                                  int max_blocks_per_seq, const int32_t* context_lens,
+                                  int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                                  int block_size, int num_blocks, float scale, pkv_dtype q_dtype,
+                                  pkv_dtype cache_dtype, float k_scale, float v_scale,
+                                  int partition_tokens, const int32_t* group_offsets,
+                                  const int32_t* group_prefix_blocks, int num_groups,
+                                  const int32_t* row_offsets, const int32_t* suffix_offsets,
+                                  const int32_t* token_start, const int32_t* prefix_item_offsets,
+                                  int total_rows, int total_suffix_partitions,
+                                  int total_prefix_items, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  if (partition_tokens <= 0) return fail(PKV_ERR_INVALID, "partition_tokens must be > 0");
+  if (total_rows < num_seqs || total_suffix_partitions < 0 || total_prefix_items < 0 ||
+      num_groups < 0)
+    return fail(PKV_ERR_INVALID, "bad plan totals");
+  if (!group_offsets || !group_prefix_blocks || !row_offsets || !suffix_offsets ||
+      !token_start || !prefix_item_offsets)
+    return fail(PKV_ERR_INVALID, "null pointer argument");
+  // validate as a split-K call over total_rows partial rows
+  DecodeCall c{out, query, key_cache, value_cache, block_tables, max_blocks_per_seq, context_lens,
+               num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, scale,
+               q_dtype, cache_dtype, k_scale, v_scale, partition_tokens, suffix_offsets,
+               total_rows, workspace, workspace_bytes};
+  DecodeArgs a;
+  int rc = check_decode(c, &a);
+  if (rc) return rc;
+  if (!decode_prefix_supported(a))
+    return fail(PKV_ERR_UNSUPPORTED, "shared-prefix decode needs bf16 q and cache, head_dim 128, "
+                                     "block_size 16");
+  if (num_seqs == 0) return PKV_OK;
+  a.ws_rows = total_rows;
+  PrefixArgs p;
+  p.group_off = group_offsets;
+  p.group_blocks = group_prefix_blocks;
+  p.pre_off = prefix_item_offsets;
+  p.row_off = row_offsets;
+  p.suf_off = suffix_offsets;
+  p.n_groups = num_groups;
+  p.total_items = total_prefix_items;
+  p.total_rows = total_rows;
+  rc = hip_status(launch_decode_prefix(a, p, stream), "shared-prefix decode launch");
+  if (rc) return rc;
+  if (total_suffix_partitions > 0) {
+    DecodeArgs b = a;
+    b.part_off = suffix_offsets;
+    b.total_parts = total_suffix_partitions;
+    b.t_start = token_start;
+    b.row_off = row_offsets;
+    rc = hip_status(launch_decode(b, stream), "shared-prefix suffix decode launch");
+    if (rc) return rc;
+  }
+  return hip_status(launch_splitk_reduce(out, a.ws, row_offsets, num_seqs, num_q_heads, head_dim,
+                                         total_rows, q_dtype, stream, 1),
+                    "shared-prefix reduce launch");
+}
+
 int paged_attention_splitk_reduce(void* out, const void* workspace, size_t workspace_bytes,
                                   const int32_t* partition_offsets, int num_seqs,
                                   int num_q_heads, int head_dim, int total_partitions,

@@ -145,11 +145,11 @@ template <int D, bool F32OUT, int HG>
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(void* __restrict__ out,
                                                             const float* __restrict__ ws,
                                                             const int32_t* __restrict__ part_off,
-                                                            int Hq, int total_parts) {
+                                                            int Hq, int total_parts, int min_parts) {
   const int s = blockIdx.x, qh0 = blockIdx.y * HG;
   const int p0 = part_off[s];
   const int n = part_off[s + 1] - p0;
-  if (n <= 1) return;
+  if (n < min_parts || n <= 0) return;
   merge_heads<D, F32OUT, HG>(out, ((size_t)s * Hq + qh0) * D, ws, ws + (size_t)total_parts * Hq * D,
                              (size_t)p0 * Hq + qh0, Hq, n);
 }
@@ -301,7 +301,7 @@ int launch_sk_reduce(const DecodeArgs& a0, void* stream) {
 }
 
 int launch_splitk_reduce(void* out, const float* ws, const int32_t* part_off, int S, int Hq, int D,
-                         int total_parts, pkv_dtype out_dtype, void* stream) {
+                         int total_parts, pkv_dtype out_dtype, void* stream, int min_parts) {
   hipStream_t st = (hipStream_t)stream;
   const int cap = 256 / D;   // heads per workgroup: 64 float4 columns at most
   const int hgs = Hq % cap == 0 ? cap : Hq % 2 == 0 ? 2 : 1;
@@ -310,7 +310,7 @@ int launch_splitk_reduce(void* out, const float* ws, const int32_t* part_off, in
   return with_hg(hgs, [&](auto hg) {
     constexpr int HG = decltype(hg)::value;
     auto go = [&](auto kern) {
-      hipLaunchKernelGGL(kern, grid, block, 0, st, out, ws, part_off, Hq, total_parts);
+      hipLaunchKernelGGL(kern, grid, block, 0, st, out, ws, part_off, Hq, total_parts, min_parts);
     };
     if (D == 64)
       f32 ? go(splitk_reduce_kernel<64, true, HG>) : go(splitk_reduce_kernel<64, false, HG>);

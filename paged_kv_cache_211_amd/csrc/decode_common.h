@@ -87,11 +87,17 @@ __device__ __forceinline__ Work locate(const DecodeArgs& a, int hpw, int lane, i
   wk.qh0 = wk.hkv * G + (hg % groups) * hpw;
   wk.item = item;
   int part;
+  int tstart = 0;
   if constexpr (SPLIT) {
     wk.s = __builtin_amdgcn_readfirstlane(find_seq(a.part_off, a.S, item, lane));
     wk.p0 = a.part_off[wk.s];
     part = item - wk.p0;
     wk.nparts = a.part_off[wk.s + 1] - wk.p0;
+    if (a.t_start) {   // shared-prefix suffix pass: always a partial row
+      tstart = a.t_start[wk.s];
+      wk.item = a.row_off[wk.s] + part;
+      wk.nparts = 2;
+    }
   } else {
     wk.s = item;
     wk.p0 = item;
@@ -103,7 +109,7 @@ __device__ __forceinline__ Work locate(const DecodeArgs& a, int hpw, int lane, i
   if (L < 0) { L = 0; wk.bad = true; }
   if (L > a.max_blocks * BS) { L = a.max_blocks * BS; wk.bad = true; }
   wk.L = L;
-  wk.t0 = SPLIT ? part * a.partition : 0;
+  wk.t0 = SPLIT ? tstart + part * a.partition : 0;
   wk.t1 = SPLIT ? min(L, wk.t0 + a.partition) : L;
   wk.jend = (wk.t1 + BS - 1) / BS;
   return wk;
@@ -196,7 +202,7 @@ __device__ __forceinline__ void merge_store(const DecodeArgs& a, const Work& wk,
 #pragma unroll
   for (int ww = 0; ww < NW; ++ww) any_bad |= bad_lds[ww];
   float* ws_o = a.ws;
-  float* ws_ml = a.ws + (size_t)a.total_parts * a.Hq * D;
+  float* ws_ml = a.ws + (size_t)(a.ws_rows ? a.ws_rows : a.total_parts) * a.Hq * D;
   for (int i = threadIdx.x; i < HPW * D; i += NW * 64) {
     const int hh = i / D, dim = i % D;
     float M = -INFINITY;

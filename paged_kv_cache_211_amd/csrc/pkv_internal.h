@@ -43,6 +43,27 @@ struct DecodeArgs {
   // sk_cu = tile_off[S] (host copy), sk_workers = waves launched.
   const int32_t* tile_off = nullptr;
   int sk_cu = 0, sk_workers = 0;
+  // Shared-prefix decode (suffix pass): sequence s's own tokens start at
+  // t_start[s] (device), its split-K partitions are part_off rows (suffix
+  // numbering), written as partial rows row_off[s] + part.  Null otherwise.
+  const int32_t* t_start = nullptr;
+  const int32_t* row_off = nullptr;
+  int ws_rows = 0;   // partial rows of the workspace when not total_parts
+};
+
+// Shared-prefix decode: groups of consecutive sequences (group_off[g] ..
+// group_off[g+1]) share their first group_blocks[g] blocks; prefix work items
+// (waves) of group g are pre_off[g] .. pre_off[g+1]; per sequence, rows
+// row_off[s] .. row_off[s+1] hold its suffix partitions (suf_off numbering)
+// then one prefix piece of kPrefixPieceBlocks blocks each.  All device.
+constexpr int kPrefixPieceBlocks = 8;
+struct PrefixArgs {
+  const int32_t* group_off = nullptr;
+  const int32_t* group_blocks = nullptr;
+  const int32_t* pre_off = nullptr;
+  const int32_t* row_off = nullptr;
+  const int32_t* suf_off = nullptr;
+  int n_groups = 0, total_items = 0, total_rows = 0;
 };
 
 // Kernel launchers (decode.hip, kv_ops.hip).  Return hipError_t as int.
@@ -60,14 +81,21 @@ int decode_sk_workers(const DecodeArgs& a);
 int decode_sk_heads_per_wave(const DecodeArgs& a);
 int launch_decode_sk(const DecodeArgs& a, bool store, void* stream);
 int launch_sk_reduce(const DecodeArgs& a, void* stream);
+// Shared-prefix decode (decode_prefix.hip): bf16 query and cache, head_dim
+// 128, block size 16.
+bool decode_prefix_supported(const DecodeArgs& a);
+int launch_decode_prefix(const DecodeArgs& a, const PrefixArgs& p, void* stream);
 // Matrix-core decode for fp8 key/value tiles with query heads in groups of 8
 // (decode_mfma.hip); launch_decode routes eligible calls there.
 bool decode_mfma_eligible(const DecodeArgs& a);
 int launch_decode_mfma(const DecodeArgs& a, void* stream, bool store = false);
 int launch_decode_mfma_sk(const DecodeArgs& a, void* stream, bool store);
 int decode_mfma_sk_workers();
+// min_parts: sequences with fewer rows are left alone (2 for split-K, whose
+// single-partition sequences write their output directly; 1 when every
+// sequence has partials only).
 int launch_splitk_reduce(void* out, const float* ws, const int32_t* part_off, int S, int Hq, int D,
-                         int total_parts, pkv_dtype out_dtype, void* stream);
+                         int total_parts, pkv_dtype out_dtype, void* stream, int min_parts = 2);
 bool decode_supported(pkv_dtype q, pkv_dtype kv, int D, int BS, int G);
 
 int launch_kv_write(const void* key, const void* value, void* kc, void* vc, const int32_t* slots,

@@ -12,7 +12,8 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-from . import (BlockAllocator, empty_pools, paged_attention_decode, paged_attention_decode_step,
+from . import (BlockAllocator, empty_pools, paged_attention_decode, paged_attention_decode_prefix,
+               paged_attention_decode_step, paged_attention_prefix_plan,
                paged_attention_decode_step_streamk, paged_attention_decode_streamk,
                paged_attention_partition_offsets, paged_attention_streamk_workers,
                paged_attention_streamk_workspace_bytes, paged_attention_tile_offsets,
@@ -84,17 +85,29 @@ class PagedKVCache:
 
     # -- decode -------------------------------------------------------------------
     def decode_inputs(self, seqs, partition_tokens: int = 0, streamk: bool = False,
-                      num_q_heads: int | None = None, q_dtype=None, workers: int | None = None):
+                      num_q_heads: int | None = None, q_dtype=None, workers: int | None = None,
+                      prefix: bool = False, prefix_min_blocks: int = 8):
         """Device tables, lengths and schedule metadata for a decode over seqs:
         split-K partitions of partition_tokens (0 = one pass), or with
         streamk=True the tile offsets and wave count of the stream-K schedule
         (num_q_heads and q_dtype needed; workers defaults to the resident
-        waves of this device)."""
+        waves of this device), or with prefix=True the shared-prefix plan for
+        the runs of sequences whose tables share at least prefix_min_blocks
+        leading blocks (partition_tokens > 0 and num_q_heads needed)."""
         lens = self.seq_lens(seqs)
         inp = {"block_tables": self.block_tables(seqs),
                "context_lens": torch.from_numpy(lens).to(self.device),
                "partition_tokens": int(partition_tokens), "partition_offsets": None,
                "total_partitions": 0, "lens_host": lens, "streamk": bool(streamk)}
+        inp["prefix"] = None
+        if prefix:
+            go, gb = self.shared_prefix_groups(seqs, prefix_min_blocks)
+            plan = paged_attention_prefix_plan(lens, go, gb, self.bs, partition_tokens,
+                                               num_q_heads, self.H)
+            inp["prefix"] = {k: torch.from_numpy(plan[k]).to(self.device)
+                             for k in ("group_offsets", "group_prefix_blocks", "row_offsets",
+                                       "suffix_offsets", "token_start", "prefix_item_offsets")}
+            inp["prefix_totals"] = plan["totals"]
         if streamk:
             off, tot = paged_attention_tile_offsets(lens, self.bs)
             inp["tile_offsets"] = torch.from_numpy(off).to(self.device)
@@ -106,6 +119,38 @@ class PagedKVCache:
             inp["partition_offsets"] = torch.from_numpy(off).to(self.device)
             inp["total_partitions"] = tot
         return inp
+
+    def shared_prefix_groups(self, seqs, min_blocks: int = 8):
+        """Runs of consecutive sequences whose tables start with the same block
+        ids (shared by reference, so identical contents): (group_offsets,
+        group_prefix_blocks) for the shared-prefix decode.  A run is kept when
+        it has at least two members and min_blocks shared blocks; every
+        shared block is full (a shared, partly filled last block is copied on
+        write before it is appended to)."""
+        seqs = list(seqs)
+        tabs = [self.alloc.block_table(s) for s in seqs]
+        offs, blocks = [0], []
+        i = 0
+        while i < len(seqs):
+            j, common = i + 1, len(tabs[i])
+            while j < len(seqs):
+                c = 0
+                lim = min(common, len(tabs[j]))
+                while c < lim and tabs[j][c] == tabs[i][c]:
+                    c += 1
+                if c < min_blocks:
+                    break
+                common = c
+                j += 1
+            if j - i < 2:
+                common = 0
+            # full blocks only: a member's last block may still be filling
+            for k in range(i, j):
+                common = min(common, (self.alloc.seq_len(seqs[k]) - 1) // self.bs if j - i > 1 else 0)
+            offs.append(j)
+            blocks.append(max(common, 0))
+            i = j
+        return np.array(offs, np.int32), np.array(blocks, np.int32)
 
     def _scratch(self, need):
         if self._ws is None or self._ws.numel() < need:
@@ -163,6 +208,14 @@ class PagedKVCache:
     def decode(self, query, inp, scale, out=None, stream=None):
         S, Hq, D = query.shape
         out = torch.empty_like(query) if out is None else out
+        if inp.get("prefix") is not None:
+            ws = self.workspace(inp["prefix_totals"][0], Hq, D)
+            paged_attention_decode_prefix(out, query, self.key_cache, self.value_cache,
+                                          inp["block_tables"], inp["context_lens"], scale,
+                                          inp["partition_tokens"], inp["prefix"],
+                                          inp["prefix_totals"], ws, k_scale=self.k_scale,
+                                          v_scale=self.v_scale, stream=stream)
+            return out
         if inp["streamk"]:
             paged_attention_decode_streamk(out, query, self.key_cache, self.value_cache,
                                            inp["block_tables"], inp["context_lens"], scale,

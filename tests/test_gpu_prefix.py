@@ -1,0 +1,148 @@
+"""Shared-prefix decode (each group's shared prefix blocks read once per 32
+query rows by a matrix-core pass, the rest by the split-K kernel from the end
+of the prefix, combined by the reduce) against the fp64 oracle, through the C
+ABI."""
+
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import replay
+from paged_kv_cache_211_amd import workload as H
+
+from .test_gpu_parity import oracle_out
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    import paged_kv_cache_211_amd  # noqa: F401  (fails loudly if libpkv.so is missing)
+
+
+def _case(name):
+    print(f"\n[case] {name}", flush=True)
+
+
+def prefix_decode(cache, step, wl, P, groups=None, inp=None):
+    """groups: None (detected from the tables) or (group_offsets, prefix_blocks)."""
+    from paged_kv_cache_211_amd import paged_attention_prefix_plan
+    c = wl.cfg
+    if inp is None:
+        inp = cache.decode_inputs(range(c.S), P, prefix=True, num_q_heads=c.H_q,
+                                  prefix_min_blocks=1)
+        if groups is not None:
+            plan = paged_attention_prefix_plan(inp["lens_host"], groups[0], groups[1], c.bs, P,
+                                               c.H_q, c.H_kv)
+            inp["prefix"] = {k: torch.from_numpy(plan[k]).cuda()
+                             for k in ("group_offsets", "group_prefix_blocks", "row_offsets",
+                                       "suffix_offsets", "token_start", "prefix_item_offsets")}
+            inp["prefix_totals"] = plan["totals"]
+    out = torch.full_like(step["query"], float("nan"))
+    cache.decode(step["query"], inp, c.scale, out=out)
+    torch.cuda.synchronize()
+    return out.double().cpu().numpy(), inp
+
+
+def _workload(G=4, seed=104, **kw):
+    base = synth.SMALL[4]
+    return synth.make(dataclasses.replace(base, H_q=base.H_kv * G, seed=seed, **kw))
+
+
+@pytest.mark.parametrize("G", [4, 8, 1])
+def test_prefix_detected_groups(G):
+    wl = _workload(G)
+    c = wl.cfg
+    _case(f"shared-prefix decode, detected groups, G={G}")
+    st, _ = replay.build(wl)
+    ref, _ = oracle_out(wl, st)
+    cache, step = H.build(wl, poison=True)
+    go, gb = cache.shared_prefix_groups(range(c.S), min_blocks=1)
+    # one group of every sequence sharing the prefix's full blocks
+    assert go.tolist() == [0, c.S] and gb.tolist() == [c.prefix // c.bs]
+    for P in (c.bs, c.partition, 4 * c.partition):
+        got, inp = prefix_decode(cache, step, wl, P)
+        assert inp["prefix_totals"][2] > 0
+        assert np.isfinite(got).all()
+        err = np.abs(got - ref).max()
+        print(f"  partition {P}: max abs err {err:.3e}", flush=True)
+        assert err <= H.TOL[c.kv_dtype], (P, err)
+
+
+@pytest.mark.parametrize("G,S", [(4, 11), (8, 5), (1, 3)])
+def test_prefix_several_pieces(G, S):
+    """A 17-block prefix (pieces of 8, 8 and 1 blocks, the last an odd single
+    block) and a row count that leaves the last 32-row block partly empty."""
+    wl = _workload(G, seed=140 + G, S=S, prefix=280)
+    c = wl.cfg
+    _case(f"shared-prefix decode, 17 prefix blocks, S={S} G={G}")
+    st, _ = replay.build(wl)
+    ref, _ = oracle_out(wl, st)
+    cache, step = H.build(wl, poison=True)
+    go, gb = cache.shared_prefix_groups(range(c.S), min_blocks=1)
+    assert go.tolist() == [0, c.S] and gb.tolist() == [17]
+    for P in (c.bs, c.partition):
+        got, _ = prefix_decode(cache, step, wl, P)
+        assert np.isfinite(got).all()
+        err = np.abs(got - ref).max()
+        print(f"  partition {P}: max abs err {err:.3e}", flush=True)
+        assert err <= H.TOL[c.kv_dtype], (P, err)
+
+
+@pytest.mark.parametrize("groups", [
+    ([0, 3, 8], [4, 3]),          # two groups, an odd block count
+    ([0, 8], [1]),                # one block shared
+    ([0, 1, 8], [0, 4]),          # a singleton with nothing shared
+    ([0, 2, 5, 8], [2, 0, 4]),    # a group with nothing shared in the middle
+])
+def test_prefix_explicit_groups(groups):
+    wl = _workload(4)
+    c = wl.cfg
+    _case(f"shared-prefix decode, groups {groups}")
+    st, _ = replay.build(wl)
+    ref, _ = oracle_out(wl, st)
+    cache, step = H.build(wl, poison=True)
+    for P in (c.bs, c.partition):
+        got, _ = prefix_decode(cache, step, wl, P, groups=(np.array(groups[0]), np.array(groups[1])))
+        assert np.isfinite(got).all()
+        assert np.abs(got - ref).max() <= H.TOL[c.kv_dtype], P
+
+
+def test_prefix_bad_block_poisons_the_group():
+    wl = _workload(4)
+    c = wl.cfg
+    _case("shared-prefix decode, out-of-range prefix block id")
+    cache, step = H.build(wl, poison=True)
+    groups = (np.array([0, 4, 8]), np.array([4, 4]))
+    inp = None
+    _, inp = prefix_decode(cache, step, wl, c.partition, groups=groups)
+    tab = inp["block_tables"].clone()
+    tab[4, 1] = wl.num_blocks + 5    # the second group's prefix comes from sequence 4's table
+    inp["block_tables"] = tab
+    got, _ = prefix_decode(cache, step, wl, c.partition, inp=inp)
+    assert np.isnan(got[4:]).all()
+    assert np.isfinite(got[:4]).all()
+
+
+def test_prefix_full_size_sampled():
+    wl = synth.make(4)
+    c = wl.cfg
+    L = wl.context_lens
+    _case(f"shared-prefix decode, full prefix workload S={c.S}")
+    rng = np.random.default_rng(2004)
+    seqs = sorted({0, c.S - 1, int(L.argmax()), int(L.argmin()),
+                   *[int(s) for s in rng.choice(c.S, size=3, replace=False)]})
+    st, _ = replay.build(wl, only_seqs=seqs)
+    cache, step = H.build(wl, poison=True)
+    got, inp = prefix_decode(cache, step, wl, c.partition)
+    assert inp["prefix"]["group_prefix_blocks"].cpu().tolist() == [c.prefix // c.bs]
+    assert np.isfinite(got).all()
+    ref, _ = oracle_out(wl, st, seqs=seqs)
+    err = np.abs(got[seqs] - ref[seqs]).max()
+    print(f"  sampled seqs {seqs}: max abs err {err:.3e}", flush=True)
+    assert err <= H.TOL[c.kv_dtype]

@@ -225,3 +225,45 @@ def test_decode_argument_validation_needs_no_gpu(pkv):
     assert w == -2
     assert L.paged_kv_copy_blocks(fake, fake, fake, 3, 100, 10, None) == -1
     assert L.paged_attention_splitk_reduce(fake, fake, 16, fake, 2, 8, 128, 2, 1, None) == -3
+
+
+def test_prefix_plan_matches_its_definition():
+    """The shared-prefix plan: per sequence its suffix partitions (from the end
+    of the group's prefix) then one row per prefix piece of 8 blocks; prefix
+    waves per group = kv heads x ceil(members * G / 32) x prefix pieces."""
+    from paged_kv_cache_211_amd import paged_attention_prefix_plan
+    bs, P, Hq, Hkv = 16, 64, 8, 2
+    G = Hq // Hkv
+    lens = np.array([340, 400, 320, 200, 150, 148, 0, 16, 300], np.int32)
+    go = np.array([0, 3, 4, 6, 8, 9], np.int32)
+    gb = np.array([20, 0, 9, 0, 8], np.int32)
+    plan = paged_attention_prefix_plan(lens, go, gb, bs, P, Hq, Hkv)
+    rows, suf, items = [0], [0], [0]
+    ts = []
+    for g in range(len(gb)):
+        npre = -(-gb[g] // 8)
+        for s in range(go[g], go[g + 1]):
+            pt = gb[g] * bs
+            nsuf = -(-(lens[s] - pt) // P)
+            if nsuf + npre == 0:
+                nsuf = 1
+            rows.append(rows[-1] + nsuf + npre)
+            suf.append(suf[-1] + nsuf)
+            ts.append(pt)
+        items.append(items[-1] + Hkv * (-(-((go[g + 1] - go[g]) * G) // 32)) * npre)
+    assert plan["row_offsets"].tolist() == rows
+    assert plan["suffix_offsets"].tolist() == suf
+    assert plan["token_start"].tolist() == ts
+    assert plan["prefix_item_offsets"].tolist() == items
+    assert plan["totals"] == (rows[-1], suf[-1], items[-1])
+
+
+def test_prefix_plan_rejects_inconsistent_groups():
+    from paged_kv_cache_211_amd import PkvError, paged_attention_prefix_plan
+    lens = np.array([100, 40], np.int32)
+    with pytest.raises(PkvError):   # sequence 1 is shorter than the 4-block prefix
+        paged_attention_prefix_plan(lens, [0, 2], [4], 16, 64, 4, 4)
+    with pytest.raises(PkvError):   # groups do not end at num_seqs
+        paged_attention_prefix_plan(lens, [0, 1], [0], 16, 64, 4, 4)
+    with pytest.raises(PkvError):   # partition not a multiple of the block size
+        paged_attention_prefix_plan(lens, [0, 2], [0], 16, 40, 4, 4)
