@@ -24,6 +24,12 @@ and then one decode step appends exactly one token per sequence, so the
 context length of the step counts the token written in that step.  A shared
 prefix is prefilled once on sequence 0, forked to every other sequence, and
 each sequence then appends its private suffix in sequence order.
+
+Chunked prefill inputs (``PREFILL``): the same cache recipe, then each
+sequence's last C_s tokens are taken as the chunk whose query rows attend
+over the cache; chunk lengths from ``default_rng([seed, 6])`` (integer
+uniform over [lo, hi] clipped to the context), chunk query rows from
+``default_rng([seed, 5])`` as fp32 N(0, 1) rounded into the query dtype.
 """
 
 from __future__ import annotations
@@ -57,6 +63,7 @@ class Config:
     short: tuple = ()      # ... then (count, lo, hi) short ones
     prefix: int = 0        # shared prompt prefix length (tokens)
     suffix_range: tuple = ()
+    chunk: tuple = ()      # chunked prefill: (lo, hi) query rows per sequence
     num_blocks: int = 0    # fixed pool size; 0 = two times the blocks the workload needs
     k_scale: float = 1.0
     v_scale: float = 1.0
@@ -99,6 +106,39 @@ SMALL = {
     5: replace(CONFIGS[5], key="fp8-skewed-small", S=8, seed=105, long=(2, 1500, 3000),
                short=(6, 10, 100)),
 }
+
+
+# Chunked prefill over the paged cache: the GQA shape with each sequence's
+# last 512 tokens as the chunk (full size), and small cases the oracle
+# finishes in seconds (several blocks, several 32-row query blocks, ragged
+# chunks from 1 row to the whole context).
+PREFILL = {
+    "full": Config("bf16-gqa-prefill", S=16, H_q=32, H_kv=8, d=128, bs=16, q_dtype="bf16",
+                   kv_dtype="bf16", scale=_SCALE_D128, partition=0, seed=6,
+                   len_range=(1024, 8192), chunk=(512, 512)),
+    "small": Config("bf16-gqa-prefill-small", S=5, H_q=32, H_kv=8, d=128, bs=16, q_dtype="bf16",
+                    kv_dtype="bf16", scale=_SCALE_D128, partition=0, seed=106,
+                    len_range=(20, 300), chunk=(1, 120)),
+}
+
+
+def prefill_chunks(wl: "Workload", lo: int | None = None, hi: int | None = None) -> np.ndarray:
+    """Seeded chunk lengths [S] (int64): C_s uniform in [min(lo, L_s), min(hi, L_s)]."""
+    c = wl.cfg
+    lo = c.chunk[0] if lo is None else lo
+    hi = c.chunk[1] if hi is None else hi
+    rng = np.random.default_rng([c.seed, 6])
+    L = wl.context_lens
+    return np.array([rng.integers(min(lo, int(l)), min(hi, int(l)), endpoint=True) for l in L],
+                    dtype=np.int64)
+
+
+def prefill_queries(wl: "Workload", chunk_lens) -> np.ndarray:
+    """Seeded chunk query rows, stored bits [sum(chunk_lens), H_q, d]."""
+    c = wl.cfg
+    T = int(np.sum(chunk_lens))
+    rng = np.random.default_rng([c.seed, 5])
+    return _round(rng.standard_normal((T, c.H_q, c.d), dtype=np.float32), c.q_dtype)
 
 
 def _round(x32: np.ndarray, dtype: str) -> np.ndarray:
