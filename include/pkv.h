@@ -338,6 +338,39 @@ int paged_attention_decode_prefix(void* out, const void* query, const void* key_
                                   int total_prefix_items, void* workspace,
                                   size_t workspace_bytes, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * paged_attention_prefill -- chunked prefill over the paged cache.
+ * The block table makes a sequence's scattered blocks read as one contiguous
+ * cache ("Day 6/90 of Inference Engineering", PagedAttention notes), and
+ * attention is QK^T, softmax, PV block by block ("PagedAttention Kernel：大
+ * 模型推理优化的显存管理革新" §3.1, fp32 accumulation per §6).  The pages
+ * only describe decode; for a chunk of new tokens this takes the plain
+ * causal reading: sequence s holds context_lens[s] = L tokens (the chunk's
+ * keys and values already stored, e.g. by paged_kv_write), its last
+ * C = query_start[s+1] - query_start[s] positions are the chunk, and chunk
+ * row i, at position L - C + i, attends tokens 0 .. L - C + i:
+ *   out[query_start[s] + i, g, :] = softmax_t(scale * q . k_t) v_t  over
+ *   those tokens, kv head g / (num_q_heads / num_kv_heads).
+ *
+ *  out, query     [total rows][num_q_heads][head_dim] bf16 (device), rows of
+ *                 all chunks in sequence order
+ *  query_start    [num_seqs + 1] int32 (device), non-decreasing, [0] = 0
+ *  max_query_len  >= every chunk length (sizes the grid); rows of a longer
+ *                 chunk past max_query_len are left unwritten
+ *  other arguments as paged_attention_decode; bf16 query and cache,
+ *  head_dim 128, block_size 16 (else PKV_ERR_UNSUPPORTED); k_scale and
+ *  v_scale are ignored.  A chunk longer than its context, or a block id out
+ *  of range among the blocks a row block reads, gives NaN rows.  One launch
+ *  on `stream`, no workspace.
+ * ------------------------------------------------------------------------- */
+int paged_attention_prefill(void* out, const void* query, const void* key_cache,
+                            const void* value_cache, const int32_t* block_tables,
+                            int max_blocks_per_seq, const int32_t* context_lens,
+                            const int32_t* query_start, int num_seqs, int max_query_len,
+                            int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                            int num_blocks, float scale, pkv_dtype q_dtype, pkv_dtype cache_dtype,
+                            float k_scale, float v_scale, void* stream);
+
 /* paged_attention_splitk_reduce -- combine the partials of every sequence
  * with more than one partition ("PagedAttention Kernel" article §3.2: uneven
  * pages need the work split): with running maxima m_p (log2 domain), sums

@@ -339,6 +339,31 @@ def paged_attention_decode_prefix(out, query, key_cache, value_cache, block_tabl
         workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
+def paged_attention_prefill(out, query, key_cache, value_cache, block_tables, context_lens,
+                            query_start, max_query_len, scale, k_scale=1.0, v_scale=1.0,
+                            stream=None):
+    """Chunked prefill: query rows [T, H_q, head_dim] of every sequence's last
+    C_s positions (C_s = query_start[s+1] - query_start[s]), causal attention
+    over the paged cache into out [T, H_q, head_dim]."""
+    nb, H, D, bs = _pool_shape(key_cache, value_cache)
+    for t, n in ((out, "out"), (query, "query"), (key_cache, "key_cache"), (value_cache, "value_cache")):
+        _need(t, n)
+    _need(block_tables, "block_tables", torch.int32)
+    _need(context_lens, "context_lens", torch.int32)
+    _need(query_start, "query_start", torch.int32)
+    T, Hq, Dq = query.shape
+    S = context_lens.numel()
+    if Dq != D or tuple(out.shape) != (T, Hq, D) or out.dtype != query.dtype:
+        raise PkvError(-1, "query/out must be [T, H_q, head_dim] of one dtype")
+    if block_tables.dim() != 2 or block_tables.shape[0] != S or query_start.numel() != S + 1:
+        raise PkvError(-1, "block_tables must be [S, max_blocks] and query_start [S + 1]")
+    check(lib().paged_attention_prefill(
+        _ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache), _ptr(block_tables),
+        block_tables.shape[1], _ptr(context_lens), _ptr(query_start), S, int(max_query_len), Hq,
+        H, D, bs, nb, float(scale), cache_dtype_code(query), cache_dtype_code(key_cache),
+        float(k_scale), float(v_scale), _stream(stream)))
+
+
 def paged_attention_splitk_reduce(out, workspace, partition_offsets, total_partitions, stream=None):
     _need(out, "out")
     _need(workspace, "workspace")

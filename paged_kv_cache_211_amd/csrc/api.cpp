@@ -563,6 +563,57 @@ int paged_attention_decode_prefix(void* out, const void* query, const void* key_
                     "shared-prefix reduce launch");
 }
 
+int paged_attention_prefill(void* out, const void* query, const void* key_cache,
+                            const void* value_cache, const int32_t* block_tables,
+                            int max_blocks_per_seq, const int32_t* context_lens,
+                            const int32_t* query_start, int num_seqs, int max_query_len,
+                            int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                            int num_blocks, float scale, pkv_dtype q_dtype, pkv_dtype cache_dtype,
+                            float k_scale, float v_scale, void* stream) {
+  (void)k_scale;
+  (void)v_scale;
+  if (!out || !query || !key_cache || !value_cache || !block_tables || !context_lens ||
+      !query_start)
+    return fail(PKV_ERR_INVALID, "null pointer argument");
+  if (num_seqs < 0 || max_query_len < 0 || num_q_heads <= 0 || num_kv_heads <= 0 ||
+      max_blocks_per_seq <= 0 || num_blocks <= 0)
+    return fail(PKV_ERR_INVALID, "bad sizes");
+  if (num_q_heads % num_kv_heads != 0)
+    return fail(PKV_ERR_INVALID, "num_q_heads %% num_kv_heads != 0");
+  if (!valid_dtype(q_dtype) || !valid_dtype(cache_dtype)) return fail(PKV_ERR_INVALID, "unknown dtype");
+  if (!std::isfinite(scale)) return fail(PKV_ERR_INVALID, "scale must be finite");
+  if (!prefill_supported(q_dtype, cache_dtype, head_dim, block_size))
+    return fail(PKV_ERR_UNSUPPORTED, "prefill needs bf16 query and cache, head_dim 128, "
+                                     "block_size 16");
+  const int G = num_q_heads / num_kv_heads;
+  const long long qblocks = prefill_query_blocks(max_query_len, G);
+  const long long total = qblocks * num_kv_heads * (long long)num_seqs;
+  if (total > (long long)INT32_MAX - 8) return fail(PKV_ERR_INVALID, "too many query blocks");
+  if ((long long)max_blocks_per_seq * block_size > (long long)INT32_MAX)
+    return fail(PKV_ERR_INVALID, "max_blocks_per_seq * block_size exceeds int32");
+  if (num_seqs == 0 || max_query_len == 0) {
+    clear_error();
+    return PKV_OK;
+  }
+  PrefillArgs a;
+  a.out = out;
+  a.q = query;
+  a.kc = key_cache;
+  a.vc = value_cache;
+  a.tables = block_tables;
+  a.lens = context_lens;
+  a.q_start = query_start;
+  a.S = num_seqs;
+  a.Hq = num_q_heads;
+  a.Hkv = num_kv_heads;
+  a.max_blocks = max_blocks_per_seq;
+  a.nb = num_blocks;
+  a.qblocks = (int)qblocks;
+  a.total_wg = (int)total;
+  a.qk_mult = scale * kLog2eHost;
+  return hip_status(launch_prefill(a, stream), "prefill launch");
+}
+
 int paged_attention_splitk_reduce(void* out, const void* workspace, size_t workspace_bytes,
                                   const int32_t* partition_offsets, int num_seqs,
                                   int num_q_heads, int head_dim, int total_partitions,

@@ -66,6 +66,23 @@ struct PrefixArgs {
   int n_groups = 0, total_items = 0, total_rows = 0;
 };
 
+// Chunked prefill (prefill.hip): sequence s owns query rows q_start[s] ..
+// q_start[s+1]-1, its last C positions; qblocks workgroups per (sequence, kv
+// head) cover up to qblocks * 128 (position, head) rows; total_wg = S * Hkv *
+// qblocks.  Pointers are device pointers.
+struct PrefillArgs {
+  void* out = nullptr;
+  const void* q = nullptr;
+  const void* kc = nullptr;
+  const void* vc = nullptr;
+  const int32_t* tables = nullptr;
+  const int32_t* lens = nullptr;
+  const int32_t* q_start = nullptr;
+  int S = 0, Hq = 0, Hkv = 0, max_blocks = 0, nb = 0;
+  int qblocks = 0, total_wg = 0;
+  float qk_mult = 0.f;   // scale * log2(e)
+};
+
 // Kernel launchers (decode.hip, kv_ops.hip).  Return hipError_t as int.
 int launch_decode(const DecodeArgs& a, void* stream);
 // Decode step (decode.hip): whether the decode launch itself can store the
@@ -85,6 +102,9 @@ int launch_sk_reduce(const DecodeArgs& a, void* stream);
 // 128, block size 16.
 bool decode_prefix_supported(const DecodeArgs& a);
 int launch_decode_prefix(const DecodeArgs& a, const PrefixArgs& p, void* stream);
+bool prefill_supported(pkv_dtype q, pkv_dtype kv, int D, int BS);
+int prefill_query_blocks(int max_query_len, int G);
+int launch_prefill(const PrefillArgs& a, void* stream);
 // Matrix-core decode for fp8 key/value tiles with query heads in groups of 8
 // (decode_mfma.hip); launch_decode routes eligible calls there.
 bool decode_mfma_eligible(const DecodeArgs& a);

@@ -1,0 +1,269 @@
+// Chunked prefill over the paged cache: the last C tokens of a sequence are
+// a chunk of new query rows, and chunk row i (position p = L - C + i)
+// attends the sequence's tokens 0 .. p, all read through the block table
+// ("Day 6/90 of Inference Engineering": the table makes the scattered blocks
+// read as one contiguous cache; "PagedAttention Kernel：大模型推理优化的显存
+// 管理革新" §3.1: QK^T per block, softmax, PV block by block on matrix
+// units; fp32 accumulation per §6).
+//
+// One wave carries 32 query rows, (position, query head) pairs of one kv head
+// in position-major order, and walks the blocks its rows can see two at a
+// time (32 tokens).  Both products run transposed on
+// v_mfma_f32_32x32x16_bf16 so that every lane owns one query row:
+//   S^T[32 tokens x 32 rows] = K[tokens x 128] . Q^T[128 x rows]   (8 k-steps)
+//   O^T[128 dims x 32 rows] += V^T[dims x 16 tokens] . P^T[16 tokens x rows]
+//                                                   (per block, 4 dim slices)
+// The row's running max and sum then live in the lane (no cross-lane
+// reductions per tile) and the rescale of O is a per-lane multiply.
+//
+// Lane layouts of the 32x32x16 bf16 MFMA (lane l, col = l % 32, g = l / 32):
+//   A[i][k]: lane holds row i = col, k = 8g .. 8g+7
+//   B[k][j]: lane holds column j = col, k = 8g .. 8g+7
+//   C[i][j]: register r holds row 8(r/4) + 4g + r%4, column col
+// S^T: A row i of a block pair is the key of token sigma(i) (bits 2 and 3 of
+// the in-block index swapped), loaded as its 16-byte key unit for dims
+// 16sl + 8g .. +7; then C register 8b + i of lane (col, g) holds token
+// 16b + 8g + i of block b of the pair, which is exactly the B-operand slot
+// (k = 8g + i) that P^T needs for block b, and V^T's A operand (dim row col,
+// k = tokens 8g .. 8g+7) is one 16-byte load of the value row.
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+
+#include "pkv_device.h"
+#include "pkv_internal.h"
+
+namespace pkv {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kD = 128, kBS = 16;
+constexpr int kTile = kBS * kD * 2;   // bytes of a bf16 (block, kv head) tile
+constexpr int kRows = 32;             // query rows per wave
+constexpr int kNW = 4;                // waves per workgroup
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// Workgroup wg (after the XCD remap) covers query block qb of (s, hkv):
+// rows [qb * kNW * 32, (qb + 1) * kNW * 32) of the C * G rows of that kv head.
+__global__ __launch_bounds__(kNW * 64) __attribute__((amdgpu_waves_per_eu(2)))
+void prefill_kernel(const PrefillArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int col = lane & 31, g = lane >> 5;
+
+  // Workgroup ids go round robin over the 8 XCDs; give each XCD a contiguous
+  // eighth of the work so the query blocks of one (sequence, kv head), which
+  // read the same blocks, share that XCD's L2.
+  const int per = (a.total_wg + 7) / 8;
+  const int wg = (blockIdx.x % 8) * per + blockIdx.x / 8;
+  if (wg >= a.total_wg) return;
+  const int qb = wg % a.qblocks;
+  const int sh = wg / a.qblocks;
+  const int hkv = sh % a.Hkv, s = sh / a.Hkv;
+  const int G = a.Hq / a.Hkv;
+  const int r0q = a.q_start[s];
+  const int C = a.q_start[s + 1] - r0q;
+  const int L = a.lens[s];
+  const int nrows = C * G;
+  const int row0 = (qb * kNW + w) * kRows;
+  if (row0 >= nrows) return;   // no rows for this wave (no barriers follow)
+  // a chunk longer than its context or a context beyond the table: NaN rows
+  bool bad = C > L || L > a.max_blocks * kBS || C < 0;
+
+  // ---- this lane's query row ----
+  const int row = row0 + col;
+  const bool row_ok = row < nrows;
+  const int pl = row_ok ? row / G : C - 1;       // chunk position (padding rows: the last)
+  const int qh = hkv * G + (row_ok ? row % G : 0);
+  const int p = L - C + pl;                       // tokens 0 .. p are visible to this row
+  const int last_row = min(nrows - 1, row0 + kRows - 1);
+  const int p_min = L - C + row0 / G;             // first row's position (wave-uniform)
+  const int p_max = L - C + last_row / G;         // last row's position (wave-uniform)
+  const int nblk = bad ? 0 : (p_max + kBS) / kBS; // blocks holding tokens 0 .. p_max
+  const int npairs = (nblk + 1) / 2;
+
+  u32x4 qv[8];
+  {
+    const uint16_t* qrow = (const uint16_t*)a.q + ((size_t)(r0q + pl) * a.Hq + qh) * kD;
+#pragma unroll
+    for (int sl = 0; sl < 8; ++sl)
+      qv[sl] = row_ok && !bad ? *(const u32x4*)(qrow + 16 * sl + 8 * g) : u32x4{0, 0, 0, 0};
+  }
+
+  const int32_t* __restrict__ tbl = a.tables + (size_t)s * a.max_blocks;
+  const size_t head_off = (size_t)hkv * kTile;
+  const size_t blk_stride = (size_t)a.Hkv * kTile;
+  // key row of A for this lane: token sigma(col) of block col / 16
+  const int kt = col & 15;
+  const int ktok = (kt & 3) | ((kt & 4) << 1) | ((kt & 8) >> 1);
+  const int kblk = col >> 4;
+
+  // block ids, 64 at a time in a VGPR (lane i holds entry base + i)
+  int tv = 0, tbase = -64;
+  auto block_id = [&](int j) -> int {   // j wave-uniform, j < nblk
+    if (j >= tbase + 64) {
+      tbase = j;
+      tv = tbase + lane < nblk ? tbl[tbase + lane] : 0;
+    }
+    int b = __builtin_amdgcn_readlane(tv, j - tbase);
+    if ((unsigned)b >= (unsigned)a.nb) {
+      bad = true;
+      b = 0;
+    }
+    return b;
+  };
+
+  u32x4 kr[8], vr[2][4];
+  auto load_pair = [&](int jp, bool keys, bool values) {
+    const int j0 = 2 * jp;
+    const bool two = j0 + 1 < nblk;
+    const size_t b0 = (size_t)block_id(j0) * blk_stride + head_off;
+    const size_t b1 = two ? (size_t)block_id(j0 + 1) * blk_stride + head_off : b0;
+    if (keys) {
+      const uint8_t* kp = (const uint8_t*)a.kc + (kblk ? b1 : b0) + (size_t)(g * kBS + ktok) * 16;
+#pragma unroll
+      for (int sl = 0; sl < 8; ++sl) kr[sl] = *(const u32x4*)(kp + (size_t)sl * 2 * kBS * 16);
+    }
+    if (values) {
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        const uint8_t* vp = (const uint8_t*)a.vc + (b ? b1 : b0) + (size_t)(col * kBS + 8 * g) * 2;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) vr[b][m] = *(const u32x4*)(vp + (size_t)m * 32 * kBS * 2);
+      }
+    }
+  };
+
+  float m_run = -INFINITY, l_run = 0.f;
+  f32x16 acc[4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[m][r] = 0.f;
+
+  if (npairs > 0) load_pair(0, true, true);
+  for (int jp = 0; jp < npairs; ++jp) {
+    const int t0 = 32 * jp;   // first token of the pair
+    // ---- S^T = K Q^T over the 8 dim slices ----
+    f32x16 sc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sc[r] = 0.f;
+#pragma unroll
+    for (int sl = 0; sl < 8; ++sl)
+      sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kr[sl]), as_bf16x8(qv[sl]), sc, 0, 0, 0);
+    if (jp + 1 < npairs) load_pair(jp + 1, true, false);
+
+    // ---- scores (log2 units); tokens after the row's position are hidden ----
+    // register 8b + i holds token t0 + 16b + 8g + i
+    const bool masked = t0 + 31 > p_min;
+    float z[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int tok = t0 + 16 * (r >> 3) + 8 * g + (r & 7);
+      const float v = sc[r] * a.qk_mult;
+      z[r] = (!masked || tok <= p) ? v : -INFINITY;
+    }
+    // A reference max that moves only when a score exceeds it by 2^8 (rare,
+    // wave-uniform rescale): every p stays <= 2^8, and O / l does not depend
+    // on the reference.
+    bool grow = false;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) grow |= z[r] > m_run + 8.0f;
+    if (__ballot(grow)) {
+      float tm = z[0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) tm = fmaxf(tm, z[r]);
+      tm = fmaxf(tm, __shfl_xor(tm, 32));   // the row's other 16 tokens
+      const bool up = tm > m_run + 8.0f;
+      const float c = up ? __builtin_amdgcn_exp2f(m_run - tm) : 1.0f;
+      m_run = up ? tm : m_run;
+      l_run *= c;
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[m][r] *= c;
+    }
+    // P^T as the B operand: bf16 of exp2(z - m), eight tokens per block
+    u32x4 pb[2];
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      uint32_t w4[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const uint32_t pk = pack_bf16x2(__builtin_amdgcn_exp2f(z[8 * b + 2 * k] - m_run),
+                                        __builtin_amdgcn_exp2f(z[8 * b + 2 * k + 1] - m_run));
+        l_run += bf16_lo(pk) + bf16_hi(pk);
+        w4[k] = pk;
+      }
+      pb[b] = u32x4{w4[0], w4[1], w4[2], w4[3]};
+    }
+
+    // ---- O^T += V^T P^T, block by block ----
+    // value rows of tokens past the wave's last position are zeroed: their
+    // probabilities are 0, but bytes past the context may hold anything
+    const bool tail = t0 + 31 > p_max;
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      if (tail) {
+        const int first = t0 + 16 * b + 8 * g;   // token of the lane's first value
+        const int keep = min(max(p_max + 1 - first, 0), 8);   // tokens kept, 0..8
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int k2 = keep - 2 * e;   // tokens kept in this dword
+            const uint32_t msk = k2 >= 2 ? 0xffffffffu : k2 == 1 ? 0x0000ffffu : 0u;
+            vr[b][m][e] &= msk;
+          }
+        }
+      }
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+        acc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vr[b][m]), as_bf16x8(pb[b]),
+                                                         acc[m], 0, 0, 0);
+    }
+    if (jp + 1 < npairs) load_pair(jp + 1, false, true);
+  }
+
+  // ---- out = O / l, rows of this lane: dims 32m + 8q + 4g + (0..3) ----
+  if (!row_ok) return;
+  const float lt = l_run + __shfl_xor(l_run, 32);
+  const float inv = 1.0f / lt;
+  uint16_t* orow = (uint16_t*)a.out + ((size_t)(r0q + pl) * a.Hq + qh) * kD;
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      float v[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = bad ? NAN : acc[m][4 * q + e] * inv;
+      *(uint2*)(orow + 32 * m + 8 * q + 4 * g) =
+          make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+    }
+  }
+}
+
+}  // namespace
+
+bool prefill_supported(pkv_dtype q, pkv_dtype kv, int D, int BS) {
+  return q == PKV_BF16 && kv == PKV_BF16 && D == kD && BS == kBS;
+}
+
+int prefill_query_blocks(int max_query_len, int G) {
+  const long long rows = (long long)max_query_len * G;
+  return (int)((rows + kNW * kRows - 1) / (kNW * kRows));
+}
+
+int launch_prefill(const PrefillArgs& a, void* stream) {
+  if (a.total_wg <= 0) return 0;
+  const int per = (a.total_wg + 7) / 8;
+  dim3 grid(8 * per), block(kNW * 64);
+  hipLaunchKernelGGL(prefill_kernel, grid, block, 0, (hipStream_t)stream, a);
+  return (int)hipGetLastError();
+}
+
+}  // namespace pkv

@@ -1,0 +1,170 @@
+"""Chunked prefill (causal attention of each sequence's last C positions over
+its paged cache, on matrix cores) against the fp64 oracle, through the C ABI.
+
+The cache holds every context token; unused pool bytes and the tail slots of
+each last block hold NaN, so a hidden or past-the-end value that reaches an
+accumulator shows up.  Outputs must be within the bf16 tolerance (2e-2 max
+abs) of the oracle.
+"""
+
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import attention as OA
+from oracle import replay
+from paged_kv_cache_211_amd import workload as H
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    import paged_kv_cache_211_amd  # noqa: F401  (fails loudly if libpkv.so is missing)
+
+
+def _case(name):
+    print(f"\n[case] {name}", flush=True)
+
+
+def _workload(G=4, key="small", **kw):
+    base = synth.PREFILL[key]
+    return synth.make(dataclasses.replace(base, H_q=base.H_kv * G, **kw))
+
+
+def gpu_prefill(cache, wl, chunks, q_bits, tables=None, lens=None):
+    from paged_kv_cache_211_amd import paged_attention_prefill
+    c = wl.cfg
+    inp = cache.decode_inputs(range(c.S), 0)
+    qs = np.concatenate([[0], np.cumsum(chunks)]).astype(np.int32)
+    q = H.to_dev(q_bits, c.q_dtype)
+    out = torch.full_like(q, float("nan"))
+    paged_attention_prefill(out, q, cache.key_cache, cache.value_cache,
+                            inp["block_tables"] if tables is None else tables,
+                            inp["context_lens"] if lens is None else lens,
+                            torch.from_numpy(qs).cuda(), int(np.max(chunks)), c.scale)
+    torch.cuda.synchronize()
+    return out.double().cpu().numpy(), qs, inp
+
+
+def oracle_prefill(wl, st, chunks, q_bits, seqs=None):
+    c = wl.cfg
+    qs = np.concatenate([[0], np.cumsum(chunks)])
+    return OA.paged_prefill(q_bits, c.q_dtype, st.kc, st.vc, st.tables(c.S), wl.context_lens, qs,
+                            bs=c.bs, cache_dtype=c.kv_dtype, scale=c.scale, seqs=seqs)
+
+
+def _chunk_sets(wl):
+    L = wl.context_lens
+    return {"drawn": synth.prefill_chunks(wl), "whole context": L.copy(),
+            "one row": np.ones_like(L), "ragged 1..33": np.minimum(L, 1 + (np.arange(len(L)) * 8))}
+
+
+@pytest.mark.parametrize("G", [4, 1, 8])
+def test_prefill_parity(G):
+    wl = _workload(G)
+    c = wl.cfg
+    st, _ = replay.build(wl)
+    cache, _ = H.build(wl, poison=True)
+    tol = H.TOL[c.kv_dtype]
+    for name, chunks in _chunk_sets(wl).items():
+        _case(f"prefill G={G} chunks {name} {chunks.tolist()}")
+        q_bits = synth.prefill_queries(wl, chunks)
+        ref = oracle_prefill(wl, st, chunks, q_bits)
+        got, _, _ = gpu_prefill(cache, wl, chunks, q_bits)
+        assert np.isfinite(got).all(), name
+        err = np.abs(got - ref).max()
+        print(f"  max abs err {err:.3e} (tol {tol})", flush=True)
+        assert err <= tol, (name, err)
+
+
+def test_prefill_one_row_chunks_match_decode():
+    """A chunk of one row is a decode step: same output as the decode kernel
+    for the same query rows, within the tolerance of each against the oracle."""
+    from paged_kv_cache_211_amd import paged_attention_decode
+    wl = _workload(4)
+    c = wl.cfg
+    _case("prefill one-row chunks vs decode")
+    cache, _ = H.build(wl, poison=True)
+    chunks = np.ones(c.S, dtype=np.int64)
+    q_bits = synth.prefill_queries(wl, chunks)
+    got, _, inp = gpu_prefill(cache, wl, chunks, q_bits)
+    q = H.to_dev(q_bits, c.q_dtype)
+    dec = torch.full_like(q, float("nan"))
+    paged_attention_decode(dec, q, cache.key_cache, cache.value_cache, inp["block_tables"],
+                           inp["context_lens"], c.scale)
+    torch.cuda.synchronize()
+    assert np.abs(got - dec.double().cpu().numpy()).max() <= 2 * H.TOL[c.kv_dtype]
+
+
+def test_prefill_bad_inputs_give_nan_rows():
+    wl = _workload(4)
+    c = wl.cfg
+    _case("prefill: out-of-range block id, chunk longer than its context")
+    st, _ = replay.build(wl)
+    cache, _ = H.build(wl, poison=True)
+    chunks = synth.prefill_chunks(wl)
+    q_bits = synth.prefill_queries(wl, chunks)
+    ref = oracle_prefill(wl, st, chunks, q_bits)
+    qs = np.concatenate([[0], np.cumsum(chunks)])
+    inp = cache.decode_inputs(range(c.S), 0)
+    # sequence 1's block 0 is read by every one of its rows
+    tab = inp["block_tables"].clone()
+    tab[1, 0] = wl.num_blocks + 3
+    got, _, _ = gpu_prefill(cache, wl, chunks, q_bits, tables=tab)
+    assert np.isnan(got[qs[1]:qs[2]]).all()
+    keep = np.r_[0:qs[1], qs[2]:qs[-1]]
+    assert np.abs(got[keep] - ref[keep]).max() <= H.TOL[c.kv_dtype]
+    # sequence 3's context made shorter than its chunk
+    lens = inp["context_lens"].clone()
+    lens[3] = int(chunks[3]) - 1
+    got, _, _ = gpu_prefill(cache, wl, chunks, q_bits, lens=lens)
+    assert np.isnan(got[qs[3]:qs[4]]).all()
+    keep = np.r_[0:qs[3], qs[4]:qs[-1]]
+    assert np.abs(got[keep] - ref[keep]).max() <= H.TOL[c.kv_dtype]
+
+
+def test_prefill_argument_checks():
+    from paged_kv_cache_211_amd import PkvError, paged_attention_prefill
+    wl = _workload(4)
+    c = wl.cfg
+    _case("prefill argument checks")
+    cache, _ = H.build(wl, poison=True)
+    inp = cache.decode_inputs(range(c.S), 0)
+    chunks = synth.prefill_chunks(wl)
+    qs = torch.from_numpy(np.concatenate([[0], np.cumsum(chunks)]).astype(np.int32)).cuda()
+    q = H.to_dev(synth.prefill_queries(wl, chunks), c.q_dtype)
+    out = torch.empty_like(q)
+    args = (out, q, cache.key_cache, cache.value_cache, inp["block_tables"], inp["context_lens"])
+    with pytest.raises(PkvError):   # query_start of the wrong length
+        paged_attention_prefill(*args, qs[:-1], int(chunks.max()), c.scale)
+    with pytest.raises(PkvError):   # fp32 query: not built
+        paged_attention_prefill(out.float(), q.float(), *args[2:], qs, int(chunks.max()), c.scale)
+    with pytest.raises(PkvError):   # non-finite scale
+        paged_attention_prefill(*args, qs, int(chunks.max()), float("inf"))
+
+
+def test_prefill_full_size_sampled():
+    """The chunked-prefill workload bench.py times (16 sequences, 512-row
+    chunks over 1k-8k contexts), in the same launch, on sampled sequences."""
+    wl = _workload(4, key="full")
+    c = wl.cfg
+    _case(f"prefill full size S={c.S}")
+    L = wl.context_lens
+    seqs = sorted({0, int(L.argmax()), int(L.argmin()), c.S - 1})
+    st, _ = replay.build(wl, only_seqs=seqs)
+    cache, _ = H.build(wl, poison=True)
+    chunks = synth.prefill_chunks(wl)
+    q_bits = synth.prefill_queries(wl, chunks)
+    got, qs, _ = gpu_prefill(cache, wl, chunks, q_bits)
+    assert np.isfinite(got).all()
+    ref = oracle_prefill(wl, st, chunks, q_bits, seqs=seqs)
+    rows = np.concatenate([np.arange(qs[s], qs[s + 1]) for s in seqs])
+    err = np.abs(got[rows] - ref[rows]).max()
+    print(f"  sampled seqs {seqs}: max abs err {err:.3e}", flush=True)
+    assert err <= H.TOL[c.kv_dtype]
