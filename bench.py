@@ -13,9 +13,16 @@ R copies of the pools ("layers", at least two and at least 2 GB of cache)
 are cycled so that each step reads its KV from HBM, not from the 256 MB
 Infinity Cache.
 
+--prefill times chunked prefill instead: one step stores every sequence's
+chunk of new key/value rows (paged_kv_write) and runs the causal attention
+of the chunk's query rows over the paged cache (paged_attention_prefill), on
+the chunked-prefill workload (16 sequences, 512-row chunks over 1k-8k
+contexts); its roofline is the bf16 matrix-core peak.
+
 Prints ONE JSON line on stdout; details go to stderr.
 
     python bench.py [--steps K] [--warmup W] [--config 3] [--gpus 1] [--mode fused]
+    python bench.py --prefill
 """
 
 from __future__ import annotations
@@ -35,6 +42,8 @@ if ROOT not in sys.path:
 
 METRIC = "paged-attn decode µs/step + effective KV GB/s as % of MI355X HBM peak"
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, vendor figure
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix cores, vendor figure
+PREFILL_METRIC = "chunked prefill µs/step (store chunk + causal attention) + matrix-core TFLOP/s"
 ELEM = {"f32": 4, "bf16": 2, "fp8": 1}
 # sources of the decode kernels: a counter file taken on other sources is stale
 SRC_FILES = ("decode.hip", "decode_valu.h", "decode_f32.hip", "decode_bf16.hip", "decode_fp8.hip",
@@ -62,6 +71,8 @@ def parse():
                    help="split-K partitions of --partition tokens, stream-K persistent waves, or "
                         "the shared-prefix decode (shared blocks read once per 32 query rows)")
     p.add_argument("--workers", type=int, default=0, help="stream-K waves (0 = resident count)")
+    p.add_argument("--prefill", action="store_true",
+                   help="time chunked prefill (store + causal attention) instead of decode")
     return p.parse_args()
 
 
@@ -156,6 +167,153 @@ def cpu_baseline(wl, token_budget):
             "cpu_model": cpu_model}
 
 
+def prefill_flops(c, lens, chunks):
+    """Algorithmic flops of the causal attention: chunk row i of sequence s
+    sees L_s - C_s + i + 1 tokens, 2 d flops each for QK^T and for PV, per
+    query head."""
+    vis = sum(int(C) * (int(L) - int(C)) + int(C) * (int(C) + 1) // 2 for L, C in zip(lens, chunks))
+    return 4 * c.d * c.H_q * vis
+
+
+def cpu_baseline_prefill(wl, chunks, q_bits, nseq):
+    """Time the oracle's prefill on `nseq` sequences, scaled by flops."""
+    import numpy as np
+
+    from oracle import attention as OA
+    from oracle.replay import OracleState
+
+    c = wl.cfg
+    sample = sorted(int(s) for s in np.random.default_rng([c.seed, 9]).permutation(c.S)[:nseq])
+    st = OracleState(wl, only_seqs=sample)
+    st.run(wl, wl.prefill)
+    st.run(wl, wl.decode)
+    qs = np.concatenate([[0], np.cumsum(chunks)])
+    t0 = time.perf_counter()
+    OA.paged_prefill(q_bits, c.q_dtype, st.kc, st.vc, st.tables(c.S), wl.context_lens, qs,
+                     bs=c.bs, cache_dtype=c.kv_dtype, scale=c.scale, seqs=sample)
+    dt = time.perf_counter() - t0
+    frac = (prefill_flops(c, wl.context_lens[sample], chunks[sample])
+            / prefill_flops(c, wl.context_lens, chunks))
+    return {"value": round(dt / frac * 1e6, 1), "unit": "us/step", "cores": _blas_threads(),
+            "kind": "oracle",
+            "sample": f"attention of {len(sample)} of {c.S} sequences ({100 * frac:.1f}% of the "
+                      f"flops), timed {dt:.2f} s, scaled by flops; the chunk store not timed",
+            "host_cpus": os.cpu_count(), "affinity_cpus": len(os.sched_getaffinity(0))}
+
+
+def _blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        info = threadpool_info()
+        return max((i.get("num_threads") or 1) for i in info) if info else 1
+    except Exception:
+        return int(os.environ.get("OMP_NUM_THREADS", "1"))
+
+
+def main_prefill(args):
+    import numpy as np
+    import torch
+
+    import synth
+    import paged_kv_cache_211_amd as pkv
+    from paged_kv_cache_211_amd import workload as W
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    wl = synth.make(synth.PREFILL["full"])
+    wl.cache_limit = 0
+    c = wl.cfg
+    chunks = synth.prefill_chunks(wl)
+    q_bits = synth.prefill_queries(wl, chunks)
+    flops = prefill_flops(c, wl.context_lens, chunks)
+    T, maxC = int(chunks.sum()), int(chunks.max())
+    log(f"[bench] prefill workload {c.key}: S={c.S} H_q={c.H_q} H_kv={c.H_kv} d={c.d} "
+        f"bs={c.bs} context {wl.total_tokens} tokens, {T} chunk rows, {flops / 1e9:.1f} GFLOP")
+    cache, _ = W.build(wl, poison=False, device=dev)
+    inp = cache.decode_inputs(range(c.S), 0)
+    tab, lens = inp["block_tables"], inp["context_lens"]
+    qs = torch.from_numpy(np.concatenate([[0], np.cumsum(chunks)]).astype(np.int32)).to(dev)
+    q = W.to_dev(q_bits, c.q_dtype, dev)
+    out = torch.empty_like(q)
+    # the chunk's key/value rows and their slots (positions L - C .. L - 1)
+    tab_h = tab.cpu().numpy()
+    ks, vs, slots = [], [], []
+    for s in range(c.S):
+        L, C = int(wl.context_lens[s]), int(chunks[s])
+        k, v = wl.values(("seq", s), L - C, C)
+        ks.append(k)
+        vs.append(v)
+        pos = np.arange(L - C, L)
+        slots.append(tab_h[s, pos // c.bs].astype(np.int64) * c.bs + pos % c.bs)
+    K = W.to_dev(np.concatenate(ks), c.src_dtype, dev)
+    V = W.to_dev(np.concatenate(vs), c.src_dtype, dev)
+    slot_dev = torch.from_numpy(np.concatenate(slots).astype(np.int32)).to(dev)
+    kv_bytes = wl.total_tokens * c.H_kv * c.d * 2 * ELEM[c.kv_dtype]
+    R = args.layers or max(2, math.ceil(2e9 / kv_bytes))
+    layers = [(cache.key_cache, cache.value_cache)]
+    for _ in range(R - 1):
+        layers.append((cache.key_cache.clone(), cache.value_cache.clone()))
+
+    def attend(i):
+        kc, vc = layers[i % R]
+        pkv.paged_attention_prefill(out, q, kc, vc, tab, lens, qs, maxC, c.scale)
+
+    def step(i):
+        kc, vc = layers[i % R]
+        pkv.paged_kv_write(K, V, kc, vc, slot_dev)
+        attend(i)
+
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    e0.record()
+    for i in range(args.steps):
+        step(i)
+    e1.record()
+    torch.cuda.synchronize()
+    us_step = e0.elapsed_time(e1) / args.steps * 1e3
+    # the roofline kernel alone, back to back on its stream
+    for i in range(args.warmup):
+        attend(i)
+    torch.cuda.synchronize()
+    e0.record()
+    for i in range(args.steps):
+        attend(i)
+    e1.record()
+    torch.cuda.synchronize()
+    kern_us = e0.elapsed_time(e1) / args.steps * 1e3
+    tflops = flops / (kern_us * 1e-6) / 1e12
+    log(f"[bench] prefill step {us_step:.1f} us; attention back to back {kern_us:.1f} us = "
+        f"{tflops:.0f} TFLOP/s ({100 * tflops / MFMA_BF16_PEAK_TFLOPS:.1f}% of "
+        f"{MFMA_BF16_PEAK_TFLOPS:.0f}); {R} pool layers")
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] timing the oracle on a bounded sample ...")
+        cpu = cpu_baseline_prefill(wl, chunks, q_bits, 2)
+        log(f"[bench] oracle: {cpu['value']} us/step est. ({cpu['sample']})")
+    line = {
+        "metric": PREFILL_METRIC, "value": round(us_step, 2), "unit": "us/step", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(us_step / 1e3, 5),
+        "higher_is_better": False, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{c.key}: {c.S} seqs, {c.H_q}/{c.H_kv} heads, head_dim {c.d}, "
+                               f"block_size {c.bs}, bf16 KV, chunks of {maxC} rows over contexts "
+                               f"of {int(wl.context_lens.min())}-{int(wl.context_lens.max())} "
+                               f"tokens (seed {c.seed}), {R} pool layers",
+                   "global_batch": c.S, "seq_len": int(wl.context_lens.max()),
+                   "chunk_rows": T, "parallelism": "single GPU"},
+        "kernel_us": {"prefill_attention_back_to_back": round(kern_us, 2)},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 1),
+                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "kernel": "prefill_kernel", "algorithmic_flops_per_launch": flops},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -164,6 +322,8 @@ def main():
               f"WORLD_SIZE {world}); paged decode shards by sequence or kv head with no "
               "exchange, so per-GPU throughput is the one-GPU figure.", file=sys.stderr)
         sys.exit(2)
+    if args.prefill:
+        return main_prefill(args)
 
     import numpy as np
     import torch

@@ -86,12 +86,20 @@ void prefill_kernel(const PrefillArgs a) {
   const int nblk = bad ? 0 : (p_max + kBS) / kBS; // blocks holding tokens 0 .. p_max
   const int npairs = (nblk + 1) / 2;
 
+  // Scores are used as exp2(s * qk - m) with qk = |scale| * log2(e) > 0: a
+  // negative scale flips the sign bits of q (exact in bf16), and a zero scale
+  // becomes a tiny positive one (every score ~0, as it should be) so that a
+  // hidden token's -inf stays -inf.
+  const float qk = fmaxf(fabsf(a.qk_mult), 1e-30f);
+  const uint32_t qflip = a.qk_mult < 0.f ? 0x80008000u : 0u;
   u32x4 qv[8];
   {
     const uint16_t* qrow = (const uint16_t*)a.q + ((size_t)(r0q + pl) * a.Hq + qh) * kD;
 #pragma unroll
-    for (int sl = 0; sl < 8; ++sl)
+    for (int sl = 0; sl < 8; ++sl) {
       qv[sl] = row_ok && !bad ? *(const u32x4*)(qrow + 16 * sl + 8 * g) : u32x4{0, 0, 0, 0};
+      qv[sl] ^= qflip;
+    }
   }
 
   const int32_t* __restrict__ tbl = a.tables + (size_t)s * a.max_blocks;
@@ -138,12 +146,16 @@ void prefill_kernel(const PrefillArgs a) {
     }
   };
 
+  // m_run: the row's reference max in log2 units (qk * score); l_run: this
+  // lane's part of the row sum (the other half of the row's tokens sits in
+  // lane ^ 32)
   float m_run = -INFINITY, l_run = 0.f;
   f32x16 acc[4];
 #pragma unroll
   for (int m = 0; m < 4; ++m)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[m][r] = 0.f;
+  const bf16x2 ones = __builtin_bit_cast(bf16x2, 0x3f803f80u);
 
   if (npairs > 0) load_pair(0, true, true);
   for (int jp = 0; jp < npairs; ++jp) {
@@ -157,26 +169,23 @@ void prefill_kernel(const PrefillArgs a) {
       sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kr[sl]), as_bf16x8(qv[sl]), sc, 0, 0, 0);
     if (jp + 1 < npairs) load_pair(jp + 1, true, false);
 
-    // ---- scores (log2 units); tokens after the row's position are hidden ----
+    // ---- tokens after the row's position are hidden (diagonal pairs only) ----
     // register 8b + i holds token t0 + 16b + 8g + i
-    const bool masked = t0 + 31 > p_min;
-    float z[16];
+    if (t0 + 31 > p_min) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int tok = t0 + 16 * (r >> 3) + 8 * g + (r & 7);
-      const float v = sc[r] * a.qk_mult;
-      z[r] = (!masked || tok <= p) ? v : -INFINITY;
+      for (int r = 0; r < 16; ++r) {
+        const int tok = t0 + 16 * (r >> 3) + 8 * g + (r & 7);
+        sc[r] = tok <= p ? sc[r] : -INFINITY;
+      }
     }
     // A reference max that moves only when a score exceeds it by 2^8 (rare,
     // wave-uniform rescale): every p stays <= 2^8, and O / l does not depend
     // on the reference.
-    bool grow = false;
+    float tm = fmaxf(__builtin_fmaxf(sc[0], sc[1]), sc[2]);
 #pragma unroll
-    for (int r = 0; r < 16; ++r) grow |= z[r] > m_run + 8.0f;
-    if (__ballot(grow)) {
-      float tm = z[0];
-#pragma unroll
-      for (int r = 1; r < 16; ++r) tm = fmaxf(tm, z[r]);
+    for (int r = 3; r < 15; r += 2) tm = fmaxf(fmaxf(tm, sc[r]), sc[r + 1]);
+    tm = fmaxf(tm, sc[15]) * qk;
+    if (__ballot(tm > m_run + 8.0f)) {
       tm = fmaxf(tm, __shfl_xor(tm, 32));   // the row's other 16 tokens
       const bool up = tm > m_run + 8.0f;
       const float c = up ? __builtin_amdgcn_exp2f(m_run - tm) : 1.0f;
@@ -187,17 +196,19 @@ void prefill_kernel(const PrefillArgs a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[m][r] *= c;
     }
-    // P^T as the B operand: bf16 of exp2(z - m), eight tokens per block
+    // P^T as the B operand: bf16 of exp2(qk s - m), eight tokens per block;
+    // the row sum adds the same bf16 values
     u32x4 pb[2];
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
       uint32_t w4[4];
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        const uint32_t pk = pack_bf16x2(__builtin_amdgcn_exp2f(z[8 * b + 2 * k] - m_run),
-                                        __builtin_amdgcn_exp2f(z[8 * b + 2 * k + 1] - m_run));
-        l_run += bf16_lo(pk) + bf16_hi(pk);
-        w4[k] = pk;
+        const f32x2 e = {__builtin_amdgcn_exp2f(__builtin_fmaf(sc[8 * b + 2 * k], qk, -m_run)),
+                         __builtin_amdgcn_exp2f(__builtin_fmaf(sc[8 * b + 2 * k + 1], qk, -m_run))};
+        const bf16x2 pk = __builtin_convertvector(e, bf16x2);
+        l_run = __builtin_amdgcn_fdot2_f32_bf16(pk, ones, l_run, false);
+        w4[k] = __builtin_bit_cast(uint32_t, pk);
       }
       pb[b] = u32x4{w4[0], w4[1], w4[2], w4[3]};
     }
@@ -205,27 +216,26 @@ void prefill_kernel(const PrefillArgs a) {
     // ---- O^T += V^T P^T, block by block ----
     // value rows of tokens past the wave's last position are zeroed: their
     // probabilities are 0, but bytes past the context may hold anything
-    const bool tail = t0 + 31 > p_max;
+    if (t0 + 31 > p_max) {
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      if (tail) {
+      for (int b = 0; b < 2; ++b) {
         const int first = t0 + 16 * b + 8 * g;   // token of the lane's first value
         const int keep = min(max(p_max + 1 - first, 0), 8);   // tokens kept, 0..8
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
+        for (int e = 0; e < 4; ++e) {
+          const int k2 = keep - 2 * e;   // tokens kept in this dword
+          const uint32_t msk = k2 >= 2 ? 0xffffffffu : k2 == 1 ? 0x0000ffffu : 0u;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int k2 = keep - 2 * e;   // tokens kept in this dword
-            const uint32_t msk = k2 >= 2 ? 0xffffffffu : k2 == 1 ? 0x0000ffffu : 0u;
-            vr[b][m][e] &= msk;
-          }
+          for (int m = 0; m < 4; ++m) vr[b][m][e] &= msk;
         }
       }
+    }
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
 #pragma unroll
       for (int m = 0; m < 4; ++m)
         acc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vr[b][m]), as_bf16x8(pb[b]),
                                                          acc[m], 0, 0, 0);
-    }
     if (jp + 1 < npairs) load_pair(jp + 1, false, true);
   }
 
