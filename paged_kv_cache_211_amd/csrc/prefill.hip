@@ -110,40 +110,47 @@ void prefill_kernel(const PrefillArgs a) {
   const int ktok = (kt & 3) | ((kt & 4) << 1) | ((kt & 8) >> 1);
   const int kblk = col >> 4;
 
-  // block ids, 64 at a time in a VGPR (lane i holds entry base + i)
-  int tv = 0, tbase = -64;
-  auto block_id = [&](int j) -> int {   // j wave-uniform, j < nblk
-    if (j >= tbase + 64) {
-      tbase = j;
-      tv = tbase + lane < nblk ? tbl[tbase + lane] : 0;
+  // Block ids, 64 at a time in a VGPR (lane i holds entry 64c + i of
+  // chunk c); pair jp reads blocks 2jp and 2jp + 1, so chunk c serves pairs
+  // 32c .. 32c + 31.  A pair's two tile offsets are resolved once, when its
+  // keys are loaded, and kept for its values.
+  int tv = 0;
+  auto pair_base = [&](int jp, size_t& b0, size_t& b1) {   // jp wave-uniform, jp < npairs
+    if ((jp & 31) == 0) {
+      const int e = 2 * jp + lane;
+      tv = e < nblk ? tbl[e] : 0;
     }
-    int b = __builtin_amdgcn_readlane(tv, j - tbase);
-    if ((unsigned)b >= (unsigned)a.nb) {
+    int id0 = __builtin_amdgcn_readlane(tv, (2 * jp) & 63);
+    int id1 = 2 * jp + 1 < nblk ? __builtin_amdgcn_readlane(tv, (2 * jp + 1) & 63) : id0;
+    if ((unsigned)id0 >= (unsigned)a.nb || (unsigned)id1 >= (unsigned)a.nb) {
       bad = true;
-      b = 0;
+      id0 = id1 = 0;
     }
-    return b;
+    b0 = (size_t)id0 * blk_stride + head_off;
+    b1 = (size_t)id1 * blk_stride + head_off;
   };
-
   u32x4 kr[8], vr[2][4];
-  auto load_pair = [&](int jp, bool keys, bool values) {
-    const int j0 = 2 * jp;
-    const bool two = j0 + 1 < nblk;
-    const size_t b0 = (size_t)block_id(j0) * blk_stride + head_off;
-    const size_t b1 = two ? (size_t)block_id(j0 + 1) * blk_stride + head_off : b0;
-    if (keys) {
-      const uint8_t* kp = (const uint8_t*)a.kc + (kblk ? b1 : b0) + (size_t)(g * kBS + ktok) * 16;
+  auto load_keys = [&](size_t b0, size_t b1) {
+    const uint8_t* kp = (const uint8_t*)a.kc + (kblk ? b1 : b0) + (size_t)(g * kBS + ktok) * 16;
 #pragma unroll
-      for (int sl = 0; sl < 8; ++sl) kr[sl] = *(const u32x4*)(kp + (size_t)sl * 2 * kBS * 16);
+    for (int sl = 0; sl < 8; ++sl) kr[sl] = *(const u32x4*)(kp + (size_t)sl * 2 * kBS * 16);
+  };
+  auto load_values = [&](size_t b0, size_t b1) {
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const uint8_t* vp = (const uint8_t*)a.vc + (b ? b1 : b0) + (size_t)(col * kBS + 8 * g) * 2;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) vr[b][m] = *(const u32x4*)(vp + (size_t)m * 32 * kBS * 2);
     }
-    if (values) {
+  };
+  auto qk_scores = [&]() {   // S^T = K Q^T over the 8 dim slices
+    f32x16 sc;
 #pragma unroll
-      for (int b = 0; b < 2; ++b) {
-        const uint8_t* vp = (const uint8_t*)a.vc + (b ? b1 : b0) + (size_t)(col * kBS + 8 * g) * 2;
+    for (int r = 0; r < 16; ++r) sc[r] = 0.f;
 #pragma unroll
-        for (int m = 0; m < 4; ++m) vr[b][m] = *(const u32x4*)(vp + (size_t)m * 32 * kBS * 2);
-      }
-    }
+    for (int sl = 0; sl < 8; ++sl)
+      sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kr[sl]), as_bf16x8(qv[sl]), sc, 0, 0, 0);
+    return sc;
   };
 
   // m_run: the row's reference max in log2 units (qk * score); l_run: this
@@ -157,17 +164,30 @@ void prefill_kernel(const PrefillArgs a) {
     for (int r = 0; r < 16; ++r) acc[m][r] = 0.f;
   const bf16x2 ones = __builtin_bit_cast(bf16x2, 0x3f803f80u);
 
-  if (npairs > 0) load_pair(0, true, true);
+  // Software pipeline: while pair jp's softmax runs on the vector ALUs, pair
+  // jp + 1's QK^T is already on the matrix cores and pair jp + 2's keys are
+  // in flight; pair jp + 1's values load behind pair jp's PV.
+  size_t cb0 = 0, cb1 = 0, nb0 = 0, nb1 = 0;   // tile offsets: current pair, next pair
+  f32x16 sc = {};
+  if (npairs > 0) {
+    pair_base(0, cb0, cb1);
+    load_keys(cb0, cb1);
+    load_values(cb0, cb1);
+    sc = qk_scores();
+    if (npairs > 1) {
+      pair_base(1, nb0, nb1);
+      load_keys(nb0, nb1);
+    }
+  }
   for (int jp = 0; jp < npairs; ++jp) {
     const int t0 = 32 * jp;   // first token of the pair
-    // ---- S^T = K Q^T over the 8 dim slices ----
-    f32x16 sc;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) sc[r] = 0.f;
-#pragma unroll
-    for (int sl = 0; sl < 8; ++sl)
-      sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kr[sl]), as_bf16x8(qv[sl]), sc, 0, 0, 0);
-    if (jp + 1 < npairs) load_pair(jp + 1, true, false);
+    f32x16 sn = {};
+    if (jp + 1 < npairs) sn = qk_scores();   // next pair's scores
+    size_t fb0 = 0, fb1 = 0;
+    if (jp + 2 < npairs) {
+      pair_base(jp + 2, fb0, fb1);
+      load_keys(fb0, fb1);
+    }
 
     // ---- tokens after the row's position are hidden (diagonal pairs only) ----
     // register 8b + i holds token t0 + 16b + 8g + i
@@ -236,7 +256,10 @@ void prefill_kernel(const PrefillArgs a) {
       for (int m = 0; m < 4; ++m)
         acc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vr[b][m]), as_bf16x8(pb[b]),
                                                          acc[m], 0, 0, 0);
-    if (jp + 1 < npairs) load_pair(jp + 1, false, true);
+    if (jp + 1 < npairs) load_values(nb0, nb1);
+    sc = sn;
+    nb0 = fb0;
+    nb1 = fb1;
   }
 
   // ---- out = O / l, rows of this lane: dims 32m + 8q + 4g + (0..3) ----
