@@ -47,6 +47,13 @@ constexpr int kNW = 4;                // waves per workgroup
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
+// Read-only int32 arrays (lengths, row offsets, block tables) through the
+// constant address space: they do not change during the launch, so
+// wave-uniform reads become scalar loads and everything derived from them
+// (the wave's block range, the table address) stays in scalar registers.
+typedef const int32_t __attribute__((address_space(4))) * cint_ptr;
+__device__ __forceinline__ cint_ptr as_const(const int32_t* p) { return (cint_ptr)p; }
+
 // Workgroup wg (after the XCD remap) covers query block qb of (s, hkv):
 // rows [qb * kNW * 32, (qb + 1) * kNW * 32) of the C * G rows of that kv head.
 __global__ __launch_bounds__(kNW * 64) __attribute__((amdgpu_waves_per_eu(2)))
@@ -65,9 +72,9 @@ void prefill_kernel(const PrefillArgs a) {
   const int sh = wg / a.qblocks;
   const int hkv = sh % a.Hkv, s = sh / a.Hkv;
   const int G = a.Hq / a.Hkv;
-  const int r0q = a.q_start[s];
-  const int C = a.q_start[s + 1] - r0q;
-  const int L = a.lens[s];
+  const int r0q = as_const(a.q_start)[s];
+  const int C = as_const(a.q_start)[s + 1] - r0q;
+  const int L = as_const(a.lens)[s];
   const int nrows = C * G;
   const int row0 = (qb * kNW + w) * kRows;
   if (row0 >= nrows) return;   // no rows for this wave (no barriers follow)
@@ -81,8 +88,10 @@ void prefill_kernel(const PrefillArgs a) {
   const int qh = hkv * G + (row_ok ? row % G : 0);
   const int p = L - C + pl;                       // tokens 0 .. p are visible to this row
   const int last_row = min(nrows - 1, row0 + kRows - 1);
-  const int p_min = L - C + row0 / G;             // first row's position (wave-uniform)
-  const int p_max = L - C + last_row / G;         // last row's position (wave-uniform)
+  // first and last row's positions; wave-uniform (the divisions expand on
+  // the vector ALUs, so their results are moved back to scalar registers)
+  const int p_min = __builtin_amdgcn_readfirstlane(L - C + row0 / G);
+  const int p_max = __builtin_amdgcn_readfirstlane(L - C + last_row / G);
   const int nblk = bad ? 0 : (p_max + kBS) / kBS; // blocks holding tokens 0 .. p_max
   const int npairs = (nblk + 1) / 2;
 
@@ -102,7 +111,8 @@ void prefill_kernel(const PrefillArgs a) {
     }
   }
 
-  const int32_t* __restrict__ tbl = a.tables + (size_t)s * a.max_blocks;
+  // scalar table reads stay off the vector load counter the tile loads wait on
+  const cint_ptr tbl = as_const(a.tables + (size_t)s * a.max_blocks);
   const size_t head_off = (size_t)hkv * kTile;
   const size_t blk_stride = (size_t)a.Hkv * kTile;
   // key row of A for this lane: token sigma(col) of block col / 16
@@ -110,22 +120,19 @@ void prefill_kernel(const PrefillArgs a) {
   const int ktok = (kt & 3) | ((kt & 4) << 1) | ((kt & 8) >> 1);
   const int kblk = col >> 4;
 
-  // Block ids, 64 at a time in a VGPR (lane i holds entry 64c + i of
-  // chunk c); pair jp reads blocks 2jp and 2jp + 1, so chunk c serves pairs
-  // 32c .. 32c + 31.  A pair's two tile offsets are resolved once, when its
-  // keys are loaded, and kept for its values.
-  int tv = 0;
+  // A pair's two tile offsets: block ids 2jp and 2jp + 1 (the second past
+  // the wave's blocks repeats the first; its tokens are hidden), read with
+  // wave-uniform addresses (scalar loads), resolved once when the pair's keys
+  // load and kept for its values.
   auto pair_base = [&](int jp, size_t& b0, size_t& b1) {   // jp wave-uniform, jp < npairs
-    if ((jp & 31) == 0) {
-      const int e = 2 * jp + lane;
-      tv = e < nblk ? tbl[e] : 0;
-    }
-    int id0 = __builtin_amdgcn_readlane(tv, (2 * jp) & 63);
-    int id1 = 2 * jp + 1 < nblk ? __builtin_amdgcn_readlane(tv, (2 * jp + 1) & 63) : id0;
+    const int j0 = 2 * jp;
+    int id0 = tbl[j0];
+    int id1 = tbl[min(j0 + 1, nblk - 1)];
     if ((unsigned)id0 >= (unsigned)a.nb || (unsigned)id1 >= (unsigned)a.nb) {
       bad = true;
       id0 = id1 = 0;
     }
+    if (j0 + 1 >= nblk) id1 = id0;
     b0 = (size_t)id0 * blk_stride + head_off;
     b1 = (size_t)id1 * blk_stride + head_off;
   };
@@ -166,28 +173,29 @@ void prefill_kernel(const PrefillArgs a) {
 
   // Software pipeline: while pair jp's softmax runs on the vector ALUs, pair
   // jp + 1's QK^T is already on the matrix cores and pair jp + 2's keys are
-  // in flight; pair jp + 1's values load behind pair jp's PV.
+  // in flight; pair jp + 1's values load behind pair jp's PV.  Every
+  // iteration issues the same loads (pairs past the last repeat the last
+  // one, their results unused), so the compiler's load counters are exact
+  // and no wait covers a later pair's loads.
+  const int plast = npairs - 1;
   size_t cb0 = 0, cb1 = 0, nb0 = 0, nb1 = 0;   // tile offsets: current pair, next pair
   f32x16 sc = {};
   if (npairs > 0) {
+    // same load order as every iteration: the next pair's keys, then this
+    // pair's values (so the counters at the loop head agree on every path)
     pair_base(0, cb0, cb1);
     load_keys(cb0, cb1);
-    load_values(cb0, cb1);
     sc = qk_scores();
-    if (npairs > 1) {
-      pair_base(1, nb0, nb1);
-      load_keys(nb0, nb1);
-    }
+    pair_base(min(1, plast), nb0, nb1);
+    load_keys(nb0, nb1);
+    load_values(cb0, cb1);
   }
   for (int jp = 0; jp < npairs; ++jp) {
     const int t0 = 32 * jp;   // first token of the pair
-    f32x16 sn = {};
-    if (jp + 1 < npairs) sn = qk_scores();   // next pair's scores
-    size_t fb0 = 0, fb1 = 0;
-    if (jp + 2 < npairs) {
-      pair_base(jp + 2, fb0, fb1);
-      load_keys(fb0, fb1);
-    }
+    const f32x16 sn = qk_scores();   // next pair's scores
+    size_t fb0, fb1;
+    pair_base(min(jp + 2, plast), fb0, fb1);
+    load_keys(fb0, fb1);
 
     // ---- tokens after the row's position are hidden (diagonal pairs only) ----
     // register 8b + i holds token t0 + 16b + 8g + i
@@ -256,7 +264,7 @@ void prefill_kernel(const PrefillArgs a) {
       for (int m = 0; m < 4; ++m)
         acc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vr[b][m]), as_bf16x8(pb[b]),
                                                          acc[m], 0, 0, 0);
-    if (jp + 1 < npairs) load_values(nb0, nb1);
+    load_values(nb0, nb1);
     sc = sn;
     nb0 = fb0;
     nb1 = fb1;
