@@ -28,6 +28,27 @@ pages are silent on it):
   * ``free_seq`` drops one reference per table entry, in table order;
   * a call that fails leaves the state exactly as it was.
 
+Swapping to host memory ("PagedAttention Kernel：大模型推理优化的显存管理革新"
+§4.1 compares page replacement policies, but its table of them is missing
+from the page, so the policy here is a reading, parity unpinned as a choice
+of policy; only its stated rules below are pinned):
+  * a host pool of ``num_host_blocks`` slots with its own FIFO free list
+    (initially 0, 1, ..., popped from the front, returned to the back);
+  * ``swap_out(seq)``: every block of the sequence must be unshared
+    (refcount 1; shared blocks stay resident); table entry by entry, pop a
+    host slot, record the pair (device block, host slot), drop the device
+    block's reference (it returns to the device free list) and put the host
+    slot in the table; the sequence is then swapped out;
+  * ``swap_in(seq)``: table entry by entry, pop a device block, record the
+    pair (host slot, device block), return the host slot to the host free
+    list and put the device block in the table;
+  * a swapped-out sequence can only be swapped in or freed (freeing returns
+    its host slots in table order); other calls on it are invalid;
+  * least recently used: a logical clock ticks on add, fork (the child),
+    append, swap_in and touch, stamping that sequence; ``lru()`` names the
+    resident sequence with at least one block, all of them unshared, whose
+    stamp is oldest.
+
 Pins (tests/test_oracle_alloc.py): the invariants the pages state (only the
 last block of a sequence may be partly filled; block count = ceil(len/bs);
 at most bs-1 unused slots per sequence; a refcount equals the number of
@@ -65,6 +86,11 @@ class AllocModel:
         self.ref = [0] * num_blocks
         self.tables: dict[int, list[int]] = {}
         self.lens: dict[int, int] = {}
+        self.host_free: deque = deque()
+        self.num_host = 0
+        self.swapped: set[int] = set()
+        self.stamp: dict[int, int] = {}
+        self.clock = 0
 
     # -- helpers ---------------------------------------------------------
     def _state(self):
@@ -73,6 +99,16 @@ class AllocModel:
 
     def _restore(self, st):
         self.free, self.ref, self.tables, self.lens = st
+
+    def _tick(self, seq: int):
+        self.clock += 1
+        self.stamp[seq] = self.clock
+
+    def _resident(self, seq: int):
+        if seq not in self.tables:
+            raise AllocError(ERR_SEQ, f"unknown sequence {seq}")
+        if seq in self.swapped:
+            raise AllocError(ERR_INVALID, f"sequence {seq} is swapped out")
 
     def _pop(self) -> int:
         if not self.free:
@@ -92,21 +128,23 @@ class AllocModel:
             raise AllocError(ERR_SEQ, f"sequence {seq} exists")
         self.tables[seq] = []
         self.lens[seq] = 0
+        self._tick(seq)
 
     def fork(self, parent: int, child: int):
         if parent not in self.tables:
             raise AllocError(ERR_SEQ, f"unknown parent {parent}")
         if child in self.tables:
             raise AllocError(ERR_SEQ, f"sequence {child} exists")
+        self._resident(parent)
         self.tables[child] = list(self.tables[parent])
         self.lens[child] = self.lens[parent]
         for b in self.tables[child]:
             self.ref[b] += 1
+        self._tick(child)
 
     def append(self, seq: int, n: int):
         """Append n tokens; returns (slots [n], cow pairs [(src, dst), ...])."""
-        if seq not in self.tables:
-            raise AllocError(ERR_SEQ, f"unknown sequence {seq}")
+        self._resident(seq)
         if n < 0:
             raise AllocError(ERR_INVALID, "negative token count")
         st = self._state()
@@ -128,14 +166,77 @@ class AllocModel:
         except AllocError:
             self._restore(st)
             raise
+        self._tick(seq)
         return slots, cows
 
     def free_seq(self, seq: int):
         if seq not in self.tables:
             raise AllocError(ERR_SEQ, f"unknown sequence {seq}")
-        for b in self.tables.pop(seq):
-            self._drop(b)
+        tab = self.tables.pop(seq)
+        if seq in self.swapped:
+            self.swapped.discard(seq)
+            self.host_free.extend(tab)
+        else:
+            for b in tab:
+                self._drop(b)
         del self.lens[seq]
+        del self.stamp[seq]
+
+    def set_host_pool(self, num_host_blocks: int):
+        if num_host_blocks < 0:
+            raise AllocError(ERR_INVALID, "negative host pool size")
+        if self.swapped:
+            raise AllocError(ERR_INVALID, "sequences are swapped out")
+        self.num_host = num_host_blocks
+        self.host_free = deque(range(num_host_blocks))
+
+    def swap_out(self, seq: int):
+        """Move seq's blocks to host slots; returns [(device block, host slot), ...]."""
+        self._resident(seq)
+        tab = self.tables[seq]
+        if any(self.ref[b] != 1 for b in tab):
+            raise AllocError(ERR_INVALID, f"sequence {seq} holds shared blocks")
+        if len(tab) > len(self.host_free):
+            raise AllocError(ERR_NO_BLOCKS, "not enough free host slots")
+        pairs = []
+        for i, b in enumerate(tab):
+            h = self.host_free.popleft()
+            pairs.append((b, h))
+            self._drop(b)
+            tab[i] = h
+        self.swapped.add(seq)
+        return pairs
+
+    def swap_in(self, seq: int):
+        """Bring seq's blocks back; returns [(host slot, device block), ...]."""
+        if seq not in self.tables:
+            raise AllocError(ERR_SEQ, f"unknown sequence {seq}")
+        if seq not in self.swapped:
+            raise AllocError(ERR_INVALID, f"sequence {seq} is resident")
+        tab = self.tables[seq]
+        if len(tab) > len(self.free):
+            raise AllocError(ERR_NO_BLOCKS, "not enough free device blocks")
+        pairs = []
+        for i, h in enumerate(tab):
+            b = self._pop()
+            pairs.append((h, b))
+            self.host_free.append(h)
+            tab[i] = b
+        self.swapped.discard(seq)
+        self._tick(seq)
+        return pairs
+
+    def touch(self, seq: int):
+        if seq not in self.tables:
+            raise AllocError(ERR_SEQ, f"unknown sequence {seq}")
+        self._tick(seq)
+
+    def lru(self) -> int:
+        cands = [s for s, t in self.tables.items()
+                 if s not in self.swapped and t and all(self.ref[b] == 1 for b in t)]
+        if not cands:
+            raise AllocError(ERR_SEQ, "no sequence can be swapped out")
+        return min(cands, key=lambda s: self.stamp[s])
 
     # -- queries ---------------------------------------------------------
     def table(self, seq: int) -> list[int]:
@@ -153,6 +254,14 @@ class AllocModel:
 
     def num_free(self) -> int:
         return len(self.free)
+
+    def num_host_free(self) -> int:
+        return len(self.host_free)
+
+    def is_swapped(self, seq: int) -> bool:
+        if seq not in self.tables:
+            raise AllocError(ERR_SEQ, f"unknown sequence {seq}")
+        return seq in self.swapped
 
     def free_list(self) -> list[int]:
         return list(self.free)

@@ -114,3 +114,11 @@ def copy_blocks(kc, vc, pairs):
     for src, dst in pairs:
         kc[dst] = kc[src]
         vc[dst] = vc[src]
+
+
+def move_blocks(dst_kc, dst_vc, src_kc, src_vc, pairs):
+    """Copy whole key and value blocks between two pools of the same layout
+    (a device pool and a host pool): dst[d] = src[s] for each pair (s, d)."""
+    for src, dst in pairs:
+        dst_kc[dst] = src_kc[src]
+        dst_vc[dst] = src_vc[src]

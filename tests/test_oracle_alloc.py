@@ -154,3 +154,113 @@ def test_full_shared_block_is_not_copied():
     slots, cows = m.append(1, 1)    # next token opens a new block, no copy
     assert cows == [] and slots == [2 * 4]
     assert m.refcount(0) == 2 and m.refcount(1) == 2
+
+
+def test_swap_hand_traced_example():
+    """Traced by hand from the rules: FIFO device and host free lists,
+    swap pairs in table order, LRU by the last add/fork/append/swap_in/touch."""
+    m = AllocModel(4, 2, [2, 0, 3, 1])
+    m.set_host_pool(3)
+    m.add_seq(0)
+    assert m.append(0, 3) == ([4, 5, 0], [])
+    m.add_seq(1)
+    assert m.append(1, 1) == ([6], [])
+    assert m.lru() == 0
+    assert m.swap_out(0) == [(2, 0), (0, 1)]
+    assert m.free_list() == [1, 2, 0] and list(m.host_free) == [2]
+    assert m.table(0) == [0, 1] and m.is_swapped(0) and m.length(0) == 3
+    with pytest.raises(AllocError) as e:
+        m.append(0, 1)                       # swapped out: invalid
+    assert e.value.code == ERR_INVALID
+    assert m.append(1, 2) == ([7, 2], [])
+    with pytest.raises(AllocError) as e:
+        m.swap_out(1)                        # 2 blocks, 1 host slot
+    assert e.value.code == ERR_NO_BLOCKS
+    assert m.table(1) == [3, 1] and list(m.host_free) == [2]
+    assert m.swap_in(0) == [(0, 2), (1, 0)]
+    assert m.table(0) == [2, 0] and m.free_list() == [] and list(m.host_free) == [2, 0, 1]
+    assert m.lru() == 1
+    m.touch(1)
+    assert m.lru() == 0
+    m.free_seq(0)
+    assert m.free_list() == [2, 0] and m.table(1) == [3, 1]
+
+
+def test_swap_rules_on_random_ops():
+    """Random ops with swaps: every device block is held by resident tables
+    only, host slots by swapped tables only, lengths survive swaps, and the
+    contents that the emitted pairs move come back to the same sequence."""
+    rng = np.random.default_rng(31)
+    for trial in range(80):
+        nb, nh = int(rng.integers(2, 16)), int(rng.integers(0, 12))
+        bs = int(rng.choice([1, 2, 4]))
+        m = AllocModel(nb, bs, rng.permutation(nb))
+        m.set_host_pool(nh)
+        dev = [None] * nb                   # content label of each device block
+        host = [None] * nh
+        label = {}                          # (seq, logical block) -> label it must hold
+        live, nxt, order = [], 0, []        # order: test's own recency list
+        for step in range(60):
+            r = rng.random()
+            try:
+                if r < 0.15 or not live:
+                    m.add_seq(nxt); live.append(nxt); order.append(nxt); nxt += 1
+                elif r < 0.25:
+                    p = int(rng.choice(live))
+                    m.fork(p, nxt)
+                    for j in range(len(m.table(nxt))):
+                        label[(nxt, j)] = label[(p, j)]
+                    live.append(nxt); order.append(nxt); nxt += 1
+                elif r < 0.55:
+                    s = int(rng.choice(live))
+                    before = len(m.table(s)) if not m.is_swapped(s) else None
+                    slots, cows = m.append(s, int(rng.integers(1, 3 * bs + 1)))
+                    for src, dst in cows:
+                        dev[dst] = dev[src]
+                    for j, b in enumerate(m.table(s)):
+                        if j >= before:
+                            dev[b] = label[(s, j)] = (trial, step, s, j)
+                    order.remove(s); order.append(s)
+                elif r < 0.7:
+                    s = int(rng.choice(live))
+                    for b, h in m.swap_out(s):
+                        host[h] = dev[b]
+                elif r < 0.85:
+                    s = int(rng.choice(live))
+                    for h, b in m.swap_in(s):
+                        dev[b] = host[h]
+                    order.remove(s); order.append(s)
+                elif r < 0.9:
+                    s = int(rng.choice(live))
+                    m.touch(s); order.remove(s); order.append(s)
+                else:
+                    s = int(rng.choice(live))
+                    m.free_seq(s); live.remove(s); order.remove(s)
+                    for k in [k for k in label if k[0] == s]:
+                        del label[k]
+            except AllocError:
+                pass
+            # invariants
+            holders = [0] * nb
+            hosts = []
+            for s, tab in m.tables.items():
+                assert len(tab) == -(-m.length(s) // bs)
+                if m.is_swapped(s):
+                    hosts += tab
+                    for j, h in enumerate(tab):
+                        assert host[h] == label[(s, j)]
+                else:
+                    for j, b in enumerate(tab):
+                        holders[b] += 1
+                        assert dev[b] == label[(s, j)]
+            assert holders == [m.refcount(b) for b in range(nb)]
+            assert sorted(m.free_list()) == [b for b in range(nb) if holders[b] == 0]
+            assert sorted(hosts + list(m.host_free)) == list(range(nh))
+            # LRU: the oldest eligible sequence in the test's own recency order
+            elig = [s for s in order if not m.is_swapped(s) and m.table(s)
+                    and all(m.refcount(b) == 1 for b in m.table(s))]
+            if elig:
+                assert m.lru() == elig[0]
+            else:
+                with pytest.raises(AllocError):
+                    m.lru()
