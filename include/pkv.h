@@ -393,6 +393,28 @@ int paged_attention_splitk_reduce(void* out, const void* workspace, size_t works
 int paged_kv_copy_blocks(void* key_cache, void* value_cache, const int32_t* pairs, int num_pairs,
                          size_t block_bytes, int num_blocks, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * paged_kv_swap_blocks -- move whole blocks between two pools of the same
+ * layout, for swapping a sequence to host memory and back (the pairs come
+ * from pkv_alloc_swap_out / pkv_alloc_swap_in).  For each pair (s, d):
+ * dst_key_cache block d = src_key_cache block s, same for values.
+ *  pools          block-major pools, block_bytes per block per pool; each
+ *                 either a device pool or a pinned host pool passed as the
+ *                 device pointer pkv_host_device_pointer returned for it
+ *  pairs          [num_pairs][2] int32 (device): (src block, dst block);
+ *                 ids outside [0, src_blocks) / [0, dst_blocks) skip the pair
+ *  Two destinations of one call must differ (else they race).  One launch
+ *  on `stream`; reads from a host pool cross the host link.
+ * ------------------------------------------------------------------------- */
+int paged_kv_swap_blocks(void* dst_key_cache, void* dst_value_cache, const void* src_key_cache,
+                         const void* src_value_cache, const int32_t* pairs, int num_pairs,
+                         size_t block_bytes, int src_blocks, int dst_blocks, void* stream);
+
+/* Device pointer of pinned host memory (hipHostGetDevicePointer); fails with
+ * PKV_ERR_HIP for memory that is not pinned.  Host memory is only ever
+ * handed to a kernel through this pointer. */
+int pkv_host_device_pointer(const void* host, void** device_out);
+
 /* paged_kv_gather -- read every sequence back through its block table into
  * dense rows: k_out, v_out [cu_ctx[num_seqs]][num_kv_heads][head_dim] of
  * cache_dtype bits, sequence s occupying rows cu_ctx[s] .. cu_ctx[s+1]-1
@@ -431,6 +453,25 @@ int pkv_hbm_read_probe(const void* buffer, size_t bytes, void* sink, int workgro
  *     reference to old and replace it in the table; the token takes slot
  *     table[pos / bs] * bs + pos % bs;
  *   - free_seq: drop one reference per table entry, in table order.
+ *  Swapping to host memory ("PagedAttention Kernel：大模型推理优化的显存管理革
+ *  新" §4.1 weighs page replacement policies; its table of them is missing,
+ *  so least-recently-used is a reading):
+ *   - a host pool of num_host_blocks slots with its own FIFO free list
+ *     (initially 0, 1, ...);
+ *   - swap_out(seq): every block must be unshared (refcount 1), else
+ *     PKV_ERR_INVALID; table entry by entry, pop a host slot, emit the pair
+ *     (device block, host slot), drop the block's reference and put the
+ *     slot in the table;
+ *   - swap_in(seq): table entry by entry, pop a device block, emit the pair
+ *     (host slot, device block), return the slot to the back of the host
+ *     free list and put the block in the table;
+ *   - a swapped-out sequence may only be swapped in or freed (its slots go
+ *     back in table order); append, fork from it and fill_tables give
+ *     PKV_ERR_INVALID; block_table returns its host slots;
+ *   - a clock ticks on add, fork (the child), append, swap_in and touch,
+ *     stamping that sequence; lru names the resident sequence with at least
+ *     one block, all unshared, whose stamp is oldest (PKV_ERR_SEQ if none).
+ *  The pairs drive paged_kv_swap_blocks, which moves the data.
  * ------------------------------------------------------------------------- */
 typedef struct pkv_alloc pkv_alloc;
 
@@ -459,6 +500,23 @@ int pkv_alloc_refcount(const pkv_alloc* a, int32_t block);
 int pkv_alloc_num_free(const pkv_alloc* a);
 /* Copies the free list, front first, into out (capacity cap); returns count. */
 int pkv_alloc_free_list(const pkv_alloc* a, int32_t* out, int cap);
+/* Sets the host pool to num_host_blocks slots (free list 0, 1, ...); fails
+ * while any sequence is swapped out. */
+int pkv_alloc_set_host_pool(pkv_alloc* a, int num_host_blocks);
+/* pairs_out: host int32 [2*cap], (device block, host slot) per table entry;
+ * *n_out = pairs written (the table length).  cap below the table length is
+ * PKV_ERR_INVALID; too few host slots PKV_ERR_NO_BLOCKS. */
+int pkv_alloc_swap_out(pkv_alloc* a, int64_t seq, int32_t* pairs_out, int cap, int* n_out);
+/* pairs_out: (host slot, device block) per table entry; too few free device
+ * blocks is PKV_ERR_NO_BLOCKS. */
+int pkv_alloc_swap_in(pkv_alloc* a, int64_t seq, int32_t* pairs_out, int cap, int* n_out);
+/* Marks seq as used now. */
+int pkv_alloc_touch(pkv_alloc* a, int64_t seq);
+/* *seq_out = the least recently used sequence that can be swapped out. */
+int pkv_alloc_lru(const pkv_alloc* a, int64_t* seq_out);
+/* 1 if seq is swapped out, 0 if resident, or a negative error. */
+int pkv_alloc_is_swapped(const pkv_alloc* a, int64_t seq);
+int pkv_alloc_num_host_free(const pkv_alloc* a);
 
 #ifdef __cplusplus
 }

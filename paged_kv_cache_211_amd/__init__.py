@@ -74,12 +74,16 @@ def _pool_shape(key_cache: torch.Tensor, value_cache: torch.Tensor):
 
 
 def empty_pools(num_blocks: int, num_kv_heads: int, head_dim: int, block_size: int,
-                dtype: torch.dtype, device="cuda"):
-    """Allocate (uninitialised) key and value pools in the library's layout."""
+                dtype: torch.dtype, device="cuda", pin: bool = False):
+    """Allocate (uninitialised) key and value pools in the library's layout;
+    pin=True gives pinned host pools (device must be "cpu")."""
     es = torch.empty((), dtype=dtype).element_size()
     x = 16 // es
-    kc = torch.empty((num_blocks, num_kv_heads, head_dim // x, block_size, x), dtype=dtype, device=device)
-    vc = torch.empty((num_blocks, num_kv_heads, head_dim, block_size), dtype=dtype, device=device)
+    kw = {"pin_memory": True} if pin else {}
+    kc = torch.empty((num_blocks, num_kv_heads, head_dim // x, block_size, x), dtype=dtype,
+                     device=device, **kw)
+    vc = torch.empty((num_blocks, num_kv_heads, head_dim, block_size), dtype=dtype, device=device,
+                     **kw)
     return kc, vc
 
 
@@ -386,6 +390,39 @@ def paged_kv_copy_blocks(key_cache, value_cache, pairs, stream=None):
                                      block_bytes, nb, _stream(stream)))
 
 
+def host_device_pointer(t: torch.Tensor) -> int:
+    """Device pointer of a pinned host tensor (the library refuses memory
+    that is not pinned)."""
+    if t.is_cuda or not t.is_pinned():
+        raise PkvError(-1, "expected a pinned host tensor")
+    out = ctypes.c_void_p()
+    check(lib().pkv_host_device_pointer(ctypes.c_void_p(t.data_ptr()), ctypes.byref(out)))
+    return int(out.value)
+
+
+def _pool_ptr(t: torch.Tensor, name: str):
+    if not t.is_contiguous():
+        raise PkvError(-1, f"{name} must be contiguous")
+    if t.is_cuda:
+        return ctypes.c_void_p(t.data_ptr())
+    return ctypes.c_void_p(host_device_pointer(t))
+
+
+def paged_kv_swap_blocks(dst_key, dst_value, src_key, src_value, pairs, stream=None):
+    """Copy whole blocks src block p[0] -> dst block p[1] for each pair,
+    between a device pool and a pinned host pool of the same layout."""
+    nbs, H, D, bs = _pool_shape(src_key, src_value)
+    nbd, Hd, Dd, bsd = _pool_shape(dst_key, dst_value)
+    if (H, D, bs) != (Hd, Dd, bsd) or src_key.dtype != dst_key.dtype:
+        raise PkvError(-1, "source and destination pools differ in layout")
+    _need(pairs, "pairs", torch.int32)
+    block_bytes = H * bs * D * src_key.element_size()
+    check(lib().paged_kv_swap_blocks(
+        _pool_ptr(dst_key, "dst_key"), _pool_ptr(dst_value, "dst_value"),
+        _pool_ptr(src_key, "src_key"), _pool_ptr(src_value, "src_value"), _ptr(pairs),
+        pairs.numel() // 2, block_bytes, nbs, nbd, _stream(stream)))
+
+
 def paged_kv_gather(k_out, v_out, key_cache, value_cache, block_tables, cu_ctx, total_tokens,
                     stream=None):
     nb, H, D, bs = _pool_shape(key_cache, value_cache)
@@ -486,6 +523,38 @@ class BlockAllocator:
         out = np.zeros(self.num_blocks, dtype=np.int32)
         n = lib().pkv_alloc_free_list(self._h, out.ctypes.data_as(_native.pi32), self.num_blocks)
         return [int(b) for b in out[:check_nonneg(n)]]
+
+    def set_host_pool(self, num_host_blocks: int):
+        check(lib().pkv_alloc_set_host_pool(self._h, int(num_host_blocks)))
+
+    def _swap(self, fn, seq):
+        cap = self.seq_len(seq) // self.block_size + 1
+        out = np.zeros(2 * cap, dtype=np.int32)
+        n = ctypes.c_int(0)
+        check(fn(self._h, int(seq), out.ctypes.data_as(_native.pi32), cap, ctypes.byref(n)))
+        return [(int(out[2 * i]), int(out[2 * i + 1])) for i in range(n.value)]
+
+    def swap_out(self, seq: int) -> list:
+        """Pairs (device block, host slot), one per table entry."""
+        return self._swap(lib().pkv_alloc_swap_out, seq)
+
+    def swap_in(self, seq: int) -> list:
+        """Pairs (host slot, device block), one per table entry."""
+        return self._swap(lib().pkv_alloc_swap_in, seq)
+
+    def touch(self, seq: int):
+        check(lib().pkv_alloc_touch(self._h, int(seq)))
+
+    def lru(self) -> int:
+        out = ctypes.c_int64(0)
+        check(lib().pkv_alloc_lru(self._h, ctypes.byref(out)))
+        return int(out.value)
+
+    def is_swapped(self, seq: int) -> bool:
+        return bool(check_nonneg(lib().pkv_alloc_is_swapped(self._h, int(seq))))
+
+    def num_host_free(self) -> int:
+        return check_nonneg(lib().pkv_alloc_num_host_free(self._h))
 
 
 def check_nonneg(r: int) -> int:

@@ -68,6 +68,8 @@ SIGNATURES = {
                                       i32, i32, f32, i32, i32, f32, f32, vp]),
     "paged_attention_splitk_reduce": (i32, [vp, vp, sz, vp, i32, i32, i32, i32, i32, vp]),
     "paged_kv_copy_blocks": (i32, [vp, vp, vp, i32, sz, i32, vp]),
+    "paged_kv_swap_blocks": (i32, [vp, vp, vp, vp, vp, i32, sz, i32, i32, vp]),
+    "pkv_host_device_pointer": (i32, [vp, ctypes.POINTER(vp)]),
     "paged_kv_gather": (i32, [vp, vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, i32, i32, i32, vp]),
     "pkv_hbm_read_probe": (i32, [vp, sz, vp, i32, vp]),
     "pkv_alloc_create": (vp, [i32, i32, pi32]),
@@ -82,6 +84,13 @@ SIGNATURES = {
     "pkv_alloc_refcount": (i32, [vp, ctypes.c_int32]),
     "pkv_alloc_num_free": (i32, [vp]),
     "pkv_alloc_free_list": (i32, [vp, pi32, i32]),
+    "pkv_alloc_set_host_pool": (i32, [vp, i32]),
+    "pkv_alloc_swap_out": (i32, [vp, i64, pi32, i32, ctypes.POINTER(i32)]),
+    "pkv_alloc_swap_in": (i32, [vp, i64, pi32, i32, ctypes.POINTER(i32)]),
+    "pkv_alloc_touch": (i32, [vp, i64]),
+    "pkv_alloc_lru": (i32, [vp, ctypes.POINTER(i64)]),
+    "pkv_alloc_is_swapped": (i32, [vp, i64]),
+    "pkv_alloc_num_host_free": (i32, [vp]),
 }
 
 

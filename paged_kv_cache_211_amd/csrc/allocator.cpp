@@ -8,7 +8,10 @@
 // they diverge; a block table maps each sequence's logical blocks to scattered
 // physical blocks.  The unstated policy (FIFO free list, copy-on-write of a
 // shared, partly filled last block, all-or-nothing calls) is spelled out in
-// pkv.h.
+// pkv.h, and so are swapping to a host pool and the least-recently-used
+// choice of a sequence to swap ("PagedAttention Kernel：大模型推理优化的显存管
+// 理革新" §4.1 compares replacement policies; its table is missing, so the
+// policy is a reading).
 //
 // Single-threaded by contract: callers serialise access to one allocator.
 
@@ -24,9 +27,14 @@ struct pkv_alloc {
   int bs = 0;
   std::deque<int32_t> free_q;
   std::vector<int32_t> ref;
+  std::deque<int32_t> host_free;   // host pool slots, FIFO
+  int num_host = 0;
+  int64_t clock = 0;                // ticks on add, fork, append, swap_in, touch
   struct Seq {
-    std::vector<int32_t> table;
+    std::vector<int32_t> table;     // device blocks, or host slots when swapped
     int64_t len = 0;
+    bool swapped = false;
+    int64_t stamp = 0;
   };
   std::unordered_map<int64_t, Seq> seqs;
 };
@@ -37,6 +45,10 @@ int no_seq(int64_t seq) { return pkv::fail(PKV_ERR_SEQ, "unknown sequence %lld",
 
 void drop_ref(pkv_alloc* a, int32_t b) {
   if (--a->ref[b] == 0) a->free_q.push_back(b);
+}
+
+int swapped_out(int64_t seq) {
+  return pkv::fail(PKV_ERR_INVALID, "sequence %lld is swapped out", (long long)seq);
 }
 
 }  // namespace
@@ -76,7 +88,9 @@ void pkv_alloc_destroy(pkv_alloc* a) { delete a; }
 int pkv_alloc_add_seq(pkv_alloc* a, int64_t seq) {
   if (!a) return pkv::fail(PKV_ERR_INVALID, "null allocator");
   if (a->seqs.count(seq)) return pkv::fail(PKV_ERR_SEQ, "sequence %lld exists", (long long)seq);
-  a->seqs.emplace(seq, pkv_alloc::Seq{});
+  pkv_alloc::Seq s;
+  s.stamp = ++a->clock;
+  a->seqs.emplace(seq, std::move(s));
   return PKV_OK;
 }
 
@@ -85,8 +99,10 @@ int pkv_alloc_fork(pkv_alloc* a, int64_t parent, int64_t child) {
   auto it = a->seqs.find(parent);
   if (it == a->seqs.end()) return no_seq(parent);
   if (a->seqs.count(child)) return pkv::fail(PKV_ERR_SEQ, "sequence %lld exists", (long long)child);
+  if (it->second.swapped) return swapped_out(parent);
   pkv_alloc::Seq c = it->second;  // copy before emplace may rehash
   for (int32_t b : c.table) ++a->ref[b];
+  c.stamp = ++a->clock;
   a->seqs.emplace(child, std::move(c));
   return PKV_OK;
 }
@@ -96,6 +112,7 @@ int pkv_alloc_append(pkv_alloc* a, int64_t seq, int n_tokens, int32_t* slots_out
   if (!a) return pkv::fail(PKV_ERR_INVALID, "null allocator");
   auto it = a->seqs.find(seq);
   if (it == a->seqs.end()) return no_seq(seq);
+  if (it->second.swapped) return swapped_out(seq);
   if (n_tokens < 0) return pkv::fail(PKV_ERR_INVALID, "negative token count");
   if (n_tokens > 0 && !slots_out) return pkv::fail(PKV_ERR_INVALID, "null slots_out");
   pkv_alloc::Seq& s = it->second;
@@ -138,6 +155,7 @@ int pkv_alloc_append(pkv_alloc* a, int64_t seq, int n_tokens, int32_t* slots_out
     s.len = pos + 1;
   }
   if (n_cow_out) *n_cow_out = n_cow;
+  s.stamp = ++a->clock;
   return PKV_OK;
 }
 
@@ -145,9 +163,120 @@ int pkv_alloc_free_seq(pkv_alloc* a, int64_t seq) {
   if (!a) return pkv::fail(PKV_ERR_INVALID, "null allocator");
   auto it = a->seqs.find(seq);
   if (it == a->seqs.end()) return no_seq(seq);
-  for (int32_t b : it->second.table) drop_ref(a, b);
+  if (it->second.swapped) {
+    for (int32_t h : it->second.table) a->host_free.push_back(h);
+  } else {
+    for (int32_t b : it->second.table) drop_ref(a, b);
+  }
   a->seqs.erase(it);
   return PKV_OK;
+}
+
+int pkv_alloc_set_host_pool(pkv_alloc* a, int num_host_blocks) {
+  if (!a) return pkv::fail(PKV_ERR_INVALID, "null allocator");
+  if (num_host_blocks < 0) return pkv::fail(PKV_ERR_INVALID, "negative host pool size");
+  for (const auto& kv : a->seqs)
+    if (kv.second.swapped) return pkv::fail(PKV_ERR_INVALID, "sequences are swapped out");
+  a->num_host = num_host_blocks;
+  a->host_free.clear();
+  for (int i = 0; i < num_host_blocks; ++i) a->host_free.push_back(i);
+  return PKV_OK;
+}
+
+int pkv_alloc_swap_out(pkv_alloc* a, int64_t seq, int32_t* pairs_out, int cap, int* n_out) {
+  if (!a) return pkv::fail(PKV_ERR_INVALID, "null allocator");
+  auto it = a->seqs.find(seq);
+  if (it == a->seqs.end()) return no_seq(seq);
+  pkv_alloc::Seq& s = it->second;
+  if (s.swapped) return swapped_out(seq);
+  for (int32_t b : s.table)
+    if (a->ref[b] != 1)
+      return pkv::fail(PKV_ERR_INVALID, "sequence %lld holds shared blocks", (long long)seq);
+  const size_t n = s.table.size();
+  if (n > a->host_free.size())
+    return pkv::fail(PKV_ERR_NO_BLOCKS, "need %zu host slots, have %zu", n, a->host_free.size());
+  if ((int64_t)n > cap || (n > 0 && !pairs_out))
+    return pkv::fail(PKV_ERR_INVALID, "pairs_out holds %d pairs, need %zu", cap, n);
+  for (size_t i = 0; i < n; ++i) {
+    const int32_t b = s.table[i];
+    const int32_t h = a->host_free.front();
+    a->host_free.pop_front();
+    pairs_out[2 * i] = b;
+    pairs_out[2 * i + 1] = h;
+    drop_ref(a, b);
+    s.table[i] = h;
+  }
+  s.swapped = true;
+  if (n_out) *n_out = (int)n;
+  return PKV_OK;
+}
+
+int pkv_alloc_swap_in(pkv_alloc* a, int64_t seq, int32_t* pairs_out, int cap, int* n_out) {
+  if (!a) return pkv::fail(PKV_ERR_INVALID, "null allocator");
+  auto it = a->seqs.find(seq);
+  if (it == a->seqs.end()) return no_seq(seq);
+  pkv_alloc::Seq& s = it->second;
+  if (!s.swapped) return pkv::fail(PKV_ERR_INVALID, "sequence %lld is resident", (long long)seq);
+  const size_t n = s.table.size();
+  if (n > a->free_q.size())
+    return pkv::fail(PKV_ERR_NO_BLOCKS, "need %zu free blocks, have %zu", n, a->free_q.size());
+  if ((int64_t)n > cap || (n > 0 && !pairs_out))
+    return pkv::fail(PKV_ERR_INVALID, "pairs_out holds %d pairs, need %zu", cap, n);
+  for (size_t i = 0; i < n; ++i) {
+    const int32_t h = s.table[i];
+    const int32_t b = a->free_q.front();
+    a->free_q.pop_front();
+    a->ref[b] = 1;
+    pairs_out[2 * i] = h;
+    pairs_out[2 * i + 1] = b;
+    a->host_free.push_back(h);
+    s.table[i] = b;
+  }
+  s.swapped = false;
+  s.stamp = ++a->clock;
+  if (n_out) *n_out = (int)n;
+  return PKV_OK;
+}
+
+int pkv_alloc_touch(pkv_alloc* a, int64_t seq) {
+  if (!a) return pkv::fail(PKV_ERR_INVALID, "null allocator");
+  auto it = a->seqs.find(seq);
+  if (it == a->seqs.end()) return no_seq(seq);
+  it->second.stamp = ++a->clock;
+  return PKV_OK;
+}
+
+int pkv_alloc_lru(const pkv_alloc* a, int64_t* seq_out) {
+  if (!a || !seq_out) return pkv::fail(PKV_ERR_INVALID, "null argument");
+  bool found = false;
+  int64_t best = 0, best_stamp = 0;
+  for (const auto& kv : a->seqs) {
+    const pkv_alloc::Seq& s = kv.second;
+    if (s.swapped || s.table.empty()) continue;
+    bool shared = false;
+    for (int32_t b : s.table) shared = shared || a->ref[b] != 1;
+    if (shared) continue;
+    if (!found || s.stamp < best_stamp) {
+      found = true;
+      best = kv.first;
+      best_stamp = s.stamp;
+    }
+  }
+  if (!found) return pkv::fail(PKV_ERR_SEQ, "no sequence can be swapped out");
+  *seq_out = best;
+  return PKV_OK;
+}
+
+int pkv_alloc_is_swapped(const pkv_alloc* a, int64_t seq) {
+  if (!a) return pkv::fail(PKV_ERR_INVALID, "null allocator");
+  auto it = a->seqs.find(seq);
+  if (it == a->seqs.end()) return no_seq(seq);
+  return it->second.swapped ? 1 : 0;
+}
+
+int pkv_alloc_num_host_free(const pkv_alloc* a) {
+  if (!a) return pkv::fail(PKV_ERR_INVALID, "null allocator");
+  return (int)a->host_free.size();
 }
 
 int pkv_alloc_block_table(const pkv_alloc* a, int64_t seq, int32_t* out, int cap, int* n_out) {
@@ -168,6 +297,7 @@ int pkv_alloc_fill_tables(const pkv_alloc* a, const int64_t* seqs, int num_seqs,
   for (int i = 0; i < num_seqs; ++i) {
     auto it = a->seqs.find(seqs[i]);
     if (it == a->seqs.end()) return no_seq(seqs[i]);
+    if (it->second.swapped) return swapped_out(seqs[i]);
     if ((int64_t)it->second.table.size() > width)
       return pkv::fail(PKV_ERR_INVALID, "table of sequence %lld wider than %d",
                        (long long)seqs[i], width);

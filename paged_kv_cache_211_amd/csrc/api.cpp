@@ -645,6 +645,35 @@ int paged_kv_copy_blocks(void* key_cache, void* value_cache, const int32_t* pair
                     "paged_kv_copy_blocks launch");
 }
 
+int paged_kv_swap_blocks(void* dst_key_cache, void* dst_value_cache, const void* src_key_cache,
+                         const void* src_value_cache, const int32_t* pairs, int num_pairs,
+                         size_t block_bytes, int src_blocks, int dst_blocks, void* stream) {
+  if (num_pairs < 0 || src_blocks <= 0 || dst_blocks <= 0) return fail(PKV_ERR_INVALID, "bad sizes");
+  if (num_pairs == 0) {
+    clear_error();
+    return PKV_OK;
+  }
+  if (!dst_key_cache || !dst_value_cache || !src_key_cache || !src_value_cache || !pairs)
+    return fail(PKV_ERR_INVALID, "null pointer argument");
+  if (block_bytes == 0 || block_bytes % 16 != 0)
+    return fail(PKV_ERR_INVALID, "block_bytes must be a positive multiple of 16");
+  return hip_status(launch_swap_blocks(dst_key_cache, dst_value_cache, src_key_cache,
+                                       src_value_cache, pairs, num_pairs, block_bytes, src_blocks,
+                                       dst_blocks, stream),
+                    "paged_kv_swap_blocks launch");
+}
+
+int pkv_host_device_pointer(const void* host, void** device_out) {
+  if (!host || !device_out) return fail(PKV_ERR_INVALID, "null pointer argument");
+  void* d = nullptr;
+  const int rc = hip_status(hipHostGetDevicePointer(&d, const_cast<void*>(host), 0),
+                            "hipHostGetDevicePointer (is the memory pinned?)");
+  if (rc) return rc;
+  if (!d) return fail(PKV_ERR_HIP, "hipHostGetDevicePointer returned null");
+  *device_out = d;
+  return PKV_OK;
+}
+
 int paged_kv_gather(void* k_out, void* v_out, const void* key_cache, const void* value_cache,
                     const int32_t* block_tables, int max_blocks_per_seq, const int32_t* cu_ctx,
                     int num_seqs, int total_tokens, int num_kv_heads, int head_dim, int block_size,

@@ -83,6 +83,38 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(uint8_t* __restrict__ 
   for (size_t i = threadIdx.x; i < n; i += 256) d[i] = s[i];
 }
 
+// Whole blocks between two pools of one layout (a device pool and a pinned
+// host pool reached through its device pointer): workgroup (i, pool) copies
+// src block pairs[i][0] to dst block pairs[i][1], four 16-byte units per
+// thread in flight (loads from host memory cross the host link, so many
+// must be outstanding).  Ids out of range skip the pair.
+__global__ __launch_bounds__(256) void swap_blocks_kernel(uint8_t* __restrict__ dk,
+                                                          uint8_t* __restrict__ dv,
+                                                          const uint8_t* __restrict__ sk,
+                                                          const uint8_t* __restrict__ sv,
+                                                          const int32_t* __restrict__ pairs,
+                                                          size_t block_bytes, int src_nb,
+                                                          int dst_nb) {
+  const int src = pairs[2 * blockIdx.x], dst = pairs[2 * blockIdx.x + 1];
+  if ((unsigned)src >= (unsigned)src_nb || (unsigned)dst >= (unsigned)dst_nb) return;
+  const u32x4* s = (const u32x4*)((blockIdx.y == 0 ? sk : sv) + (size_t)src * block_bytes);
+  u32x4* d = (u32x4*)((blockIdx.y == 0 ? dk : dv) + (size_t)dst * block_bytes);
+  const size_t n = block_bytes / 16;
+  for (size_t i0 = threadIdx.x; i0 < n; i0 += 4 * 256) {
+    u32x4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const size_t i = i0 + (size_t)u * 256;
+      if (i < n) v[u] = s[i];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const size_t i = i0 + (size_t)u * 256;
+      if (i < n) d[i] = v[u];
+    }
+  }
+}
+
 // One thread per (output row, kv head, 16-byte unit of the dense row).
 template <int CACHE>
 __global__ __launch_bounds__(256) void gather_kernel(uint8_t* __restrict__ k_out,
@@ -178,6 +210,15 @@ int launch_copy_blocks(void* kc, void* vc, const int32_t* pairs, int n, size_t b
   if (n == 0) return 0;
   hipLaunchKernelGGL(copy_blocks_kernel, dim3(n, 2), dim3(256), 0, (hipStream_t)stream,
                      (uint8_t*)kc, (uint8_t*)vc, pairs, block_bytes, nb);
+  return (int)hipGetLastError();
+}
+
+int launch_swap_blocks(void* dk, void* dv, const void* sk, const void* sv, const int32_t* pairs,
+                       int n, size_t block_bytes, int src_nb, int dst_nb, void* stream) {
+  if (n == 0) return 0;
+  hipLaunchKernelGGL(swap_blocks_kernel, dim3(n, 2), dim3(256), 0, (hipStream_t)stream,
+                     (uint8_t*)dk, (uint8_t*)dv, (const uint8_t*)sk, (const uint8_t*)sv, pairs,
+                     block_bytes, src_nb, dst_nb);
   return (int)hipGetLastError();
 }
 

@@ -17,7 +17,8 @@ from . import (BlockAllocator, empty_pools, paged_attention_decode, paged_attent
                paged_attention_decode_step_streamk, paged_attention_decode_streamk,
                paged_attention_partition_offsets, paged_attention_streamk_workers,
                paged_attention_streamk_workspace_bytes, paged_attention_tile_offsets,
-               paged_attention_workspace_bytes, paged_kv_copy_blocks, paged_kv_write)
+               paged_attention_workspace_bytes, paged_kv_copy_blocks, paged_kv_swap_blocks,
+               paged_kv_write)
 
 
 class PagedKVCache:
@@ -68,6 +69,31 @@ class PagedKVCache:
             V = torch.cat(vals) if len(vals) > 1 else vals[0]
             self.write(K.contiguous(), V.contiguous(), torch.from_numpy(sl).to(self.device), stream)
         return sl
+
+    # -- swapping to host memory -----------------------------------------------
+    def host_pool(self, num_host_blocks: int):
+        """Pinned host pools of num_host_blocks blocks for swapped-out sequences."""
+        self.host_key, self.host_value = empty_pools(num_host_blocks, self.H, self.D, self.bs,
+                                                     self.dtype, "cpu", pin=True)
+        self.alloc.set_host_pool(num_host_blocks)
+
+    def swap_out(self, seq: int, stream=None):
+        """Move seq's blocks to host slots; its device blocks become free
+        (later writes to them are ordered after this copy on the stream)."""
+        pairs = self.alloc.swap_out(seq)
+        if pairs:
+            p = torch.tensor(pairs, dtype=torch.int32).to(self.device)
+            paged_kv_swap_blocks(self.host_key, self.host_value, self.key_cache, self.value_cache,
+                                 p, stream=stream)
+        return pairs
+
+    def swap_in(self, seq: int, stream=None):
+        pairs = self.alloc.swap_in(seq)
+        if pairs:
+            p = torch.tensor(pairs, dtype=torch.int32).to(self.device)
+            paged_kv_swap_blocks(self.key_cache, self.value_cache, self.host_key, self.host_value,
+                                 p, stream=stream)
+        return pairs
 
     def write(self, key, value, slot_mapping, stream=None):
         paged_kv_write(key, value, self.key_cache, self.value_cache, slot_mapping,

@@ -133,6 +133,16 @@ def prefill_chunks(wl: "Workload", lo: int | None = None, hi: int | None = None)
                     dtype=np.int64)
 
 
+def extra_rows(wl: "Workload", n: int, tag: int):
+    """Seeded key/value rows [n, H_kv, d] (stored bits of the written dtype)
+    for a sequence outside the workload, from default_rng([seed, 7, tag])."""
+    c = wl.cfg
+    rng = np.random.default_rng([c.seed, 7, tag])
+    k = _round(rng.standard_normal((n, c.H_kv, c.d), dtype=np.float32), c.src_dtype)
+    v = _round(rng.standard_normal((n, c.H_kv, c.d), dtype=np.float32), c.src_dtype)
+    return k, v
+
+
 def prefill_queries(wl: "Workload", chunk_lens) -> np.ndarray:
     """Seeded chunk query rows, stored bits [sum(chunk_lens), H_q, d]."""
     c = wl.cfg

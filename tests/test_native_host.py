@@ -65,14 +65,18 @@ class Both:
         if op == "append" and err_m is None:
             slots, cows = r_m
             assert list(r_c[0]) == slots and [tuple(p) for p in r_c[1]] == [tuple(p) for p in cows]
+        if op in ("swap_out", "swap_in", "lru") and err_m is None:
+            assert r_c == r_m, (op, args, r_c, r_m)
         self.compare()
 
     def compare(self):
         assert self.c.free_list() == self.m.free_list()
         assert [self.c.refcount(b) for b in range(self.nb)] == [self.m.refcount(b) for b in range(self.nb)]
+        assert self.c.num_host_free() == self.m.num_host_free()
         for s in self.m.tables:
             assert list(self.c.block_table(s)) == self.m.table(s)
             assert self.c.seq_len(s) == self.m.length(s)
+            assert self.c.is_swapped(s) == self.m.is_swapped(s)
 
 
 def test_allocator_matches_model_on_hand_trace(pkv, golden_dir):
@@ -145,6 +149,78 @@ def test_allocator_matches_model_exhaustively(pkv):
 
     walk([], [], 0, 6)
     assert count > 20000
+
+
+def test_allocator_swaps_match_model_on_random_ops(pkv):
+    rng = np.random.default_rng(23)
+    for _ in range(60):
+        nb, nh = int(rng.integers(1, 16)), int(rng.integers(0, 12))
+        bs = int(rng.choice([1, 2, 4]))
+        b = Both(pkv, nb, bs, rng.permutation(nb))
+        b.do("set_host_pool", nh)
+        live, nxt = [], 0
+        for _ in range(50):
+            r = rng.random()
+            if r < 0.15 or not live:
+                b.do("add_seq", nxt); live.append(nxt); nxt += 1
+            elif r < 0.25:
+                b.do("fork", int(rng.choice(live)), nxt)
+                if nxt in b.m.tables:
+                    live.append(nxt)
+                nxt += 1
+            elif r < 0.55:
+                b.do("append", int(rng.choice(live)), int(rng.integers(0, 3 * bs + 1)))
+            elif r < 0.68:
+                b.do("swap_out", int(rng.choice(live)))
+            elif r < 0.8:
+                b.do("swap_in", int(rng.choice(live)))
+            elif r < 0.86:
+                b.do("touch", int(rng.choice(live)))
+            elif r < 0.92:
+                b.do("lru")
+            elif r < 0.94:
+                b.do("set_host_pool", int(rng.integers(0, 12)))
+            else:
+                s = int(rng.choice(live)); b.do("free_seq", s); live.remove(s)
+
+
+def test_allocator_swaps_match_model_exhaustively(pkv):
+    """Every op sequence of length <= 5 with swaps on a 3-block pool, 2 host slots."""
+    nb, bs, order = 3, 2, [1, 2, 0]
+
+    def ops(live, nxt):
+        yield ("add_seq", nxt)
+        yield ("lru",)
+        for s in live:
+            yield ("fork", s, nxt)
+            yield ("append", s, 1)
+            yield ("append", s, 3)
+            yield ("swap_out", s)
+            yield ("swap_in", s)
+            yield ("touch", s)
+            yield ("free_seq", s)
+
+    count = 0
+
+    def walk(path, live, nxt, depth):
+        nonlocal count
+        if depth == 0:
+            return
+        for op in ops(live, nxt):
+            b = Both(pkv, nb, bs, order)
+            b.do("set_host_pool", 2)
+            for p in path + [op]:
+                b.do(*p)
+            count += 1
+            lv, nx = list(live), nxt
+            if op[0] in ("add_seq", "fork") and op[-1] in b.m.tables:
+                lv.append(op[-1]); nx += 1
+            if op[0] == "free_seq":
+                lv.remove(op[1])
+            walk(path + [op], lv, nx, depth - 1)
+
+    walk([], [], 0, 5)
+    assert count > 10000
 
 
 def test_allocator_error_paths(pkv):
