@@ -23,6 +23,11 @@ Prints ONE JSON line on stdout; details go to stderr.
 
     python bench.py [--steps K] [--warmup W] [--config 3] [--gpus 1] [--mode fused]
     python bench.py --prefill
+    python bench.py --swap
+
+--swap times moving whole sequences of the GQA workload to a pinned host
+pool and back (paged_kv_swap_blocks driven by the allocator's swap pairs);
+its roofline is the host link (PCIe 5.0 x16, 64 GB/s each way).
 """
 
 from __future__ import annotations
@@ -43,6 +48,8 @@ if ROOT not in sys.path:
 METRIC = "paged-attn decode µs/step + effective KV GB/s as % of MI355X HBM peak"
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, vendor figure
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix cores, vendor figure
+HOST_LINK_PEAK_GBPS = 64.0  # PCIe 5.0 x16, one direction
+SWAP_METRIC = "KV swap to host and back: µs per round trip + host-link GB/s"
 PREFILL_METRIC = "chunked prefill µs/step (store chunk + causal attention) + matrix-core TFLOP/s"
 ELEM = {"f32": 4, "bf16": 2, "fp8": 1}
 # sources of the decode kernels: a counter file taken on other sources is stale
@@ -73,6 +80,9 @@ def parse():
     p.add_argument("--workers", type=int, default=0, help="stream-K waves (0 = resident count)")
     p.add_argument("--prefill", action="store_true",
                    help="time chunked prefill (store + causal attention) instead of decode")
+    p.add_argument("--swap", action="store_true",
+                   help="time swapping sequences to a pinned host pool and back")
+    p.add_argument("--swap-seqs", type=int, default=16, help="sequences moved per swap")
     return p.parse_args()
 
 
@@ -314,6 +324,91 @@ def main_prefill(args):
     print(json.dumps(line), flush=True)
 
 
+def main_swap(args):
+    import numpy as np
+    import torch
+
+    import synth
+    import paged_kv_cache_211_amd as pkv
+    from paged_kv_cache_211_amd import workload as W
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    wl = synth.make(3)
+    c = wl.cfg
+    cache, _ = W.build(wl, poison=False, device=dev)
+    n = min(args.swap_seqs, c.S)
+    seqs = list(range(n))
+    nblocks = sum(len(cache.alloc.block_table(s)) for s in seqs)
+    cache.host_pool(nblocks)
+    block_bytes = c.H_kv * c.bs * c.d * ELEM[c.kv_dtype]
+    moved = nblocks * block_bytes * 2            # key and value pools
+    log(f"[bench] swap: {n} sequences, {nblocks} blocks, {moved / 1e6:.1f} MB each way")
+    # the kernel alone, on fixed pairs (every device block of the sequences
+    # to host slots 0.. and back), K launches each way between events
+    dblk = np.concatenate([cache.alloc.block_table(s) for s in seqs]).astype(np.int32)
+    hslot = np.arange(nblocks, dtype=np.int32)
+    out_pairs = torch.from_numpy(np.stack([dblk, hslot], 1).copy()).to(dev)
+    in_pairs = torch.from_numpy(np.stack([hslot, dblk], 1).copy()).to(dev)
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+
+    def d2h():
+        pkv.paged_kv_swap_blocks(cache.host_key, cache.host_value, cache.key_cache,
+                                 cache.value_cache, out_pairs)
+
+    def h2d():
+        pkv.paged_kv_swap_blocks(cache.key_cache, cache.value_cache, cache.host_key,
+                                 cache.host_value, in_pairs)
+
+    for _ in range(args.warmup):
+        d2h()
+        h2d()
+    torch.cuda.synchronize()
+    e[0].record()
+    for _ in range(args.steps):
+        d2h()
+    e[1].record()
+    for _ in range(args.steps):
+        h2d()
+    e[2].record()
+    torch.cuda.synchronize()
+    out_us = e[0].elapsed_time(e[1]) / args.steps * 1e3
+    in_us = e[1].elapsed_time(e[2]) / args.steps * 1e3
+    # the whole call path: allocator swap pairs, their upload, the kernel
+    t0 = time.perf_counter()
+    steps = max(1, args.steps // 5)
+    for _ in range(steps):
+        for s in seqs:
+            cache.swap_out(s)
+        for s in seqs:
+            cache.swap_in(s)
+    torch.cuda.synchronize()
+    rt_us = (time.perf_counter() - t0) / steps * 1e6
+    gbps_out, gbps_in = moved / (out_us * 1e-6) / 1e9, moved / (in_us * 1e-6) / 1e9
+    log(f"[bench] swap kernel: device->host {out_us:.1f} us = {gbps_out:.1f} GB/s, host->device "
+        f"{in_us:.1f} us = {gbps_in:.1f} GB/s; per-sequence calls round trip {rt_us:.0f} us")
+    slow = min(gbps_out, gbps_in)
+    line = {
+        "metric": SWAP_METRIC, "value": round(out_us + in_us, 2), "unit": "us/round-trip",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round((out_us + in_us) / 1e3, 5), "higher_is_better": False,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"{c.key}: sequences 0..{n - 1} ({nblocks} blocks of "
+                               f"{block_bytes * 2} bytes) to a pinned host pool and back",
+                   "parallelism": "single GPU"},
+        "kernel_us": {"swap_device_to_host": round(out_us, 2), "swap_host_to_device": round(in_us, 2),
+                      "swap_calls_round_trip": round(rt_us, 1)},
+        "roofline": {"bound": "host-link", "achieved": round(slow, 2), "peak": HOST_LINK_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(slow / HOST_LINK_PEAK_GBPS, 4), "traffic": None,
+                     "kernel": "swap_blocks_kernel (slower direction)",
+                     "algorithmic_bytes_per_launch": moved,
+                     "device_to_host_GBps": round(gbps_out, 2), "host_to_device_GBps": round(gbps_in, 2)},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -324,6 +419,8 @@ def main():
         sys.exit(2)
     if args.prefill:
         return main_prefill(args)
+    if args.swap:
+        return main_swap(args)
 
     import numpy as np
     import torch
