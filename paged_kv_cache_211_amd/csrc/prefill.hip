@@ -54,10 +54,24 @@ __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast
 typedef const int32_t __attribute__((address_space(4))) * cint_ptr;
 __device__ __forceinline__ cint_ptr as_const(const int32_t* p) { return (cint_ptr)p; }
 
+// LDS ring: kStages block pairs per workgroup, each [K block 0][K block 1]
+// [V block 0][V block 1] of kTile bytes.  Keys keep the pool's layout; the
+// 16-byte units of a value tile are swizzled so that the transposed reads
+// (lanes 0..15 reading dim rows 0..15 at one half) hit distinct banks: dim
+// row d's half h sits in unit 2d + (h ^ ((d >> 3) & 1)).
+constexpr int kStages = 3;
+constexpr int kPairBytes = 4 * kTile;
+
+__device__ __forceinline__ int vunit(int d, int h) { return 2 * d + (h ^ ((d >> 3) & 1)); }
+
 // Workgroup wg (after the XCD remap) covers query block qb of (s, hkv):
 // rows [qb * kNW * 32, (qb + 1) * kNW * 32) of the C * G rows of that kv head.
+// Its waves share one copy of each block pair in LDS: every wave loads a
+// quarter of the pair straight into LDS (16-byte direct loads), a barrier per
+// pair publishes it, and each wave reads its matrix-core operands from LDS.
 __global__ __launch_bounds__(kNW * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void prefill_kernel(const PrefillArgs a) {
+  __shared__ __align__(16) uint8_t ring[kStages][kPairBytes];
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int col = lane & 31, g = lane >> 5;
@@ -67,7 +81,7 @@ void prefill_kernel(const PrefillArgs a) {
   // read the same blocks, share that XCD's L2.
   const int per = (a.total_wg + 7) / 8;
   const int wg = (blockIdx.x % 8) * per + blockIdx.x / 8;
-  if (wg >= a.total_wg) return;
+  if (wg >= a.total_wg) return;   // whole workgroup
   const int qb = wg % a.qblocks;
   const int sh = wg / a.qblocks;
   const int hkv = sh % a.Hkv, s = sh / a.Hkv;
@@ -76,10 +90,12 @@ void prefill_kernel(const PrefillArgs a) {
   const int C = as_const(a.q_start)[s + 1] - r0q;
   const int L = as_const(a.lens)[s];
   const int nrows = C * G;
-  const int row0 = (qb * kNW + w) * kRows;
-  if (row0 >= nrows) return;   // no rows for this wave (no barriers follow)
+  const int wg_row0 = qb * kNW * kRows;
+  if (wg_row0 >= nrows) return;   // whole workgroup: no rows here
   // a chunk longer than its context or a context beyond the table: NaN rows
   bool bad = C > L || L > a.max_blocks * kBS || C < 0;
+  const int row0 = wg_row0 + w * kRows;
+  const bool active = row0 < nrows;   // a wave past the chunk still loads and syncs
 
   // ---- this lane's query row ----
   const int row = row0 + col;
@@ -87,12 +103,14 @@ void prefill_kernel(const PrefillArgs a) {
   const int pl = row_ok ? row / G : C - 1;       // chunk position (padding rows: the last)
   const int qh = hkv * G + (row_ok ? row % G : 0);
   const int p = L - C + pl;                       // tokens 0 .. p are visible to this row
-  const int last_row = min(nrows - 1, row0 + kRows - 1);
-  // first and last row's positions; wave-uniform (the divisions expand on
-  // the vector ALUs, so their results are moved back to scalar registers)
-  const int p_min = __builtin_amdgcn_readfirstlane(L - C + row0 / G);
-  const int p_max = __builtin_amdgcn_readfirstlane(L - C + last_row / G);
-  const int nblk = bad ? 0 : (p_max + kBS) / kBS; // blocks holding tokens 0 .. p_max
+  // first and last row's positions of this wave and of the workgroup;
+  // uniform (the divisions expand on the vector ALUs, so their results are
+  // moved back to scalar registers)
+  const int p_min = __builtin_amdgcn_readfirstlane(L - C + min(row0, nrows - 1) / G);
+  const int p_max = __builtin_amdgcn_readfirstlane(L - C + min(nrows - 1, row0 + kRows - 1) / G);
+  const int wg_last = min(nrows - 1, wg_row0 + kNW * kRows - 1);
+  const int wg_p_max = __builtin_amdgcn_readfirstlane(L - C + wg_last / G);
+  const int nblk = bad ? 0 : (wg_p_max + kBS) / kBS;   // blocks holding tokens 0 .. wg_p_max
   const int npairs = (nblk + 1) / 2;
 
   // Scores are used as exp2(s * qk - m) with qk = |scale| * log2(e) > 0: a
@@ -111,20 +129,17 @@ void prefill_kernel(const PrefillArgs a) {
     }
   }
 
-  // scalar table reads stay off the vector load counter the tile loads wait on
+  // scalar table reads stay off the vector load counter
   const cint_ptr tbl = as_const(a.tables + (size_t)s * a.max_blocks);
   const size_t head_off = (size_t)hkv * kTile;
   const size_t blk_stride = (size_t)a.Hkv * kTile;
-  // key row of A for this lane: token sigma(col) of block col / 16
-  const int kt = col & 15;
-  const int ktok = (kt & 3) | ((kt & 4) << 1) | ((kt & 8) >> 1);
-  const int kblk = col >> 4;
 
-  // A pair's two tile offsets: block ids 2jp and 2jp + 1 (the second past
-  // the wave's blocks repeats the first; its tokens are hidden), read with
-  // wave-uniform addresses (scalar loads), resolved once when the pair's keys
-  // load and kept for its values.
-  auto pair_base = [&](int jp, size_t& b0, size_t& b1) {   // jp wave-uniform, jp < npairs
+  // ---- staging: this wave's quarter of pair jp into ring stage st ----
+  // key units: identity; value units: lane slot q = 64w + lane holds dim
+  // row q / 2, half (q & 1) ^ bit 3 of that row
+  const int kq = w * 64 + lane;
+  const int vd = kq >> 1, vh = (kq & 1) ^ ((vd >> 3) & 1);
+  auto stage_pair = [&](int jp, int st) {   // jp, st wave-uniform, jp < npairs
     const int j0 = 2 * jp;
     int id0 = tbl[j0];
     int id1 = tbl[min(j0 + 1, nblk - 1)];
@@ -132,31 +147,36 @@ void prefill_kernel(const PrefillArgs a) {
       bad = true;
       id0 = id1 = 0;
     }
-    if (j0 + 1 >= nblk) id1 = id0;
-    b0 = (size_t)id0 * blk_stride + head_off;
-    b1 = (size_t)id1 * blk_stride + head_off;
-  };
-  u32x4 kr[8], vr[2][4];
-  auto load_keys = [&](size_t b0, size_t b1) {
-    const uint8_t* kp = (const uint8_t*)a.kc + (kblk ? b1 : b0) + (size_t)(g * kBS + ktok) * 16;
+    if (j0 + 1 >= nblk) id1 = id0;   // past the last block: a copy of the first, hidden
+    const size_t b[2] = {(size_t)id0 * blk_stride + head_off, (size_t)id1 * blk_stride + head_off};
+    uint8_t* dst = ring[st] + w * 1024;
 #pragma unroll
-    for (int sl = 0; sl < 8; ++sl) kr[sl] = *(const u32x4*)(kp + (size_t)sl * 2 * kBS * 16);
-  };
-  auto load_values = [&](size_t b0, size_t b1) {
-#pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      const uint8_t* vp = (const uint8_t*)a.vc + (b ? b1 : b0) + (size_t)(col * kBS + 8 * g) * 2;
-#pragma unroll
-      for (int m = 0; m < 4; ++m) vr[b][m] = *(const u32x4*)(vp + (size_t)m * 32 * kBS * 2);
+    for (int t = 0; t < 2; ++t) {
+      __builtin_amdgcn_global_load_lds(
+          (const void __attribute__((address_space(1)))*)((const uint8_t*)a.kc + b[t] + kq * 16),
+          (void __attribute__((address_space(3)))*)(dst + t * kTile), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(
+          (const void __attribute__((address_space(1)))*)((const uint8_t*)a.vc + b[t] +
+                                                           (2 * vd + vh) * 16),
+          (void __attribute__((address_space(3)))*)(dst + (2 + t) * kTile), 16, 0, 0);
     }
   };
-  auto qk_scores = [&]() {   // S^T = K Q^T over the 8 dim slices
+
+  // ---- operands from LDS ----
+  // key row of A for this lane: token sigma(col) of block col / 16
+  const int kt = col & 15;
+  const int ktok = (kt & 3) | ((kt & 4) << 1) | ((kt & 8) >> 1);
+  const int koff = (col >> 4) * kTile + (g * kBS + ktok) * 16;
+  auto qk_scores = [&](int st) {   // S^T = K Q^T over the 8 dim slices
+    const uint8_t* kp = ring[st] + koff;
     f32x16 sc;
 #pragma unroll
     for (int r = 0; r < 16; ++r) sc[r] = 0.f;
 #pragma unroll
-    for (int sl = 0; sl < 8; ++sl)
-      sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kr[sl]), as_bf16x8(qv[sl]), sc, 0, 0, 0);
+    for (int sl = 0; sl < 8; ++sl) {
+      const u32x4 k = *(const u32x4*)(kp + sl * 2 * kBS * 16);
+      sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(k), as_bf16x8(qv[sl]), sc, 0, 0, 0);
+    }
     return sc;
   };
 
@@ -171,31 +191,28 @@ void prefill_kernel(const PrefillArgs a) {
     for (int r = 0; r < 16; ++r) acc[m][r] = 0.f;
   const bf16x2 ones = __builtin_bit_cast(bf16x2, 0x3f803f80u);
 
-  // Software pipeline: while pair jp's softmax runs on the vector ALUs, pair
-  // jp + 1's QK^T is already on the matrix cores and pair jp + 2's keys are
-  // in flight; pair jp + 1's values load behind pair jp's PV.  Every
-  // iteration issues the same loads (pairs past the last repeat the last
-  // one, their results unused), so the compiler's load counters are exact
-  // and no wait covers a later pair's loads.
-  const int plast = npairs - 1;
-  size_t cb0 = 0, cb1 = 0, nb0 = 0, nb1 = 0;   // tile offsets: current pair, next pair
+  // Pipeline: pair jp + 2 streams into LDS while pair jp + 1's QK^T runs on
+  // the matrix cores and pair jp's softmax on the vector ALUs.  One barrier
+  // per pair: after it, pair jp + 1 is in LDS (every wave waited for its own
+  // quarter first) and every wave is done with pair jp - 1's stage, which
+  // pair jp + 2 then overwrites.
   f32x16 sc = {};
   if (npairs > 0) {
-    // same load order as every iteration: the next pair's keys, then this
-    // pair's values (so the counters at the loop head agree on every path)
-    pair_base(0, cb0, cb1);
-    load_keys(cb0, cb1);
-    sc = qk_scores();
-    pair_base(min(1, plast), nb0, nb1);
-    load_keys(nb0, nb1);
-    load_values(cb0, cb1);
+    stage_pair(0, 0);
+    if (npairs > 1) stage_pair(1, 1);
+    __builtin_amdgcn_s_waitcnt(0);   // all loads, query rows included
+    __syncthreads();
+    if (active) sc = qk_scores(0);
   }
   for (int jp = 0; jp < npairs; ++jp) {
     const int t0 = 32 * jp;   // first token of the pair
-    const f32x16 sn = qk_scores();   // next pair's scores
-    size_t fb0, fb1;
-    pair_base(min(jp + 2, plast), fb0, fb1);
-    load_keys(fb0, fb1);
+    const int st = jp % kStages;
+    __builtin_amdgcn_s_waitcnt(0);   // this wave's quarter of pair jp + 1
+    __syncthreads();
+    if (jp + 2 < npairs) stage_pair(jp + 2, (jp + 2) % kStages);
+    if (!active) continue;
+    f32x16 sn = {};
+    if (jp + 1 < npairs) sn = qk_scores((jp + 1) % kStages);   // next pair's scores
 
     // ---- tokens after the row's position are hidden (diagonal pairs only) ----
     // register 8b + i holds token t0 + 16b + 8g + i
@@ -241,12 +258,17 @@ void prefill_kernel(const PrefillArgs a) {
       pb[b] = u32x4{w4[0], w4[1], w4[2], w4[3]};
     }
 
-    // ---- O^T += V^T P^T, block by block ----
+    // ---- O^T += V^T P^T, block by block, value rows from LDS ----
     // value rows of tokens past the wave's last position are zeroed: their
     // probabilities are 0, but bytes past the context may hold anything
-    if (t0 + 31 > p_max) {
+    const bool tail = t0 + 31 > p_max;
 #pragma unroll
-      for (int b = 0; b < 2; ++b) {
+    for (int b = 0; b < 2; ++b) {
+      const uint8_t* vt = ring[st] + (2 + b) * kTile;
+      u32x4 vr[4];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) vr[m] = *(const u32x4*)(vt + vunit(32 * m + col, g) * 16);
+      if (tail) {
         const int first = t0 + 16 * b + 8 * g;   // token of the lane's first value
         const int keep = min(max(p_max + 1 - first, 0), 8);   // tokens kept, 0..8
 #pragma unroll
@@ -254,24 +276,19 @@ void prefill_kernel(const PrefillArgs a) {
           const int k2 = keep - 2 * e;   // tokens kept in this dword
           const uint32_t msk = k2 >= 2 ? 0xffffffffu : k2 == 1 ? 0x0000ffffu : 0u;
 #pragma unroll
-          for (int m = 0; m < 4; ++m) vr[b][m][e] &= msk;
+          for (int m = 0; m < 4; ++m) vr[m][e] &= msk;
         }
       }
-    }
-#pragma unroll
-    for (int b = 0; b < 2; ++b)
 #pragma unroll
       for (int m = 0; m < 4; ++m)
-        acc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vr[b][m]), as_bf16x8(pb[b]),
+        acc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vr[m]), as_bf16x8(pb[b]),
                                                          acc[m], 0, 0, 0);
-    load_values(nb0, nb1);
+    }
     sc = sn;
-    nb0 = fb0;
-    nb1 = fb1;
   }
 
   // ---- out = O / l, rows of this lane: dims 32m + 8q + 4g + (0..3) ----
-  if (!row_ok) return;
+  if (!active || !row_ok) return;
   const float lt = l_run + __shfl_xor(l_run, 32);
   const float inv = 1.0f / lt;
   uint16_t* orow = (uint16_t*)a.out + ((size_t)(r0q + pl) * a.Hq + qh) * kD;
