@@ -69,7 +69,7 @@ __device__ __forceinline__ int vunit(int d, int h) { return 2 * d + (h ^ ((d >> 
 // Its waves share one copy of each block pair in LDS: every wave loads a
 // quarter of the pair straight into LDS (16-byte direct loads), a barrier per
 // pair publishes it, and each wave reads its matrix-core operands from LDS.
-__global__ __launch_bounds__(kNW * 64) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ __launch_bounds__(kNW * 64) __attribute__((amdgpu_waves_per_eu(3)))
 void prefill_kernel(const PrefillArgs a) {
   __shared__ __align__(16) uint8_t ring[kStages][kPairBytes];
   const int lane = threadIdx.x & 63;
