@@ -46,7 +46,11 @@ using namespace dec;
 // (piece, head) pairs for the maxima and the weights (kept in LDS, a chunk
 // of pieces at a time); then PL piece lanes each sum every PL-th piece over
 // the NV = HG*D/4 float4 columns, four pieces' loads in flight, and LDS adds
-// the lanes.
+// the lanes.  With at most 4*PL pieces (every sequence of up to a few
+// partitions) all loads -- the (m, l) pairs and every partial row -- go out
+// at once: the weights then come from registers and the partial rows are
+// already in flight while the maxima are reduced, one memory round trip in
+// all instead of three.
 template <int D, bool F32OUT, int HG>
 __device__ __forceinline__ void merge_heads(void* __restrict__ out, size_t oi0,
                                             const float* __restrict__ ws_o,
@@ -59,6 +63,80 @@ __device__ __forceinline__ void merge_heads(void* __restrict__ out, size_t oi0,
   __shared__ float m_s[HG], l_s[HG];
   __shared__ f32x4 part[PL][NV];
   const int tid = threadIdx.x, hh_t = tid % HG, p_t = tid / HG;
+  const int pl = tid / NV, e = tid % NV;
+  const int hh_e = e * 4 / D, d4 = e * 4 % D;   // this thread's float4 column
+
+  // combine the PL lanes' sums and the row sums, normalise, store
+  auto finish = [&](f32x4 acc, float lsum) {
+    part[pl][e] = acc;
+    red[tid] = lsum;
+    __syncthreads();
+    for (int k = NT / 2; k >= HG; k >>= 1) {
+      if (tid < k) red[tid] += red[tid + k];
+      __syncthreads();
+    }
+    if (tid < HG) l_s[tid] = red[tid];
+    __syncthreads();
+    if (pl == 0) {
+#pragma unroll
+      for (int q = 1; q < PL; ++q) {
+        const f32x4 u = part[q][e];
+        acc.x += u.x; acc.y += u.y; acc.z += u.z; acc.w += u.w;
+      }
+      const float L = l_s[hh_e];
+      const float inv = L > 0.f ? 1.f / L : 0.f;   // a NaN partial stays NaN through acc
+      const float r0 = acc.x * inv, r1 = acc.y * inv, r2 = acc.z * inv, r3 = acc.w * inv;
+      const size_t o4 = oi0 + (size_t)hh_e * D + d4;
+      if constexpr (F32OUT) {
+        *(f32x4*)((float*)out + o4) = f32x4{r0, r1, r2, r3};
+      } else {
+        uint16_t* o16 = (uint16_t*)out + o4;
+        *(uint2*)o16 = make_uint2(pack_bf16x2(r0, r1), pack_bf16x2(r2, r3));
+      }
+    }
+  };
+
+  if (n <= 4 * PL && n <= PSTEP) {
+    float m_own = -INFINITY, l_own = 0.f;
+    if (p_t < n) {
+      const f32x2 ml = *(const f32x2*)(ws_ml + (row0 + (size_t)p_t * pstride + hh_t) * 2);
+      m_own = ml.x;
+      l_own = ml.y;
+    }
+    const float* op = ws_o + (row0 + hh_e) * D + d4;
+    const size_t ps = pstride * D;
+    f32x4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int p = pl + u * PL;
+      v[u] = p < n ? *(const f32x4*)(op + (size_t)p * ps) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    red[tid] = m_own;
+    __syncthreads();
+    for (int k = NT / 2; k >= HG; k >>= 1) {
+      if (tid < k) red[tid] = fmaxf(red[tid], red[tid + k]);
+      __syncthreads();
+    }
+    const float M_t = red[hh_t];
+    const float w_own = p_t < n && M_t != -INFINITY ? __builtin_amdgcn_exp2f(m_own - M_t) : 0.f;
+    if (p_t < n) w_lds[p_t][hh_t] = w_own;
+    __syncthreads();
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int p = pl + u * PL;
+      if (p < n) {
+        const float w = w_lds[p][hh_e];
+        acc.x = fmaf(v[u].x, w, acc.x);
+        acc.y = fmaf(v[u].y, w, acc.y);
+        acc.z = fmaf(v[u].z, w, acc.z);
+        acc.w = fmaf(v[u].w, w, acc.w);
+      }
+    }
+    __syncthreads();   // every thread has read red / w_lds before finish reuses red
+    finish(acc, p_t < n ? l_own * w_own : 0.f);
+    return;
+  }
 
   float mx = -INFINITY;
   for (int p = p_t; p < n; p += PSTEP) mx = fmaxf(mx, ws_ml[(row0 + p * pstride + hh_t) * 2]);
@@ -72,8 +150,6 @@ __device__ __forceinline__ void merge_heads(void* __restrict__ out, size_t oi0,
   __syncthreads();
   const float M_t = m_s[hh_t];
 
-  const int pl = tid / NV, e = tid % NV;
-  const int hh_e = e * 4 / D, d4 = e * 4 % D;   // this thread's float4 column
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   float lsum = 0.f;
   for (int pc = 0; pc < n; pc += PCH) {
@@ -111,32 +187,7 @@ __device__ __forceinline__ void merge_heads(void* __restrict__ out, size_t oi0,
     }
     __syncthreads();
   }
-  part[pl][e] = acc;
-  red[tid] = lsum;
-  __syncthreads();
-  for (int k = NT / 2; k >= HG; k >>= 1) {
-    if (tid < k) red[tid] += red[tid + k];
-    __syncthreads();
-  }
-  if (tid < HG) l_s[tid] = red[tid];
-  __syncthreads();
-  if (pl == 0) {
-#pragma unroll
-    for (int q = 1; q < PL; ++q) {
-      const f32x4 u = part[q][e];
-      acc.x += u.x; acc.y += u.y; acc.z += u.z; acc.w += u.w;
-    }
-    const float L = l_s[hh_e];
-    const float inv = L > 0.f ? 1.f / L : 0.f;   // a NaN partial stays NaN through acc
-    const float r0 = acc.x * inv, r1 = acc.y * inv, r2 = acc.z * inv, r3 = acc.w * inv;
-    const size_t o4 = oi0 + (size_t)hh_e * D + d4;
-    if constexpr (F32OUT) {
-      *(f32x4*)((float*)out + o4) = f32x4{r0, r1, r2, r3};
-    } else {
-      uint16_t* o16 = (uint16_t*)out + o4;
-      *(uint2*)o16 = make_uint2(pack_bf16x2(r0, r1), pack_bf16x2(r2, r3));
-    }
-  }
+  finish(acc, lsum);
 }
 
 // Split-K reduce: one workgroup per (sequence, group of HG query heads);
