@@ -473,7 +473,7 @@ def main():
     out = torch.empty_like(q)
     tab, lens = inp["block_tables"], inp["context_lens"]
     if PF:
-        n_launch = 4
+        n_launch = 3   # the store, the fused prefix + suffix pass, the reduce
     elif SK:
         n_launch = 2 if pkv.paged_attention_decode_step_launches(c.H_q, c.H_kv, c.d, c.bs, q.dtype,
                                                                  cache.dtype, 0) == 1 else 3

@@ -547,17 +547,19 @@ int paged_attention_decode_prefix(void* out, const void* query, const void* key_
   p.n_groups = num_groups;
   p.total_items = total_prefix_items;
   p.total_rows = total_rows;
-  rc = hip_status(launch_decode_prefix(a, p, stream), "shared-prefix decode launch");
-  if (rc) return rc;
   if (total_suffix_partitions > 0) {
+    // the prefix pass and the split-K pass over each sequence's own tokens
+    // in one launch (they write disjoint partial rows)
     DecodeArgs b = a;
     b.part_off = suffix_offsets;
     b.total_parts = total_suffix_partitions;
     b.t_start = token_start;
     b.row_off = row_offsets;
-    rc = hip_status(launch_decode(b, stream), "shared-prefix suffix decode launch");
-    if (rc) return rc;
+    rc = hip_status(launch_decode_prefix_fused(a, b, p, stream), "shared-prefix decode launch");
+  } else {
+    rc = hip_status(launch_decode_prefix(a, p, stream), "shared-prefix decode launch");
   }
+  if (rc) return rc;
   return hip_status(launch_splitk_reduce(out, a.ws, row_offsets, num_seqs, num_q_heads, head_dim,
                                          total_rows, q_dtype, stream, 1),
                     "shared-prefix reduce launch");

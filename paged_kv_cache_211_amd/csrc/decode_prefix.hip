@@ -30,6 +30,7 @@
 #include <hip/hip_runtime.h>
 
 #include "decode_common.h"
+#include "decode_valu.h"
 
 namespace pkv {
 namespace {
@@ -48,15 +49,14 @@ constexpr int kRows = 32;                  // query rows per wave
 // pre_off[g] + ((hkv * npre + pp) * RB + rb), so the row blocks of one piece
 // are neighbours (one workgroup reads each block for up to 128 rows).
 template <int NW>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
-void decode_prefix_kernel(const DecodeArgs a, PrefixArgs p) {
+__device__ __forceinline__ void prefix_body(const DecodeArgs& a, const PrefixArgs& p, int bid) {
   constexpr int D = kPD, BS = kPBS, TILE = kPTile;
   __shared__ __align__(16) uint16_t p_lds[NW][kRows][2 * BS];
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int col = lane & 31, g = lane >> 5;
-  const int item = blockIdx.x * NW + w;
+  const int item = bid * NW + w;
   if (item >= p.total_items) return;
 
   // ---- locate: group, then (kv head, piece, row block) ----
@@ -225,7 +225,40 @@ void decode_prefix_kernel(const DecodeArgs a, PrefixArgs p) {
   }
 }
 
+template <int NW>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
+void decode_prefix_kernel(const DecodeArgs a, PrefixArgs p) {
+  prefix_body<NW>(a, p, blockIdx.x);
+}
+
+// Both passes in one launch: workgroups [0, npre) run the prefix pass (args
+// a), the rest the split-K pass over each sequence's own tokens (args b).
+// Both are bound by memory latency, not bandwidth, so side by side on the
+// same compute units they hide each other's waits; npre is a multiple of 8
+// so the split-K workgroups keep their XCD order.
+template <int HPW>
+__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2)))
+void decode_prefix_fused_kernel(const DecodeArgs a, const DecodeArgs b, PrefixArgs p, int npre) {
+  if ((int)blockIdx.x < npre)
+    prefix_body<kWaves>(a, p, blockIdx.x);
+  else
+    valu::decode_body<PKV_BF16, kPD, kPBS, HPW, kWaves, kBufs, true, false>(b, blockIdx.x - npre);
+}
+
 }  // namespace
+
+int launch_decode_prefix_fused(const DecodeArgs& a, const DecodeArgs& b, const PrefixArgs& p,
+                               void* stream) {
+  const int npre = ((p.total_items + kWaves - 1) / kWaves + 7) / 8 * 8;
+  return valu::with_hpw<PKV_BF16, kPD, kPBS>(a.Hq / a.Hkv, [&](auto h) {
+    constexpr int HPW = decltype(h)::value;
+    const int groups = b.Hq / b.Hkv / HPW;
+    dim3 block(kWaves * 64), grid(npre + b.total_parts * b.Hkv * groups);
+    hipLaunchKernelGGL(decode_prefix_fused_kernel<HPW>, grid, block, 0, (hipStream_t)stream, a, b,
+                       p, npre);
+    return (int)hipGetLastError();
+  });
+}
 
 bool decode_prefix_supported(const DecodeArgs& a) {
   return a.q_dtype == PKV_BF16 && a.kv_dtype == PKV_BF16 && a.D == kPD && a.BS == kPBS;

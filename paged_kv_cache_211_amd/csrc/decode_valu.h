@@ -314,8 +314,10 @@ struct ValuHeads {
 
 // Shared-item schedule.  STORE (decode step): the workgroup that reads the
 // last block of a sequence first stores the sequence's new token there.
+// The body takes its workgroup index so that another kernel can run it on a
+// range of its own workgroups.
 template <int KV, int D, int BS, int HPW, int NW, int NBUF, bool SPLIT, bool STORE>
-__global__ __launch_bounds__(NW * 64) void decode_kernel(const DecodeArgs a) {
+__device__ __forceinline__ void decode_body(const DecodeArgs& a, int bid) {
   using St = ValuHeads<KV, D, BS, HPW, kQLds>;
   constexpr int NLOAD = St::NLOAD, RU = St::RU, DPI = St::DPI, TILE = Geo<KV, D, BS>::TILE;
 
@@ -332,7 +334,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const DecodeArgs a) {
   // every XCD serves one kv head, and blocks that several sequences share
   // stay in that XCD's L2.
   const int nhg = a.Hkv * (a.Hq / a.Hkv / HPW);
-  const Work wk = locate<SPLIT, BS>(a, HPW, lane, blockIdx.x / nhg, blockIdx.x % nhg);
+  const Work wk = locate<SPLIT, BS>(a, HPW, lane, bid / nhg, bid % nhg);
   bool bad = wk.bad;
   const int32_t* __restrict__ tbl = a.tables + (size_t)wk.s * a.max_blocks;
   const size_t head_off = (size_t)wk.hkv * TILE;
@@ -387,6 +389,11 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const DecodeArgs a) {
 
   // ---- merge the waves, then write the output or the partial ----
   merge_store<HPW, D, NW, St::F32>(a, wk, !SPLIT || wk.nparts == 1, o_lds, m_lds, l_lds, bad_lds);
+}
+
+template <int KV, int D, int BS, int HPW, int NW, int NBUF, bool SPLIT, bool STORE>
+__global__ __launch_bounds__(NW * 64) void decode_kernel(const DecodeArgs a) {
+  decode_body<KV, D, BS, HPW, NW, NBUF, SPLIT, STORE>(a, blockIdx.x);
 }
 
 // Stream-K schedule: wave gw of R = a.sk_workers takes tiles

@@ -102,6 +102,9 @@ int launch_sk_reduce(const DecodeArgs& a, void* stream);
 // 128, block size 16.
 bool decode_prefix_supported(const DecodeArgs& a);
 int launch_decode_prefix(const DecodeArgs& a, const PrefixArgs& p, void* stream);
+// the prefix pass (a) and the suffix split-K pass (b) in one launch
+int launch_decode_prefix_fused(const DecodeArgs& a, const DecodeArgs& b, const PrefixArgs& p,
+                               void* stream);
 int launch_swap_blocks(void* dk, void* dv, const void* sk, const void* sv, const int32_t* pairs,
                        int n, size_t block_bytes, int src_nb, int dst_nb, void* stream);
 bool prefill_supported(pkv_dtype q, pkv_dtype kv, int D, int BS);
