@@ -302,6 +302,33 @@ def test_decode_argument_validation_needs_no_gpu(pkv):
     assert L.paged_kv_copy_blocks(fake, fake, fake, 3, 100, 10, None) == -1
     assert L.paged_attention_splitk_reduce(fake, fake, 16, fake, 2, 8, 128, 2, 1, None) == -3
 
+    # chunked prefill: the same host checks, bf16 / head_dim 128 / block 16 only
+    def pre(**kw):
+        a = dict(dict(good, qs=fake, maxq=64), **kw)
+        return L.paged_attention_prefill(a["out"], a["q"], a["kc"], a["vc"], a["tb"], a["mb"],
+                                         a["lens"], a["qs"], a["S"], a["maxq"], a["Hq"], a["Hkv"],
+                                         a["D"], a["bs"], a["nb"], a["scale"], a["qd"], a["cd"],
+                                         a["ks"], a["vs"], None)
+
+    assert pre(qs=None) == -1
+    assert pre(maxq=-1) == -1
+    assert pre(Hq=7) == -1
+    assert pre(D=64) == -2
+    assert pre(bs=32) == -2
+    assert pre(qd=1, cd=2) == -2            # fp8 cache: not built for prefill
+    assert pre(scale=float("inf")) == -1
+    assert pre(S=0) == 0                    # nothing to do, nothing launched
+    assert pre(maxq=0) == 0
+    # swap: sizes, pointers and block size checked before any launch
+    sw = L.paged_kv_swap_blocks
+    assert sw(fake, fake, fake, fake, fake, 4, 100, 10, 10, None) == -1     # not a multiple of 16
+    assert sw(fake, fake, fake, fake, fake, -1, 4096, 10, 10, None) == -1
+    assert sw(fake, fake, fake, fake, fake, 4, 4096, 0, 10, None) == -1
+    assert sw(None, fake, fake, fake, fake, 4, 4096, 10, 10, None) == -1
+    assert sw(fake, fake, fake, fake, fake, 0, 4096, 10, 10, None) == 0
+    out = ctypes.c_void_p()
+    assert L.pkv_host_device_pointer(None, ctypes.byref(out)) == -1
+
 
 def test_prefix_plan_matches_its_definition():
     """The shared-prefix plan: per sequence its suffix partitions (from the end
