@@ -413,7 +413,7 @@ def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}, "
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, "
               f"WORLD_SIZE {world}); paged decode shards by sequence or kv head with no "
               "exchange, so per-GPU throughput is the one-GPU figure.", file=sys.stderr)
         sys.exit(2)

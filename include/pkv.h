@@ -431,7 +431,7 @@ int paged_kv_gather(void* k_out, void* v_out, const void* key_cache, const void*
  * `buffer` with 16-byte loads, eight in flight per lane, and store at most
  * one word to device `sink` (4 bytes).  Timing it gives the attainable HBM
  * read rate, the ceiling for the decode kernel's key/value stream (an HBM
- * bound kernel is judged by bytes moved, "Memory Systems" notes, core idea
+ * bound kernel is measured by bytes moved, "Memory Systems" notes, core idea
  * 1). */
 int pkv_hbm_read_probe(const void* buffer, size_t bytes, void* sink, int workgroups, void* stream);
 
