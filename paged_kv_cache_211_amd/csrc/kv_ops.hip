@@ -40,6 +40,114 @@ __global__ __launch_bounds__(256) void kv_write_kernel(const void* __restrict__ 
   write_kv_unit<CACHE>(key, value, kc, vc, t, h, c, slot, H, D, BS, k_inv, v_inv);
 }
 
+// Block-wise scatter (bf16 rows into a bf16 or fp8 cache).  Workgroup (g, h)
+// owns input rows g*BS .. g*BS + BS - 1 of kv head h.  A row is covered when
+// the BS rows around it that its slot's block needs (its block's slots, in
+// order, on consecutive input rows) are all present -- the usual case inside
+// the chunk of a prefill, wherever the chunk starts.  The workgroup whose
+// rows hold a covered block's first slot writes that whole block: key units
+// as contiguous 16-byte runs, value rows staged in LDS and written as whole
+// dim rows of the block's value tile (16-byte pieces, full lines) instead of
+// one element per dim row per token.  Rows that are not covered are
+// scattered one unit at a time as kv_write_kernel does.  The stored bits are
+// the same either way.
+template <int CACHE, int D, int BS>
+__global__ __launch_bounds__(256) void kv_write_block_kernel(const uint16_t* __restrict__ key,
+                                                             const uint16_t* __restrict__ value,
+                                                             uint8_t* __restrict__ kc,
+                                                             uint8_t* __restrict__ vc,
+                                                             const int32_t* __restrict__ slots,
+                                                             int T, int H, int nb, float k_inv,
+                                                             float v_inv) {
+  constexpr int E = CACHE == PKV_BF16 ? 2 : 1;   // cache element bytes
+  constexpr int X = 16 / E;                       // elements per 16-byte cache unit
+  constexpr int UNITS = D / X;                    // key units per token
+  constexpr int PER = 16 / E;                     // tokens per 16-byte piece of a value row
+  __shared__ uint32_t vt[BS][D / 2 + 1];          // a block's value rows (bf16 pairs)
+  __shared__ int covered[BS];
+  __shared__ int start;                           // row of a covered block's first slot
+  const int tid = threadIdx.x;
+  const int t0 = blockIdx.x * BS, h = blockIdx.y;
+  const int nslots = nb * BS;
+  if (tid < BS) covered[tid] = 1;
+  if (tid == 0) start = -1;
+  __syncthreads();
+  // coverage: pair (row r, offset k) checks that input row r - o + k holds
+  // slot (slot_r - o) + k, o being row r's offset in its block
+  for (int i = tid; i < BS * BS; i += 256) {
+    const int r = i / BS, k = i % BS, t = t0 + r;
+    bool ok = false;
+    if (t < T) {
+      const int sr = slots[t];
+      if (sr >= 0 && sr < nslots) {
+        const int o = sr % BS, ts = t - o;
+        ok = ts >= 0 && ts + BS <= T && slots[ts + k] == sr - o + k;
+      }
+    }
+    if (!ok) covered[r] = 0;
+  }
+  __syncthreads();
+  // a covered row at offset 0 starts its block; two such rows are at least
+  // BS rows apart, so at most one lies here
+  if (tid < BS && covered[tid] && slots[t0 + tid] % BS == 0) start = tid;
+  // rows that are not covered: one unit at a time
+  for (int i = tid; i < BS * UNITS; i += 256) {
+    const int r = i / UNITS, c = i % UNITS, t = t0 + r;
+    if (t >= T || covered[r]) continue;
+    const int slot = slots[t];
+    if (slot < 0 || slot >= nslots) continue;
+    write_kv_unit<CACHE>(key, value, kc, vc, t, h, c, slot, H, D, BS, k_inv, v_inv);
+  }
+  __syncthreads();
+  const int r0 = start;
+  if (r0 < 0) return;                     // no whole block starts in these rows
+  const int ts = t0 + r0;                 // its rows: ts .. ts + BS - 1
+  const size_t tile = (size_t)(slots[ts] / BS) * H + h;   // (block, kv head) tile index
+  // keys: unit (c, token k) at ((tile * UNITS + c) * BS + k) * 16
+  for (int i = tid; i < BS * UNITS; i += 256) {
+    const int c = i / BS, k = i % BS;
+    const uint16_t* src = key + ((size_t)(ts + k) * H + h) * D + c * X;
+    uint8_t* dst = kc + ((tile * UNITS + c) * BS + k) * 16;
+    if constexpr (CACHE == PKV_BF16) {
+      *(u32x4*)dst = *(const u32x4*)src;
+    } else {
+      const u32x4 ka = *(const u32x4*)src, kb = *(const u32x4*)(src + 8);
+      const uint32_t kw[8] = {ka.x, ka.y, ka.z, ka.w, kb.x, kb.y, kb.z, kb.w};
+      uint32_t kout[4] = {0, 0, 0, 0};
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const uint32_t k0 = f32_to_e4m3(bf16_lo(kw[j]) * k_inv);
+        const uint32_t k1 = f32_to_e4m3(bf16_hi(kw[j]) * k_inv);
+        kout[j / 2] |= (k0 | (k1 << 8)) << (16 * (j % 2));
+      }
+      *(u32x4*)dst = u32x4{kout[0], kout[1], kout[2], kout[3]};
+    }
+  }
+  // values: stage the rows, then write dim row d's tokens PER at a time
+  for (int i = tid; i < BS * (D / 8); i += 256) {
+    const int k = i / (D / 8), q = i % (D / 8);
+    const u32x4 v = *(const u32x4*)(value + ((size_t)(ts + k) * H + h) * D + q * 8);
+    vt[k][4 * q] = v.x;
+    vt[k][4 * q + 1] = v.y;
+    vt[k][4 * q + 2] = v.z;
+    vt[k][4 * q + 3] = v.w;
+  }
+  __syncthreads();
+  for (int i = tid; i < D * (BS / PER); i += 256) {
+    const int d = i / (BS / PER), piece = i % (BS / PER);
+    uint32_t out[4] = {0, 0, 0, 0};
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const uint32_t w = vt[piece * PER + j][d / 2];
+      const float f = (d & 1) ? bf16_hi(w) : bf16_lo(w);
+      const uint32_t code = CACHE == PKV_BF16 ? ((d & 1) ? w >> 16 : w & 0xffffu)
+                                              : f32_to_e4m3(f * v_inv);
+      out[j * E / 4] |= code << (8 * ((j * E) % 4));
+    }
+    *(u32x4*)(vc + ((tile * D + d) * BS + piece * PER) * E) = u32x4{out[0], out[1], out[2], out[3]};
+  }
+}
+
 // Decode-step scatter: one thread per (sequence, kv head, key unit); row s
 // of key/value is sequence s's new token, stored at position lens[s] - 1 in
 // the slot its block table gives.  Sequences of length 0, beyond the table or
@@ -171,6 +279,26 @@ int launch_kv_write(const void* key, const void* value, void* kc, void* vc, cons
   const long n = (long)T * H * (D / X);
   if (n == 0) return 0;
   dim3 grid((unsigned)((n + 255) / 256)), block(256);
+  if (cache != PKV_F32 && src == PKV_BF16) {
+    // block-wise: one workgroup per (BS input rows, kv head)
+    dim3 bgrid((unsigned)((T + BS - 1) / BS), (unsigned)H);
+    auto k16 = (const uint16_t*)key, v16 = (const uint16_t*)value;
+    auto kc8 = (uint8_t*)kc, vc8 = (uint8_t*)vc;
+    auto go = [&](auto kern) {
+      hipLaunchKernelGGL(kern, bgrid, block, 0, st, k16, v16, kc8, vc8, slots, T, H, nb, k_inv,
+                         v_inv);
+    };
+    const bool f8 = cache == PKV_FP8_E4M3;
+    if (D == 128 && BS == 16)
+      f8 ? go(kv_write_block_kernel<PKV_FP8_E4M3, 128, 16>) : go(kv_write_block_kernel<PKV_BF16, 128, 16>);
+    else if (D == 128)
+      f8 ? go(kv_write_block_kernel<PKV_FP8_E4M3, 128, 32>) : go(kv_write_block_kernel<PKV_BF16, 128, 32>);
+    else if (BS == 16)
+      f8 ? go(kv_write_block_kernel<PKV_FP8_E4M3, 64, 16>) : go(kv_write_block_kernel<PKV_BF16, 64, 16>);
+    else
+      f8 ? go(kv_write_block_kernel<PKV_FP8_E4M3, 64, 32>) : go(kv_write_block_kernel<PKV_BF16, 64, 32>);
+    return (int)hipGetLastError();
+  }
   if (cache == PKV_F32)
     hipLaunchKernelGGL((kv_write_kernel<PKV_F32, PKV_F32>), grid, block, 0, st, key, value,
                        (uint8_t*)kc, (uint8_t*)vc, slots, T, H, D, BS, nb, k_inv, v_inv);
