@@ -554,7 +554,7 @@ def main():
     copy_gbps = 2 * copy_n * 5 / (ce0.elapsed_time(ce1) * 1e-3) / 1e9
     del dst_b
     # attainable streaming-read rate of this GPU: the library's read probe
-    # (16-byte non-temporal loads, 32768 workgroups) over 1 GiB
+    # (contiguous 32 KiB runs per workgroup, 16-byte non-temporal loads, 32768 workgroups) over 1 GiB
     sink = torch.zeros(4, dtype=torch.int32, device=dev)
     for _ in range(2):
         pkv.pkv_hbm_read_probe(src_b, sink, 32768)

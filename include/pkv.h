@@ -428,7 +428,8 @@ int paged_kv_gather(void* k_out, void* v_out, const void* key_cache, const void*
 
 /* pkv_hbm_read_probe -- measurement aid: `workgroups` workgroups of 256
  * lanes stream-read `bytes` (rounded down to 16) of device memory at
- * `buffer` with 16-byte loads, eight in flight per lane, and store at most
+ * `buffer`, each workgroup a contiguous 32 KiB run at a time (16-byte
+ * non-temporal loads, eight in flight per lane), and store at most
  * one word to device `sink` (4 bytes).  Timing it gives the attainable HBM
  * read rate, the ceiling for the decode kernel's key/value stream (an HBM
  * bound kernel is measured by bytes moved, "Memory Systems" notes, core idea

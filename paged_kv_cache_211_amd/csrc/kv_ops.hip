@@ -381,23 +381,26 @@ int launch_gather(void* k_out, void* v_out, const void* kc, const void* vc, cons
 // rate of this GPU, the ceiling the decode kernel's KV stream is held to.
 namespace pkv {
 namespace {
+// Streaming read: workgroup g reads one contiguous run of 256 * UNROLL
+// 16-byte units (lane t: units base + t, base + t + 256, ...), all loads in
+// flight before any is used, non-temporal.  Of the layouts measured on
+// MI355X (a grid-stride sweep with 4 to 8 loads per lane, contiguous runs of
+// 4 to 16 loads per lane, plain and non-temporal loads, direct-to-LDS loads)
+// this one streamed fastest.
 template <int UNROLL>
 __global__ __launch_bounds__(256) void read_probe_kernel(const u32x4* __restrict__ src, size_t n16,
                                                          uint32_t* __restrict__ sink) {
-  const size_t tid = (size_t)blockIdx.x * 256 + threadIdx.x;
-  const size_t stride = (size_t)gridDim.x * 256;
+  constexpr size_t RUN = 256 * UNROLL;
   uint32_t acc = 0;
-  size_t i = tid;
-  for (; i + (UNROLL - 1) * stride < n16; i += UNROLL * stride) {
+  for (size_t base = (size_t)blockIdx.x * RUN; base < n16; base += (size_t)gridDim.x * RUN) {
     u32x4 v[UNROLL];
 #pragma unroll
-    for (int u = 0; u < UNROLL; ++u) v[u] = __builtin_nontemporal_load(src + i + u * stride);
+    for (int u = 0; u < UNROLL; ++u) {
+      const size_t i = base + (size_t)u * 256 + threadIdx.x;
+      v[u] = i < n16 ? __builtin_nontemporal_load(src + i) : u32x4{0, 0, 0, 0};
+    }
 #pragma unroll
     for (int u = 0; u < UNROLL; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
-  }
-  for (; i < n16; i += stride) {
-    const u32x4 v = src[i];
-    acc ^= v.x ^ v.y ^ v.z ^ v.w;
   }
   if (acc == 0x9e3779b9u) sink[0] = acc;
 }
