@@ -65,7 +65,7 @@ def _chunk_sets(wl):
             "one row": np.ones_like(L), "ragged 1..33": np.minimum(L, 1 + (np.arange(len(L)) * 8))}
 
 
-@pytest.mark.parametrize("G", [4, 1, 8])
+@pytest.mark.parametrize("G", [4, 1, 8, 3])
 def test_prefill_parity(G):
     wl = _workload(G)
     c = wl.cfg

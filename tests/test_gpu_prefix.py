@@ -54,7 +54,7 @@ def _workload(G=4, seed=104, **kw):
     return synth.make(dataclasses.replace(base, H_q=base.H_kv * G, seed=seed, **kw))
 
 
-@pytest.mark.parametrize("G", [4, 8, 1])
+@pytest.mark.parametrize("G", [4, 8, 1, 3])
 def test_prefix_detected_groups(G):
     wl = _workload(G)
     c = wl.cfg
