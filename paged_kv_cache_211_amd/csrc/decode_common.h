@@ -53,6 +53,91 @@ __device__ __forceinline__ int find_seq(const int32_t* __restrict__ part_off, in
   return s;
 }
 
+// Longest-first dispatch of split-K partitions.  Launch slots are filled
+// in workgroup-id order, so the slot -> partition map decides which work is
+// left for the end of the grid.  Every partition but a sequence's last has P
+// tokens; the last ones vary from 1 to P tokens.  Slots x < F = total_parts -
+// S take the F non-last partitions in sequence order; slot F + r takes the
+// last partition with the r-th most tiles (ties: lower sequence first), so
+// the grid ends on its shortest pieces ("PagedAttention Kernel：大模型推理优化
+// 的显存管理革新" §3.2: pages of uneven length leave units idle unless the
+// work is balanced).  The rank is found with a binary search over tile
+// counts, one ballot per 64 sequences and step, on counts held in registers;
+// with more than 64 * kOrderChunks sequences, or offsets that do not add up,
+// slots map to partitions in sequence order.  Returns the sequence and its
+// partition; the workspace row stays part_off[s] + part.
+constexpr int kOrderChunks = 8;
+
+template <int BS>
+__device__ __forceinline__ void split_slot(const DecodeArgs& a, int x, int lane, int& s,
+                                           int& part) {
+  const int S = a.S;
+  const int F = a.total_parts - S;
+  if (S > 64 * kOrderChunks || F < 0 || a.part_off[S] != a.total_parts) {
+    s = __builtin_amdgcn_readfirstlane(find_seq(a.part_off, S, x, lane));
+    part = x - a.part_off[s];
+    return;
+  }
+  if (x < F) {
+    // sequence s owns non-last slots [part_off[s] - s, part_off[s+1] - s - 1)
+    int c = 0;
+    for (int base = 1; base <= S; base += 64) {
+      const int i = base + lane;
+      const bool le = i <= S && a.part_off[i] - i <= x;
+      c += __popcll(__ballot(le));
+    }
+    s = __builtin_amdgcn_readfirstlane(c);
+    part = x - (a.part_off[s] - s);
+    return;
+  }
+  const int r = x - F;                      // rank among the last partitions, < S
+  const int kmax = a.partition / BS;        // tiles of a full partition
+  int key[kOrderChunks];
+#pragma unroll
+  for (int ch = 0; ch < kOrderChunks; ++ch) {
+    const int i = ch * 64 + lane;
+    key[ch] = -1;                           // no sequence: never counted
+    if (ch * 64 < S && i < S) {
+      int L = a.lens[i];
+      L = L < 0 ? 0 : min(L, a.max_blocks * BS);
+      const int n = a.part_off[i + 1] - a.part_off[i];
+      const int t = L - (n - 1) * a.partition;
+      key[ch] = min(max((t + BS - 1) / BS, 0), kmax);
+    }
+  }
+  auto count_gt = [&](int c) {
+    int n = 0;
+#pragma unroll
+    for (int ch = 0; ch < kOrderChunks; ++ch)
+      if (ch * 64 < S) n += __popcll(__ballot(key[ch] > c));
+    return n;
+  };
+  // smallest c with count_gt(c) <= r: the tile count of the rank-r piece
+  int lo = 0, hi = kmax;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (count_gt(mid) <= r) hi = mid; else lo = mid + 1;
+  }
+  int idx = r - count_gt(lo);               // position among the pieces with lo tiles
+  int found = S - 1;
+#pragma unroll
+  for (int ch = 0; ch < kOrderChunks; ++ch) {
+    if (ch * 64 < S) {
+      const uint64_t m = __ballot(key[ch] == lo);
+      const int n = __popcll(m);
+      if (idx >= 0 && idx < n) {
+        const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                    __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
+        const uint64_t sel = __ballot(key[ch] == lo && below == idx);
+        found = ch * 64 + (int)__builtin_ctzll(sel);
+      }
+      idx -= n;
+    }
+  }
+  s = __builtin_amdgcn_readfirstlane(found);
+  part = a.part_off[s + 1] - a.part_off[s] - 1;
+}
+
 // One 16-byte load of streamed key/value data.
 __device__ __forceinline__ u32x4 load16(const uint8_t* p) {
 #if PKV_DECODE_NT
@@ -89,9 +174,14 @@ __device__ __forceinline__ Work locate(const DecodeArgs& a, int hpw, int lane, i
   int part;
   int tstart = 0;
   if constexpr (SPLIT) {
-    wk.s = __builtin_amdgcn_readfirstlane(find_seq(a.part_off, a.S, item, lane));
+    if (a.t_start) {
+      wk.s = __builtin_amdgcn_readfirstlane(find_seq(a.part_off, a.S, item, lane));
+      part = item - a.part_off[wk.s];
+    } else {
+      split_slot<BS>(a, item, lane, wk.s, part);
+    }
     wk.p0 = a.part_off[wk.s];
-    part = item - wk.p0;
+    wk.item = wk.p0 + part;
     wk.nparts = a.part_off[wk.s + 1] - wk.p0;
     if (a.t_start) {   // shared-prefix suffix pass: always a partial row
       tstart = a.t_start[wk.s];

@@ -229,16 +229,17 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_fp8_kernel(const DecodeAr
   // ---- locate the work item ----
   const int hkv = hg / (G / HPW);
   const int qh0 = hkv * G + (hg % (G / HPW)) * HPW;
-  int s, part, nparts;
+  int s, part, nparts, row;
   if constexpr (SPLIT) {
-    s = __builtin_amdgcn_readfirstlane(find_seq(a.part_off, a.S, item, lane));
+    split_slot<BS>(a, item, lane, s, part);
     const int p0 = a.part_off[s];
-    part = item - p0;
+    row = p0 + part;
     nparts = a.part_off[s + 1] - p0;
   } else {
     s = item;
     part = 0;
     nparts = 1;
+    row = item;
   }
   int L = a.lens[s];
   bool bad = false;
@@ -248,7 +249,7 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_fp8_kernel(const DecodeAr
   const int t1 = SPLIT ? min(L, t0 + a.partition) : L;
   const int jend = (t1 + BS - 1) / BS;
   mfma_item(a, s, hkv, qh0, t0 / BS, jend, t1, bad, !SPLIT || nparts == 1,
-            (size_t)item * a.Hq + qh0, a.ws, a.ws + (size_t)a.total_parts * a.Hq * D, p_lds[w],
+            (size_t)row * a.Hq + qh0, a.ws, a.ws + (size_t)a.total_parts * a.Hq * D, p_lds[w],
             lane, STORE && !bad && L > 0 && t0 < L && t1 == L, L);
 }
 
