@@ -472,6 +472,8 @@ def main():
     q, key, value, slots = step["query"], step["key"], step["value"], step["slots_dev"]
     out = torch.empty_like(q)
     tab, lens = inp["block_tables"], inp["context_lens"]
+    # longest sequence's partition count: sizes the standalone reduce's launch
+    max_parts = int(-(-int(inp["lens_host"].max()) // P)) if P else 0
     if PF:
         n_launch = 3   # the store, the fused prefix + suffix pass, the reduce
     elif SK:
@@ -529,7 +531,7 @@ def main():
             if ev:
                 ev[2].record()
             pkv.paged_attention_splitk_reduce(out, ws, inp["partition_offsets"],
-                                              inp["total_partitions"])
+                                              inp["total_partitions"], max_parts)
         else:
             pkv.paged_attention_decode(out, q, kc, vc, tab, lens, c.scale, c.k_scale, c.v_scale)
             if ev:

@@ -74,7 +74,7 @@ const char* pkv_last_error(void);
 
 /* ABI version of this header (bumped on incompatible change). */
 int pkv_abi_version(void);
-#define PKV_ABI_VERSION 1
+#define PKV_ABI_VERSION 2
 
 /* ---------------------------------------------------------------------------
  * paged_kv_write -- scatter new key/value rows into their slots.
@@ -376,11 +376,14 @@ int paged_attention_prefill(void* out, const void* query, const void* key_cache,
  * pages need the work split): with running maxima m_p (log2 domain), sums
  * l_p and unnormalised outputs o_p, out = sum_p 2^(m_p - M) o_p /
  * sum_p 2^(m_p - M) l_p, M = max_p m_p.  Sequences with one partition are
- * left untouched. */
+ * left untouched.  max_partitions_per_seq: the caller's bound on one
+ * sequence's partition count, or 0 if unknown; it only selects the launch
+ * shape (past 4 partials per piece lane of the reduce, a kernel that holds
+ * more partial rows in flight), and every value gives the same result. */
 int paged_attention_splitk_reduce(void* out, const void* workspace, size_t workspace_bytes,
                                   const int32_t* partition_offsets, int num_seqs,
                                   int num_q_heads, int head_dim, int total_partitions,
-                                  pkv_dtype out_dtype, void* stream);
+                                  int max_partitions_per_seq, pkv_dtype out_dtype, void* stream);
 
 /* ---------------------------------------------------------------------------
  * paged_kv_copy_blocks -- copy whole key and value blocks (all kv heads):

@@ -368,15 +368,16 @@ def paged_attention_prefill(out, query, key_cache, value_cache, block_tables, co
         float(k_scale), float(v_scale), _stream(stream)))
 
 
-def paged_attention_splitk_reduce(out, workspace, partition_offsets, total_partitions, stream=None):
+def paged_attention_splitk_reduce(out, workspace, partition_offsets, total_partitions,
+                                  max_partitions_per_seq=0, stream=None):
     _need(out, "out")
     _need(workspace, "workspace")
     _need(partition_offsets, "partition_offsets", torch.int32)
     S, Hq, D = out.shape
     check(lib().paged_attention_splitk_reduce(
         _ptr(out), _ptr(workspace), workspace.numel() * workspace.element_size(),
-        _ptr(partition_offsets), S, Hq, D, int(total_partitions), cache_dtype_code(out),
-        _stream(stream)))
+        _ptr(partition_offsets), S, Hq, D, int(total_partitions), int(max_partitions_per_seq),
+        cache_dtype_code(out), _stream(stream)))
 
 
 def paged_kv_copy_blocks(key_cache, value_cache, pairs, stream=None):

@@ -66,7 +66,7 @@ SIGNATURES = {
                                             vp, vp, i32, i32, i32, vp, sz, vp]),
     "paged_attention_prefill": (i32, [vp, vp, vp, vp, vp, i32, vp, vp, i32, i32, i32, i32, i32,
                                       i32, i32, f32, i32, i32, f32, f32, vp]),
-    "paged_attention_splitk_reduce": (i32, [vp, vp, sz, vp, i32, i32, i32, i32, i32, vp]),
+    "paged_attention_splitk_reduce": (i32, [vp, vp, sz, vp, i32, i32, i32, i32, i32, i32, vp]),
     "paged_kv_copy_blocks": (i32, [vp, vp, vp, i32, sz, i32, vp]),
     "paged_kv_swap_blocks": (i32, [vp, vp, vp, vp, vp, i32, sz, i32, i32, vp]),
     "pkv_host_device_pointer": (i32, [vp, ctypes.POINTER(vp)]),

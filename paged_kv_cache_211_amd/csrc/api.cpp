@@ -184,7 +184,8 @@ static int decode_common(const DecodeCall& c, bool reduce, void* stream) {
   if (rc || !reduce || c.partition_tokens == 0) return rc;
   return hip_status(launch_splitk_reduce(c.out, a.ws, c.partition_offsets, c.num_seqs,
                                          c.num_q_heads, c.head_dim, c.total_partitions,
-                                         c.q_dtype, stream),
+                                         c.q_dtype, stream, 2,
+                                         max_partitions(a.max_blocks, a.BS, a.partition)),
                     "paged_attention_splitk_reduce launch");
 }
 
@@ -258,7 +259,8 @@ int paged_attention_decode_step(void* out, const void* query, const void* new_ke
   }
   if (rc || partition_tokens == 0) return rc;
   return hip_status(launch_splitk_reduce(out, a.ws, partition_offsets, num_seqs, num_q_heads,
-                                         head_dim, total_partitions, q_dtype, stream),
+                                         head_dim, total_partitions, q_dtype, stream, 2,
+                                         max_partitions(a.max_blocks, a.BS, a.partition)),
                     "paged_attention_splitk_reduce launch");
 }
 
@@ -619,7 +621,7 @@ int paged_attention_prefill(void* out, const void* query, const void* key_cache,
 int paged_attention_splitk_reduce(void* out, const void* workspace, size_t workspace_bytes,
                                   const int32_t* partition_offsets, int num_seqs,
                                   int num_q_heads, int head_dim, int total_partitions,
-                                  pkv_dtype out_dtype, void* stream) {
+                                  int max_partitions_per_seq, pkv_dtype out_dtype, void* stream) {
   if (!out || !workspace || !partition_offsets) return fail(PKV_ERR_INVALID, "null pointer argument");
   if (num_seqs < 0 || num_q_heads <= 0 || total_partitions < num_seqs)
     return fail(PKV_ERR_INVALID, "bad sizes");
@@ -631,7 +633,8 @@ int paged_attention_splitk_reduce(void* out, const void* workspace, size_t works
     return fail(PKV_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", need, workspace_bytes);
   if (num_seqs == 0) return PKV_OK;
   return hip_status(launch_splitk_reduce(out, (const float*)workspace, partition_offsets, num_seqs,
-                                         num_q_heads, head_dim, total_partitions, out_dtype, stream),
+                                         num_q_heads, head_dim, total_partitions, out_dtype, stream,
+                                         2, max_partitions_per_seq),
                     "paged_attention_splitk_reduce launch");
 }
 

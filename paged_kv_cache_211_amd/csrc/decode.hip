@@ -39,6 +39,11 @@ namespace {
 
 using namespace dec;
 
+// Partial rows one thread of the reduce loads at once when a sequence has
+// too many partials for four each (long contexts split into tens of
+// partitions): one memory round trip instead of one per four rows.
+constexpr int kReduceRowsInFlight = 32;
+
 // Combine the n partials of HG query heads of one sequence: partial p of head
 // hh is row row0 + p*pstride + hh of o (D floats each) and of (m, l) (2
 // floats each); out = sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p with
@@ -47,11 +52,11 @@ using namespace dec;
 // of pieces at a time); then PL piece lanes each sum every PL-th piece over
 // the NV = HG*D/4 float4 columns, four pieces' loads in flight, and LDS adds
 // the lanes.  With at most 4*PL pieces (every sequence of up to a few
-// partitions) all loads -- the (m, l) pairs and every partial row -- go out
-// at once: the weights then come from registers and the partial rows are
-// already in flight while the maxima are reduced, one memory round trip in
-// all instead of three.
-template <int D, bool F32OUT, int HG>
+// partitions), or kReduceRowsInFlight*PL, all loads -- the (m, l) pairs and
+// every partial row -- go out at once: the weights then come from registers
+// and the partial rows are already in flight while the maxima are reduced,
+// one memory round trip in all instead of three or more.
+template <int D, bool F32OUT, int HG, bool WIDE = false>
 __device__ __forceinline__ void merge_heads(void* __restrict__ out, size_t oi0,
                                             const float* __restrict__ ws_o,
                                             const float* __restrict__ ws_ml, size_t row0,
@@ -96,7 +101,9 @@ __device__ __forceinline__ void merge_heads(void* __restrict__ out, size_t oi0,
     }
   };
 
-  if (n <= 4 * PL && n <= PSTEP) {
+  // all loads at once: UNR partial rows per piece lane (n <= UNR * PL)
+  auto one_trip = [&](auto unr) {
+    constexpr int UNR = decltype(unr)::value;
     float m_own = -INFINITY, l_own = 0.f;
     if (p_t < n) {
       const f32x2 ml = *(const f32x2*)(ws_ml + (row0 + (size_t)p_t * pstride + hh_t) * 2);
@@ -105,9 +112,9 @@ __device__ __forceinline__ void merge_heads(void* __restrict__ out, size_t oi0,
     }
     const float* op = ws_o + (row0 + hh_e) * D + d4;
     const size_t ps = pstride * D;
-    f32x4 v[4];
+    f32x4 v[UNR];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < UNR; ++u) {
       const int p = pl + u * PL;
       v[u] = p < n ? *(const f32x4*)(op + (size_t)p * ps) : f32x4{0.f, 0.f, 0.f, 0.f};
     }
@@ -123,7 +130,7 @@ __device__ __forceinline__ void merge_heads(void* __restrict__ out, size_t oi0,
     __syncthreads();
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < UNR; ++u) {
       const int p = pl + u * PL;
       if (p < n) {
         const float w = w_lds[p][hh_e];
@@ -135,7 +142,16 @@ __device__ __forceinline__ void merge_heads(void* __restrict__ out, size_t oi0,
     }
     __syncthreads();   // every thread has read red / w_lds before finish reuses red
     finish(acc, p_t < n ? l_own * w_own : 0.f);
+  };
+  if (n <= 4 * PL && n <= PSTEP) {
+    one_trip(std::integral_constant<int, 4>());
     return;
+  }
+  if constexpr (WIDE) {
+    if (n <= kReduceRowsInFlight * PL && n <= PSTEP) {
+      one_trip(std::integral_constant<int, kReduceRowsInFlight>());
+      return;
+    }
   }
 
   float mx = -INFINITY;
@@ -191,8 +207,10 @@ __device__ __forceinline__ void merge_heads(void* __restrict__ out, size_t oi0,
 }
 
 // Split-K reduce: one workgroup per (sequence, group of HG query heads);
-// sequences with one partition are left alone.
-template <int D, bool F32OUT, int HG>
+// sequences with one partition are left alone.  WIDE: sequences of up to
+// kReduceRowsInFlight * PL partials also load everything at once (a larger
+// register budget, so it is launched only where such sequences can occur).
+template <int D, bool F32OUT, int HG, bool WIDE>
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(void* __restrict__ out,
                                                             const float* __restrict__ ws,
                                                             const int32_t* __restrict__ part_off,
@@ -201,7 +219,7 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(void* __restrict__ o
   const int p0 = part_off[s];
   const int n = part_off[s + 1] - p0;
   if (n < min_parts || n <= 0) return;
-  merge_heads<D, F32OUT, HG>(out, ((size_t)s * Hq + qh0) * D, ws, ws + (size_t)total_parts * Hq * D,
+  merge_heads<D, F32OUT, HG, WIDE>(out, ((size_t)s * Hq + qh0) * D, ws, ws + (size_t)total_parts * Hq * D,
                              (size_t)p0 * Hq + qh0, Hq, n);
 }
 
@@ -352,10 +370,13 @@ int launch_sk_reduce(const DecodeArgs& a0, void* stream) {
 }
 
 int launch_splitk_reduce(void* out, const float* ws, const int32_t* part_off, int S, int Hq, int D,
-                         int total_parts, pkv_dtype out_dtype, void* stream, int min_parts) {
+                         int total_parts, pkv_dtype out_dtype, void* stream, int min_parts,
+                         int max_rows) {
   hipStream_t st = (hipStream_t)stream;
   const int cap = 256 / D;   // heads per workgroup: 64 float4 columns at most
   const int hgs = Hq % cap == 0 ? cap : Hq % 2 == 0 ? 2 : 1;
+  const int pl = 256 / (hgs * D / 4);   // piece lanes of merge_heads
+  const bool wide = max_rows > 4 * pl;
   dim3 grid(S, Hq / hgs), block(256);
   const bool f32 = out_dtype == PKV_F32;
   return with_hg(hgs, [&](auto hg) {
@@ -363,10 +384,14 @@ int launch_splitk_reduce(void* out, const float* ws, const int32_t* part_off, in
     auto go = [&](auto kern) {
       hipLaunchKernelGGL(kern, grid, block, 0, st, out, ws, part_off, Hq, total_parts, min_parts);
     };
-    if (D == 64)
-      f32 ? go(splitk_reduce_kernel<64, true, HG>) : go(splitk_reduce_kernel<64, false, HG>);
-    else
-      f32 ? go(splitk_reduce_kernel<128, true, HG>) : go(splitk_reduce_kernel<128, false, HG>);
+    auto pick = [&](auto w) {
+      constexpr bool W = decltype(w)::value;
+      if (D == 64)
+        f32 ? go(splitk_reduce_kernel<64, true, HG, W>) : go(splitk_reduce_kernel<64, false, HG, W>);
+      else
+        f32 ? go(splitk_reduce_kernel<128, true, HG, W>) : go(splitk_reduce_kernel<128, false, HG, W>);
+    };
+    wide ? pick(std::true_type()) : pick(std::false_type());
     return (int)hipGetLastError();
   });
 }

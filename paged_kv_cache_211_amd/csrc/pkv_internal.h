@@ -1,6 +1,7 @@
 // Internal declarations shared by the host-side translation units of libpkv.
 #pragma once
 
+#include <algorithm>
 #include <cstddef>
 #include <cstdint>
 
@@ -118,9 +119,19 @@ int launch_decode_mfma_sk(const DecodeArgs& a, void* stream, bool store);
 int decode_mfma_sk_workers();
 // min_parts: sequences with fewer rows are left alone (2 for split-K, whose
 // single-partition sequences write their output directly; 1 when every
-// sequence has partials only).
+// sequence has partials only).  max_rows: an upper bound on one sequence's
+// rows (0 = small); past four per piece lane the kernel that holds more rows
+// in flight is launched (either kernel is correct for any count).
 int launch_splitk_reduce(void* out, const float* ws, const int32_t* part_off, int S, int Hq, int D,
-                         int total_parts, pkv_dtype out_dtype, void* stream, int min_parts = 2);
+                         int total_parts, pkv_dtype out_dtype, void* stream, int min_parts = 2,
+                         int max_rows = 0);
+// Upper bound on the split-K partitions of one sequence whose table holds
+// max_blocks blocks of bs tokens.
+inline int max_partitions(int max_blocks, int bs, int partition) {
+  if (partition <= 0) return 1;
+  const long long t = (long long)max_blocks * bs;
+  return (int)std::min<long long>((t + partition - 1) / partition, 1 << 30);
+}
 bool decode_supported(pkv_dtype q, pkv_dtype kv, int D, int BS, int G);
 
 int launch_kv_write(const void* key, const void* value, void* kc, void* vc, const int32_t* slots,

@@ -130,6 +130,18 @@ def test_partials_plus_reduce_equals_decode():
     paged_attention_splitk_reduce(out, ws, inp["partition_offsets"], inp["total_partitions"])
     torch.cuda.synchronize()
     assert np.array_equal(out.double().cpu().numpy(), whole)
+    # a large bound selects the reduce kernel with more rows in flight; with
+    # these few partials it sums the same terms in the same order
+    out.fill_(float("nan"))
+    paged_attention_decode_partials(out, step["query"], cache.key_cache, cache.value_cache,
+                                    inp["block_tables"], inp["context_lens"], c.scale,
+                                    k_scale=c.k_scale, v_scale=c.v_scale, partition_tokens=512,
+                                    partition_offsets=inp["partition_offsets"],
+                                    total_partitions=inp["total_partitions"], workspace=ws)
+    paged_attention_splitk_reduce(out, ws, inp["partition_offsets"], inp["total_partitions"],
+                                  max_partitions_per_seq=1000)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.double().cpu().numpy(), whole)
 
 
 def test_block_permutation_is_bit_identical():

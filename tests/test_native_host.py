@@ -38,7 +38,7 @@ def test_every_header_symbol_is_exported(pkv):
     for n in names:
         assert hasattr(raw, n), n
     assert sorted(_native.SIGNATURES) == names
-    assert _native.lib().pkv_abi_version() == 1
+    assert _native.lib().pkv_abi_version() == 2
 
 
 class Both:
@@ -300,7 +300,7 @@ def test_decode_argument_validation_needs_no_gpu(pkv):
     w = L.paged_kv_write(fake, fake, fake, fake, fake, 4, 2, 128, 16, 10, 0, 1, 1.0, 1.0, None)
     assert w == -2
     assert L.paged_kv_copy_blocks(fake, fake, fake, 3, 100, 10, None) == -1
-    assert L.paged_attention_splitk_reduce(fake, fake, 16, fake, 2, 8, 128, 2, 1, None) == -3
+    assert L.paged_attention_splitk_reduce(fake, fake, 16, fake, 2, 8, 128, 2, 0, 1, None) == -3
 
     # chunked prefill: the same host checks, bf16 / head_dim 128 / block 16 only
     def pre(**kw):
