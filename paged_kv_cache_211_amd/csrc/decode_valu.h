@@ -16,8 +16,9 @@
 //   * key layout [D/X][BS][X] puts one token in each lane with X dims per
 //     load, so q.k is a per-lane dot product over NLOAD*X dims followed by a
 //     reduction across the 64/BS lanes holding the same token;
-//   * one-pass online softmax per tile (running max m, sum l, rescale of the
-//     accumulator once per tile), in the log2 domain;
+//   * one-pass online softmax per tile in the log2 domain (running max m,
+//     sum l; the accumulator is rescaled only when a tile's max exceeds the
+//     reference by more than 2^8);
 //   * probabilities go through LDS to the value layout [D][BS], where each
 //     lane holds X consecutive tokens of one dim per load, so PV is a dot
 //     product over token pairs.
@@ -207,22 +208,41 @@ struct ValuHeads {
     for (int hh = 0; hh < HPW; ++hh) sc[hh] = token_sum<BS>(sc[hh]);
 
     // ---- online softmax over this tile ----
+    // Probabilities are taken against a reference max m_run that moves only
+    // when a tile's max exceeds it by more than 2^8 (then l and the
+    // accumulator are rescaled: a rare, wave-uniform branch instead of a
+    // correction factor and a rescale every tile).  p <= 2^8 keeps bf16 and
+    // fp32 in range, and O / l does not depend on the reference.
     const int tile_t0 = j * BS;
     const bool valid = tile_t0 + tk < t1;
-    float cfac[HPW];
+    float z[HPW], tmax[HPW];
+    bool grow = false;
 #pragma unroll
     for (int hh = 0; hh < HPW; ++hh) {
-      const float z = valid ? sc[hh] * qk_mult : -INFINITY;
-      const float mnew = fmaxf(m_run[hh], tile_max<BS>(z));
-      cfac[hh] = __builtin_amdgcn_exp2f(m_run[hh] - mnew);
-      float p = __builtin_amdgcn_exp2f(z - mnew);
-      m_run[hh] = mnew;
+      z[hh] = valid ? sc[hh] * qk_mult : -INFINITY;
+      tmax[hh] = tile_max<BS>(z[hh]);
+      grow |= tmax[hh] > m_run[hh] + 8.0f;
+    }
+    if (__ballot(grow)) {
+#pragma unroll
+      for (int hh = 0; hh < HPW; ++hh) {
+        const bool up = tmax[hh] > m_run[hh] + 8.0f;
+        const float c = up ? __builtin_amdgcn_exp2f(m_run[hh] - tmax[hh]) : 1.0f;
+        m_run[hh] = up ? tmax[hh] : m_run[hh];
+        l_run[hh] *= c;
+#pragma unroll
+        for (int l = 0; l < NLOAD; ++l) acc[hh][l] *= c;
+      }
+    }
+#pragma unroll
+    for (int hh = 0; hh < HPW; ++hh) {
+      float p = __builtin_amdgcn_exp2f(z[hh] - m_run[hh]);
       uint16_t pb = 0;
       if constexpr (!F32) {
         pb = cvt_bf16(p);
         p = bf16_to_f32(pb);
       }
-      l_run[hh] = l_run[hh] * cfac[hh] + p;
+      l_run[hh] += p;
       if (lane < BS) {
         if constexpr (F32)
           prow[hh][lane] = p;
@@ -235,11 +255,6 @@ struct ValuHeads {
     // ---- PV: acc[hh][dim] += sum over this lane's X tokens ----
     const int nvalid = t1 - tile_t0;  // tokens of this tile inside the partition
     const bool tail = nvalid < BS;
-#pragma unroll
-    for (int hh = 0; hh < HPW; ++hh) {
-#pragma unroll
-      for (int l = 0; l < NLOAD; ++l) acc[hh][l] *= cfac[hh];
-    }
     if constexpr (F32) {
       float pv[HPW][4];
 #pragma unroll
