@@ -38,6 +38,16 @@ constexpr int kSkWaves = PKV_SK_WAVES;            // waves per workgroup, stream
 constexpr bool kQLds = PKV_DECODE_QLDS;           // vector-ALU kernels: query rows in LDS
 
 constexpr int kBufs = PKV_DECODE_DEPTH + 1;      // tiles in registers per wave (VALU kernel)
+#ifndef PKV_DECODE_DEPTH_1H
+#define PKV_DECODE_DEPTH_1H 2
+#endif
+// Tiles in registers per wave of the split-K vector-ALU kernel holding HPW
+// query heads over tiles of TILE bytes: one more when a wave holds a single
+// head, whose query takes few registers, and a tile is at most 4 KiB (32
+// VGPRs for its key and value loads).  One kv head per query head: 3 tiles
+// in flight measured 2.5% faster; 4 heads per wave: slower, at 244 VGPRs.
+template <int HPW, int TILE>
+constexpr int valu_bufs() { return HPW == 1 && TILE <= 4096 ? PKV_DECODE_DEPTH_1H + 1 : kBufs; }
 constexpr int kMfmaBufs = PKV_MFMA_DEPTH + 1;    // same, matrix-core kernel
 
 // Number of i in [1, S] with part_off[i] <= idx, i.e. the sequence owning

@@ -555,14 +555,14 @@ int launch_t(const DecodeArgs& a, bool store, hipStream_t st) {
   dim3 grid((a.partition > 0 ? a.total_parts : a.S) * a.Hkv * groups);
   if (a.partition > 0) {
     if (store)
-      hipLaunchKernelGGL((decode_kernel<KV, D, BS, HPW, kWaves, kBufs, true, true>), grid, block, 0, st, a);
+      hipLaunchKernelGGL((decode_kernel<KV, D, BS, HPW, kWaves, valu_bufs<HPW, Geo<KV, D, BS>::TILE>(), true, true>), grid, block, 0, st, a);
     else
-      hipLaunchKernelGGL((decode_kernel<KV, D, BS, HPW, kWaves, kBufs, true, false>), grid, block, 0, st, a);
+      hipLaunchKernelGGL((decode_kernel<KV, D, BS, HPW, kWaves, valu_bufs<HPW, Geo<KV, D, BS>::TILE>(), true, false>), grid, block, 0, st, a);
   } else {
     if (store)
-      hipLaunchKernelGGL((decode_kernel<KV, D, BS, HPW, kWaves, kBufs, false, true>), grid, block, 0, st, a);
+      hipLaunchKernelGGL((decode_kernel<KV, D, BS, HPW, kWaves, valu_bufs<HPW, Geo<KV, D, BS>::TILE>(), false, true>), grid, block, 0, st, a);
     else
-      hipLaunchKernelGGL((decode_kernel<KV, D, BS, HPW, kWaves, kBufs, false, false>), grid, block, 0, st, a);
+      hipLaunchKernelGGL((decode_kernel<KV, D, BS, HPW, kWaves, valu_bufs<HPW, Geo<KV, D, BS>::TILE>(), false, false>), grid, block, 0, st, a);
   }
   return (int)hipGetLastError();
 }
