@@ -83,12 +83,32 @@ void prefill_kernel(const PrefillArgs a) {
   // serves one head of every sequence and gets the same amount of work
   // whatever the length mix (a contiguous eighth of the units per XCD left
   // one XCD with 1.28x the mean work on the 16-sequence prefill workload).
+  // Within an XCD the units run longest first: with at most 64 sequences,
+  // unit slot v takes kv head v % H_kv of the sequence with the (v / H_kv)-th
+  // most visible (row, token) pairs, C (2L - C + 1) / 2 (ties: lower index),
+  // so each XCD ends on its cheapest units.
   const int nunits = a.total_wg / a.qblocks;
   const int k = blockIdx.x / 8;
-  const int sh = (int)(blockIdx.x % 8) + 8 * (k / a.qblocks);
+  const int vslot = (int)(blockIdx.x % 8) + 8 * (k / a.qblocks);
   const int qb = k % a.qblocks;
-  if (sh >= nunits) return;   // whole workgroup
-  const int hkv = sh % a.Hkv, s = sh / a.Hkv;
+  if (vslot >= nunits) return;   // whole workgroup
+  const int hkv = vslot % a.Hkv;
+  int s = vslot / a.Hkv;
+  if (a.S <= 64) {
+    float key = -1.f;
+    if (lane < a.S) {
+      const float Li = (float)a.lens[lane];
+      const float Ci = (float)(a.q_start[lane + 1] - a.q_start[lane]);
+      key = fmaxf(Ci * (2.f * Li - Ci + 1.f), 0.f);
+    }
+    int rank = 0;
+    for (int j = 0; j < a.S; ++j) {
+      const float kj = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(key), j));
+      rank += (kj > key || (kj == key && j < lane)) ? 1 : 0;
+    }
+    const uint64_t hit = __ballot(lane < a.S && rank == s);
+    s = __builtin_amdgcn_readfirstlane(hit ? (int)__builtin_ctzll(hit) : s);
+  }
   const int G = a.Hq / a.Hkv;
   const int r0q = as_const(a.q_start)[s];
   const int C = as_const(a.q_start)[s + 1] - r0q;
