@@ -83,6 +83,27 @@ def test_prefill_parity(G):
         assert err <= tol, (name, err)
 
 
+@pytest.mark.parametrize("S, tie", [(40, False), (40, True), (70, False)])
+def test_prefill_many_sequences_dispatch_order(S, tie):
+    """Units of each XCD run longest first (a device-side rank of up to 64
+    sequences, ties by index) and in index order past 64 sequences: every row
+    of every sequence against the oracle, with drawn lengths and chunks, and
+    with all sequences alike (every key tied)."""
+    wl = _workload(4, S=S, seed=300 + S + int(tie), len_range=(96, 96) if tie else (20, 160))
+    c = wl.cfg
+    st, _ = replay.build(wl)
+    cache, _ = H.build(wl, poison=True)
+    chunks = np.full(c.S, 32) if tie else synth.prefill_chunks(wl)
+    _case(f"prefill dispatch order S={S} tie={tie} rows={int(chunks.sum())}")
+    q_bits = synth.prefill_queries(wl, chunks)
+    ref = oracle_prefill(wl, st, chunks, q_bits)
+    got, _, _ = gpu_prefill(cache, wl, chunks, q_bits)
+    assert np.isfinite(got).all()
+    err = np.abs(got - ref).max()
+    print(f"  max abs err {err:.3e}", flush=True)
+    assert err <= H.TOL[c.kv_dtype]
+
+
 def test_prefill_one_row_chunks_match_decode():
     """A chunk of one row is a decode step: same output as the decode kernel
     for the same query rows, within the tolerance of each against the oracle."""
