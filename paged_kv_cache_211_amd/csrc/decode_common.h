@@ -73,9 +73,10 @@ __device__ __forceinline__ int find_seq(const int32_t* __restrict__ part_off, in
 // 的显存管理革新" §3.2: pages of uneven length leave units idle unless the
 // work is balanced).  The rank is found with a binary search over tile
 // counts, one ballot per 64 sequences and step, on counts held in registers;
-// with more than 64 * kOrderChunks sequences, or offsets that do not add up,
-// slots map to partitions in sequence order.  Returns the sequence and its
-// partition; the workspace row stays part_off[s] + part.
+// with more than 64 * kOrderChunks sequences, or offsets that do not add up
+// or give a sequence no partition, slots map to partitions in sequence
+// order.  Returns the sequence and its partition; the workspace row stays
+// part_off[s] + part.
 constexpr int kOrderChunks = 8;
 
 template <int BS>
@@ -83,18 +84,27 @@ __device__ __forceinline__ void split_slot(const DecodeArgs& a, int x, int lane,
                                            int& part) {
   const int S = a.S;
   const int F = a.total_parts - S;
-  if (S > 64 * kOrderChunks || F < 0 || a.part_off[S] != a.total_parts) {
+  auto in_order = [&] {
     s = __builtin_amdgcn_readfirstlane(find_seq(a.part_off, S, x, lane));
     part = x - a.part_off[s];
+  };
+  if (S > 64 * kOrderChunks || F < 0 || a.part_off[S] != a.total_parts) {
+    in_order();
     return;
   }
   if (x < F) {
     // sequence s owns non-last slots [part_off[s] - s, part_off[s+1] - s - 1)
     int c = 0;
+    bool empty = false;   // a sequence without partitions
     for (int base = 1; base <= S; base += 64) {
       const int i = base + lane;
-      const bool le = i <= S && a.part_off[i] - i <= x;
-      c += __popcll(__ballot(le));
+      const int hi = i <= S ? a.part_off[i] : 0, lo = i <= S ? a.part_off[i - 1] : 0;
+      c += __popcll(__ballot(i <= S && hi - i <= x));
+      empty |= __ballot(i <= S && hi - lo < 1) != 0;
+    }
+    if (empty) {
+      in_order();
+      return;
     }
     s = __builtin_amdgcn_readfirstlane(c);
     part = x - (a.part_off[s] - s);
@@ -103,17 +113,24 @@ __device__ __forceinline__ void split_slot(const DecodeArgs& a, int x, int lane,
   const int r = x - F;                      // rank among the last partitions, < S
   const int kmax = a.partition / BS;        // tiles of a full partition
   int key[kOrderChunks];
+  bool empty = false;
 #pragma unroll
   for (int ch = 0; ch < kOrderChunks; ++ch) {
     const int i = ch * 64 + lane;
     key[ch] = -1;                           // no sequence: never counted
+    int n = 1;
     if (ch * 64 < S && i < S) {
       int L = a.lens[i];
       L = L < 0 ? 0 : min(L, a.max_blocks * BS);
-      const int n = a.part_off[i + 1] - a.part_off[i];
+      n = a.part_off[i + 1] - a.part_off[i];
       const int t = L - (n - 1) * a.partition;
       key[ch] = min(max((t + BS - 1) / BS, 0), kmax);
     }
+    if (ch * 64 < S) empty |= __ballot(n < 1) != 0;
+  }
+  if (empty) {
+    in_order();
+    return;
   }
   auto count_gt = [&](int c) {
     int n = 0;
