@@ -210,7 +210,8 @@ __device__ __forceinline__ void mfma_item(const DecodeArgs& a, int s, int hkv, i
 // group of 8 query heads per kv head): the wave that reads a sequence's last
 // block first stores the sequence's new token; it is that block's only reader.
 template <int NW, bool SPLIT, bool STORE = false>
-__global__ __launch_bounds__(NW * 64) void decode_mfma_fp8_kernel(const DecodeArgs a) {
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
+void decode_mfma_fp8_kernel(const DecodeArgs a) {
   constexpr int BS = kBS, HPW = kHPW, D = kD;
   __shared__ uint16_t p_lds[NW][HPW][BS];
 
