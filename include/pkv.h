@@ -100,18 +100,32 @@ int paged_kv_write(const void* key, const void* value, void* key_cache, void* va
                    float k_scale, float v_scale, void* stream);
 
 /* ---------------------------------------------------------------------------
- * Split-K partitions.  With partition_tokens = P > 0, sequence s is cut into
+ * Split-K partitions ("PagedAttention Kernel：大模型推理优化的显存管理革新"
+ * §3.2: sequences of very different lengths leave compute units idle unless
+ * the work is cut into balanced pieces; here a long sequence's blocks are cut
+ * into partitions that separate workgroups decode, and a reduce combines
+ * them).  With partition_tokens = P > 0, sequence s is cut into
  * n_s = max(1, ceil(context_lens[s] / P)) partitions of logical tokens
  * [p*P, (p+1)*P); partition_offsets[s] = sum_{r<s} n_r, partition_offsets[S]
- * = total_partitions.  paged_attention_partition_offsets computes that on the
- * host from host-side lengths.
+ * = total_partitions.
+ *
+ * paged_attention_partition_offsets computes those offsets on the host.
+ *  context_lens_host [num_seqs] int32 (host, caller-owned, read only)
+ *  offsets_host_out  [num_seqs + 1] int32 (host, caller-owned, written)
+ *  *total_partitions_out  (host, may be NULL) = offsets_host_out[num_seqs]
+ * Returns PKV_ERR_INVALID for a null array, P <= 0, a negative length or a
+ * total above INT32_MAX (nothing useful is written then).  Touches no device.
  * ------------------------------------------------------------------------- */
 int paged_attention_partition_offsets(const int32_t* context_lens_host, int num_seqs,
                                       int partition_tokens, int32_t* offsets_host_out,
                                       int* total_partitions_out);
 
-/* Workspace bytes paged_attention_decode needs for total_partitions
- * partitions: total_partitions * num_q_heads * (head_dim + 2) * 4. */
+/* Workspace bytes the split-K decode needs for total_partitions partitions
+ * (the partials of "PagedAttention Kernel：大模型推理优化的显存管理革新"
+ * §3.2's split work, combined by the reduce): one fp32 row of head_dim
+ * unnormalised outputs and one (max, sum) pair per (partition, query head),
+ * total_partitions * num_q_heads * (head_dim + 2) * 4 bytes.  Returns 0 when
+ * an argument is not positive.  Pure arithmetic, no device access. */
 size_t paged_attention_workspace_bytes(int total_partitions, int num_q_heads, int head_dim);
 
 /* ---------------------------------------------------------------------------
@@ -419,11 +433,22 @@ int paged_kv_swap_blocks(void* dst_key_cache, void* dst_value_cache, const void*
 int pkv_host_device_pointer(const void* host, void** device_out);
 
 /* paged_kv_gather -- read every sequence back through its block table into
- * dense rows: k_out, v_out [cu_ctx[num_seqs]][num_kv_heads][head_dim] of
- * cache_dtype bits, sequence s occupying rows cu_ctx[s] .. cu_ctx[s+1]-1
- * (cu_ctx: device int32 [num_seqs+1], prefix sum of lengths; total_tokens
- * = its last entry, passed from the host).  A test aid for bit-exact checks
- * of the cache contents. */
+ * dense rows, i.e. the contiguous cache the block table makes the scattered
+ * blocks look like ("Day 6/90 of Inference Engineering", PagedAttention
+ * notes: the block table maps logical blocks to physical ones).  A test aid
+ * for bit-exact checks of the cache contents.
+ *  k_out, v_out   [total_tokens][num_kv_heads][head_dim] of cache_dtype bits
+ *                 (device, caller-owned, written); sequence s occupies rows
+ *                 cu_ctx[s] .. cu_ctx[s+1]-1, token t of it in row
+ *                 cu_ctx[s] + t, read from block block_tables[s][t / bs],
+ *                 slot t % bs
+ *  cu_ctx         [num_seqs + 1] int32 (device): 0, then running sums of the
+ *                 lengths; total_tokens = cu_ctx[num_seqs], passed from the
+ *                 host (it sizes the launch)
+ *  block_tables   [num_seqs][max_blocks_per_seq] int32 (device)
+ * Host-visible errors as paged_kv_write; a block id outside [0, num_blocks),
+ * or a position past the table width, gives rows of zero bits instead of a
+ * read outside the pool or the table. */
 int paged_kv_gather(void* k_out, void* v_out, const void* key_cache, const void* value_cache,
                     const int32_t* block_tables, int max_blocks_per_seq, const int32_t* cu_ctx,
                     int num_seqs, int total_tokens, int num_kv_heads, int head_dim, int block_size,
@@ -479,8 +504,10 @@ int pkv_hbm_read_probe(const void* buffer, size_t bytes, void* sink, int workgro
  * ------------------------------------------------------------------------- */
 typedef struct pkv_alloc pkv_alloc;
 
-/* NULL on invalid arguments (see pkv_last_error). free_order, if not NULL,
- * must be a permutation of 0..num_blocks-1 (host memory, copied). */
+/* NULL on invalid arguments (see pkv_last_error): num_blocks or block_size
+ * not positive, num_blocks * block_size above INT32_MAX (slot ids are int32),
+ * or a free_order that is not a permutation of 0..num_blocks-1 (host memory,
+ * copied). */
 pkv_alloc* pkv_alloc_create(int num_blocks, int block_size, const int32_t* free_order);
 void pkv_alloc_destroy(pkv_alloc* a);
 int pkv_alloc_add_seq(pkv_alloc* a, int64_t seq);
@@ -497,7 +524,11 @@ int pkv_alloc_block_table(const pkv_alloc* a, int64_t seq, int32_t* out, int cap
  * pad; fails if a table is wider than width. */
 int pkv_alloc_fill_tables(const pkv_alloc* a, const int64_t* seqs, int num_seqs, int32_t* out,
                           int width, int32_t pad);
-/* Length in tokens of seq, or a negative error. */
+/* Length in tokens of seq, or a negative error (PKV_ERR_SEQ for an unknown
+ * sequence).  A length never exceeds num_blocks * block_size, which
+ * pkv_alloc_create keeps within INT32_MAX, so the int result is exact.
+ * pkv_alloc_seq_len is the same value as int64_t. */
+int pkv_alloc_len(const pkv_alloc* a, int64_t seq);
 int64_t pkv_alloc_seq_len(const pkv_alloc* a, int64_t seq);
 /* Refcount of a block, or a negative error. */
 int pkv_alloc_refcount(const pkv_alloc* a, int32_t block);

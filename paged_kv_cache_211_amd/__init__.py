@@ -494,7 +494,7 @@ class BlockAllocator:
         check(lib().pkv_alloc_free_seq(self._h, int(seq)))
 
     def seq_len(self, seq: int) -> int:
-        r = lib().pkv_alloc_seq_len(self._h, int(seq))
+        r = lib().pkv_alloc_len(self._h, int(seq))
         if r < 0:
             check(int(r))
         return int(r)

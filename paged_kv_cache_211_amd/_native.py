@@ -80,6 +80,7 @@ SIGNATURES = {
     "pkv_alloc_free_seq": (i32, [vp, i64]),
     "pkv_alloc_block_table": (i32, [vp, i64, pi32, i32, ctypes.POINTER(i32)]),
     "pkv_alloc_fill_tables": (i32, [vp, pi64, i32, pi32, i32, ctypes.c_int32]),
+    "pkv_alloc_len": (i32, [vp, i64]),
     "pkv_alloc_seq_len": (i64, [vp, i64]),
     "pkv_alloc_refcount": (i32, [vp, ctypes.c_int32]),
     "pkv_alloc_num_free": (i32, [vp]),

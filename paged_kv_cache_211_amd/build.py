@@ -22,7 +22,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libpkv.so")
 ARCH = "gfx950"
 
-SOURCES = ["api.cpp", "allocator.cpp", "kv_ops.hip", "decode.hip", "decode_f32.hip",
+SOURCES = ["api.cpp", "host.cpp", "allocator.cpp", "kv_ops.hip", "decode.hip", "decode_f32.hip",
            "decode_bf16.hip", "decode_fp8.hip", "decode_mfma.hip", "decode_prefix.hip",
            "prefill.hip"]
 

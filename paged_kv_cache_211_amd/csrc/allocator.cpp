@@ -60,6 +60,12 @@ pkv_alloc* pkv_alloc_create(int num_blocks, int block_size, const int32_t* free_
     pkv::fail(PKV_ERR_INVALID, "num_blocks and block_size must be positive");
     return nullptr;
   }
+  // slot ids (block * block_size + offset) are int32 in every interface
+  if ((int64_t)num_blocks * block_size > (int64_t)INT32_MAX) {
+    pkv::fail(PKV_ERR_INVALID, "num_blocks * block_size = %lld exceeds int32 slot ids",
+              (long long)num_blocks * block_size);
+    return nullptr;
+  }
   auto* a = new pkv_alloc;
   a->num_blocks = num_blocks;
   a->bs = block_size;
@@ -315,6 +321,11 @@ int64_t pkv_alloc_seq_len(const pkv_alloc* a, int64_t seq) {
   auto it = a->seqs.find(seq);
   if (it == a->seqs.end()) return no_seq(seq);
   return it->second.len;
+}
+
+int pkv_alloc_len(const pkv_alloc* a, int64_t seq) {
+  const int64_t n = pkv_alloc_seq_len(a, seq);
+  return (int)n;   // an error code, or a length <= num_blocks * block_size <= INT32_MAX
 }
 
 int pkv_alloc_refcount(const pkv_alloc* a, int32_t block) {

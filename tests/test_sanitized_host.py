@@ -1,0 +1,334 @@
+"""The library's host code under AddressSanitizer and UndefinedBehaviorSanitizer.
+
+allocator.cpp and host.cpp (the block allocator and the host-side planning
+of the C ABI: partition offsets, tile offsets, the shared-prefix plan) are
+compiled with g++ -fsanitize=address,undefined, no HIP involved, together
+with tests/native/alloc_replay.cpp, a driver that reads one call per line.
+The same comparisons with the specification model that run against the
+built library in test_native_host.py run here against the sanitized build:
+the hand trace, random operation sequences, every sequence of up to six
+operations on a four-block pool (five with swaps), and the planning helpers
+on random and edge-case inputs.  Any out-of-bounds access, use after free,
+leak, signed overflow or other undefined behaviour aborts the driver and
+fails the test.
+"""
+
+import json
+import os
+import shutil
+import subprocess
+
+import numpy as np
+import pytest
+
+from oracle.alloc_model import AllocError, AllocModel
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "paged_kv_cache_211_amd", "csrc")
+
+
+@pytest.fixture(scope="module")
+def driver(tmp_path_factory):
+    gxx = shutil.which("g++")
+    if gxx is None:
+        pytest.skip("g++ not available")
+    exe = str(tmp_path_factory.mktemp("asan") / "alloc_replay")
+    cmd = [gxx, "-std=c++17", "-O1", "-g", "-fno-omit-frame-pointer",
+           "-fsanitize=address,undefined", "-fno-sanitize-recover=all",
+           "-D_GLIBCXX_ASSERTIONS", "-I", os.path.join(ROOT, "include"), "-I", CSRC,
+           os.path.join(CSRC, "allocator.cpp"), os.path.join(CSRC, "host.cpp"),
+           os.path.join(ROOT, "tests", "native", "alloc_replay.cpp"), "-o", exe]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=1:abort_on_error=1",
+               UBSAN_OPTIONS="print_stacktrace=1:halt_on_error=1")
+    p = subprocess.Popen([exe], stdin=subprocess.PIPE, stdout=subprocess.PIPE,
+                         stderr=subprocess.PIPE, text=True, bufsize=1, env=env)
+    d = Driver(p)
+    yield d
+    p.stdin.close()
+    err = p.stderr.read()
+    rc = p.wait(timeout=60)
+    assert rc == 0 and "ERROR: AddressSanitizer" not in err and "runtime error" not in err, err
+
+
+class Driver:
+    def __init__(self, p):
+        self.p = p
+
+    def call(self, *words):
+        self.p.stdin.write(" ".join(str(int(w)) if not isinstance(w, str) else w
+                                    for w in words) + "\n")
+        line = self.p.stdout.readline()
+        if not line:
+            raise AssertionError("sanitized driver died: " + self.p.stderr.read())
+        return [int(x) if x.lstrip("-").isdigit() else x for x in line.split()]
+
+
+def take(v, i):
+    """A length-prefixed list at v[i]: (list, next index)."""
+    n = v[i]
+    return v[i + 1:i + 1 + n], i + 1 + n
+
+
+class SanAlloc:
+    """The sanitized allocator behind the same calls as AllocModel."""
+
+    def __init__(self, drv, nb, bs, order):
+        self.d = drv
+        o = [] if order is None else [int(x) for x in order]
+        r = self.d.call("new", nb, bs, len(o), *o)
+        if r[1] != 0:
+            raise AllocError(r[1], "create failed")
+
+    def _rc(self, r):
+        if r[1] != 0:
+            raise AllocError(r[1], "")
+        return r
+
+    def add_seq(self, s): self._rc(self.d.call("add", s))
+    def fork(self, p, c): self._rc(self.d.call("fork", p, c))
+    def free_seq(self, s): self._rc(self.d.call("free", s))
+    def touch(self, s): self._rc(self.d.call("touch", s))
+    def set_host_pool(self, n): self._rc(self.d.call("pool", n))
+
+    def append(self, s, n):
+        r = self._rc(self.d.call("append", s, n))
+        slots, i = take(r, 2)
+        cow, _ = take(r, i)
+        return slots, [(cow[2 * k], cow[2 * k + 1]) for k in range(len(cow) // 2)]
+
+    def _swap(self, w, s):
+        r = self._rc(self.d.call(w, s))
+        p, _ = take(r, 2)
+        return [(p[2 * k], p[2 * k + 1]) for k in range(len(p) // 2)]
+
+    def swap_out(self, s): return self._swap("out", s)
+    def swap_in(self, s): return self._swap("in", s)
+
+    def lru(self):
+        return self._rc(self.d.call("lru"))[2]
+
+    def state(self, seqs):
+        r = self.d.call("state", len(seqs), *seqs)
+        assert r[0] == "free"
+        free, i = take(r, 1)
+        assert r[i] == "ref"
+        ref, i = take(r, i + 1)
+        assert r[i] == "host"
+        host = r[i + 1]
+        i += 2
+        per = {}
+        while i < len(r):
+            assert r[i] == "seq"
+            s, ln, ln64, sw = r[i + 1:i + 5]
+            tab, i = take(r, i + 5)
+            assert ln == ln64
+            per[s] = (ln, bool(sw), tab)
+        return free, ref, host, per
+
+
+def same(san, model, op, *args):
+    try:
+        r_m, err_m = getattr(model, op)(*args), None
+    except AllocError as e:
+        r_m, err_m = None, e.code
+    try:
+        r_s, err_s = getattr(san, op)(*args), None
+    except AllocError as e:
+        r_s, err_s = None, e.code
+    assert err_m == err_s, (op, args, err_m, err_s)
+    if err_m is None and op in ("append", "swap_out", "swap_in", "lru"):
+        if op == "append":
+            assert list(r_s[0]) == list(r_m[0]) and r_s[1] == [tuple(p) for p in r_m[1]]
+        else:
+            assert r_s == r_m, (op, args)
+    seqs = sorted(model.tables)
+    free, ref, host, per = san.state(seqs)
+    assert free == model.free_list()
+    assert ref == [model.refcount(b) for b in range(len(ref))]
+    assert host == model.num_host_free()
+    for s in seqs:
+        assert per[s] == (model.length(s), model.is_swapped(s), model.table(s)), s
+
+
+def pair(drv, nb, bs, order):
+    return SanAlloc(drv, nb, bs, order), AllocModel(nb, bs, order)
+
+
+def test_hand_trace_under_sanitizers(driver, golden_dir):
+    with open(os.path.join(golden_dir, "alloc_trace.json")) as f:
+        g = json.load(f)
+    s, m = pair(driver, g["num_blocks"], g["block_size"], g["free_order"])
+    for st in g["steps"]:
+        op = st["op"]
+        if op == "add":
+            same(s, m, "add_seq", st["seq"])
+        elif op == "fork":
+            same(s, m, "fork", st["parent"], st["child"])
+        elif op == "free":
+            same(s, m, "free_seq", st["seq"])
+        else:
+            same(s, m, "append", st["seq"], st["n"])
+
+
+def test_random_ops_with_swaps_under_sanitizers(driver):
+    rng = np.random.default_rng(31)
+    for _ in range(80):
+        nb, nh = int(rng.integers(1, 16)), int(rng.integers(0, 12))
+        bs = int(rng.choice([1, 2, 4, 16]))
+        s, m = pair(driver, nb, bs, rng.permutation(nb))
+        same(s, m, "set_host_pool", nh)
+        live, nxt = [], 0
+        for _ in range(50):
+            r = rng.random()
+            if r < 0.15 or not live:
+                same(s, m, "add_seq", nxt); live.append(nxt); nxt += 1
+            elif r < 0.25:
+                same(s, m, "fork", int(rng.choice(live)), nxt)
+                if nxt in m.tables:
+                    live.append(nxt)
+                nxt += 1
+            elif r < 0.55:
+                same(s, m, "append", int(rng.choice(live)), int(rng.integers(0, 3 * bs + 1)))
+            elif r < 0.65:
+                same(s, m, "swap_out", int(rng.choice(live)))
+            elif r < 0.75:
+                same(s, m, "swap_in", int(rng.choice(live)))
+            elif r < 0.8:
+                same(s, m, "touch", int(rng.choice(live)))
+            elif r < 0.85:
+                same(s, m, "lru")
+            elif r < 0.88:
+                same(s, m, "set_host_pool", int(rng.integers(0, 12)))
+            elif r < 0.91:
+                same(s, m, "append", 10_000, 1)            # unknown sequence
+            elif r < 0.93:
+                same(s, m, "append", int(rng.choice(live)), -1)
+            else:
+                q = int(rng.choice(live)); same(s, m, "free_seq", q); live.remove(q)
+
+
+def _walk(driver, nb, bs, order, host, depth, ops):
+    count = 0
+
+    def walk(path, live, nxt, d):
+        nonlocal count
+        if d == 0:
+            return
+        for op in ops(live, nxt):
+            s, m = pair(driver, nb, bs, order)
+            if host is not None:
+                same(s, m, "set_host_pool", host)
+            for p in path + [op]:
+                same(s, m, *p)
+            count += 1
+            lv, nx = list(live), nxt
+            if op[0] in ("add_seq", "fork") and op[-1] in m.tables:
+                lv.append(op[-1]); nx += 1
+            if op[0] == "free_seq":
+                lv.remove(op[1])
+            walk(path + [op], lv, nx, d - 1)
+
+    walk([], [], 0, depth)
+    return count
+
+
+def test_every_short_op_sequence_under_sanitizers(driver):
+    def ops(live, nxt):
+        yield ("add_seq", nxt)
+        for s in live:
+            yield ("fork", s, nxt)
+            yield ("append", s, 1)
+            yield ("append", s, 3)
+            yield ("free_seq", s)
+
+    assert _walk(driver, 4, 2, [2, 0, 3, 1], None, 6, ops) > 20000
+
+
+def test_every_short_swap_sequence_under_sanitizers(driver):
+    def ops(live, nxt):
+        yield ("add_seq", nxt)
+        yield ("lru",)
+        for s in live:
+            yield ("fork", s, nxt)
+            yield ("append", s, 1)
+            yield ("append", s, 3)
+            yield ("swap_out", s)
+            yield ("swap_in", s)
+            yield ("touch", s)
+            yield ("free_seq", s)
+
+    assert _walk(driver, 3, 2, [1, 2, 0], 2, 5, ops) > 10000
+
+
+def test_create_rejects_pools_beyond_int32_slots(driver):
+    # num_blocks * block_size must fit the int32 slot ids
+    assert driver.call("new", 1 << 20, 2047, 0)[1] == 0     # 2,146,435,072 slots
+    assert driver.call("new", 1 << 20, 2048, 0)[1] == -1    # 2^31 slots
+    assert driver.call("new", 2_147_483_647, 2, 0)[1] == -1
+    assert driver.call("new", 0, 16, 0)[1] == -1
+    assert driver.call("new", 3, 16, 3, 0, 0, 1)[1] == -1    # not a permutation
+    # the largest slot of an accepted pool is still a valid int32
+    assert driver.call("new", 2, 1 << 30, 0)[1] == -1
+    assert driver.call("new", 1, (1 << 31) - 1, 0)[1] == 0
+    assert driver.call("add", 0)[1] == 0
+    r = driver.call("append", 0, 1)
+    assert r[1] == 0 and r[3] == 0
+
+
+def test_planning_helpers_under_sanitizers(driver):
+    rng = np.random.default_rng(41)
+    for _ in range(200):
+        n = int(rng.integers(0, 40))
+        lens = rng.integers(0, 20000, size=n)
+        P = int(rng.choice([16, 32, 512, 1536]))
+        r = driver.call("poff", P, n, *lens)
+        want = np.concatenate([[0], np.cumsum(np.maximum(1, -(-lens // P)))]).astype(int)
+        assert r[1] == 0 and r[2] == n + 1 and r[3:3 + n + 1] == list(want) and r[-1] == want[-1]
+        bs = int(rng.choice([16, 32]))
+        r = driver.call("toff", bs, n, *lens)
+        want = np.concatenate([[0], np.cumsum(-(-lens // bs))]).astype(int)
+        assert r[1] == 0 and r[3:3 + n + 1] == list(want)
+    # errors: negative length, totals past INT32_MAX, bad partition
+    assert driver.call("poff", 16, 2, 5, -1)[1] == -1
+    assert driver.call("poff", 0, 1, 5)[1] == -1
+    assert driver.call("poff", 1, 3, 2_000_000_000, 2_000_000_000, 5)[1] == -1
+    assert driver.call("toff", 1, 2, 2_000_000_000, 2_000_000_000)[1] == -1
+    # the shared-prefix plan: its definition on random groups
+    for _ in range(200):
+        bs, P = 16, int(rng.choice([16, 64, 2048]))
+        Hkv = int(rng.choice([1, 2, 8]))
+        Hq = Hkv * int(rng.choice([1, 4, 8]))
+        ng = int(rng.integers(0, 6))
+        sizes = rng.integers(0, 5, size=ng)
+        go = np.concatenate([[0], np.cumsum(sizes)]).astype(int)
+        gb = rng.integers(0, 12, size=ng)
+        n = int(go[-1])
+        lens = np.zeros(n, int)
+        for g in range(ng):
+            lens[go[g]:go[g + 1]] = gb[g] * bs + rng.integers(0, 300, size=sizes[g])
+        r = driver.call("plan", bs, P, Hq, Hkv, n, *lens, ng, *go, *gb)
+        assert r[1] == 0, r
+        rows, i = take(r, 2)
+        suf, i = take(r, i)
+        ts, i = take(r, i)
+        pre, i = take(r, i)
+        tot, _ = take(r, i)
+        G = Hq // Hkv
+        w_rows, w_suf, w_ts, w_pre = [0], [0], [], [0]
+        for g in range(ng):
+            npre = -(-int(gb[g]) // 8)
+            for s in range(go[g], go[g + 1]):
+                pt = int(gb[g]) * bs
+                nsuf = -(-(int(lens[s]) - pt) // P)
+                if nsuf + npre == 0:
+                    nsuf = 1
+                w_rows.append(w_rows[-1] + nsuf + npre)
+                w_suf.append(w_suf[-1] + nsuf)
+                w_ts.append(pt)
+            w_pre.append(w_pre[-1] + Hkv * (-(-int(sizes[g]) * G // 32)) * npre)
+        assert rows == w_rows and suf == w_suf and ts == w_ts and pre == w_pre
+        assert tot == [w_rows[-1], w_suf[-1], w_pre[-1]]
+    # a member shorter than its group's prefix is refused
+    assert driver.call("plan", 16, 64, 4, 4, 2, 100, 40, 1, 0, 2, 4)[1] == -1
