@@ -149,7 +149,12 @@ size_t paged_attention_workspace_bytes(int total_partitions, int num_q_heads, in
  *                 partitions of P tokens, partials in `workspace`, then the
  *                 split-K reduce (both launched here, in order, on `stream`)
  *  partition_offsets [num_seqs + 1] int32 (device), as described above;
- *                 NULL when partition_tokens == 0
+ *                 NULL when partition_tokens == 0.  A sequence whose entry
+ *                 count disagrees with its device length (stale offsets, say
+ *                 from the lengths before a step) gets NaN output rows, and
+ *                 so does a sequence given no partition; with such offsets
+ *                 whether the decode step stores that sequence's new row is
+ *                 unspecified
  *  total_partitions host copy of partition_offsets[num_seqs]
  *  workspace      device scratch of >= paged_attention_workspace_bytes()
  *                 bytes (caller-owned; contents need no initialisation)

@@ -29,7 +29,11 @@ heads; a pure-Python loop with math.fsum on tiny inputs; closed forms (L = 1
 returns its value row, q = 0 returns the mean of the value rows, constant
 value rows return the constant, two keys give the logistic weights); the
 hand-computed example in tests/golden/attention_tiny.json; invariance under
-any permutation of physical blocks and under prefix sharing.  Prefill pins
+any permutation of physical blocks and under prefix sharing.  For an fp8
+cache: the SDPA pin quantises and dequantises with torch's own float8_e4m3fn
+type (not this package's codec), on a workload with distinct key and value
+scales; a hand-computed two-token case pins the key scale to the scores and
+the value scale to the output (tests/test_oracle_fp8_scales.py).  Prefill pins
 (tests/test_oracle_prefill.py): torch's scaled_dot_product_attention in fp64
 with an explicit causal mask on the contiguous cache; a pure-Python fsum
 evaluation on tiny paged inputs; q = 0 gives the running mean of the value

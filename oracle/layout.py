@@ -20,7 +20,12 @@ in block ``table[t // block_size]`` at slot ``t % block_size``; a slot id is
 Pins (tests/test_oracle_layout.py): hand-written flat offsets for a small case
 (tests/golden/layout_offsets.json); write-then-gather returns the written bits;
 relabelling physical blocks by any permutation (moving the pool blocks with
-them) leaves every gathered sequence unchanged.
+them) leaves every gathered sequence unchanged; block copies and moves
+between pools on pools whose blocks carry known byte patterns (listed
+destinations take their sources' blocks whole, others keep theirs, a move
+there and back restores the pool); the key scale routed to keys and the
+value scale to values on an fp8 write, by hand-computed codes
+(tests/test_oracle_fp8_scales.py).
 """
 
 from __future__ import annotations

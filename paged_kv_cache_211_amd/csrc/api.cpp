@@ -21,25 +21,6 @@ static int hip_status(int e, const char* what) {
   return PKV_OK;
 }
 
-struct DecodeCall {
-  void* out;
-  const void* query;
-  const void* key_cache;
-  const void* value_cache;
-  const int32_t* block_tables;
-  int max_blocks_per_seq;
-  const int32_t* context_lens;
-  int num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks;
-  float scale;
-  pkv_dtype q_dtype, cache_dtype;
-  float k_scale, v_scale;
-  int partition_tokens;
-  const int32_t* partition_offsets;
-  int total_partitions;
-  void* workspace;
-  size_t workspace_bytes;
-};
-
 static int check_decode(const DecodeCall& c, DecodeArgs* a) {
   if (!c.out || !c.query || !c.key_cache || !c.value_cache || !c.block_tables || !c.context_lens)
     return fail(PKV_ERR_INVALID, "null pointer argument");
@@ -95,6 +76,20 @@ static int check_decode(const DecodeCall& c, DecodeArgs* a) {
   return PKV_OK;
 }
 
+int decode_common(const DecodeCall& c, bool reduce, void* stream) {
+  DecodeArgs a;
+  int rc = check_decode(c, &a);
+  if (rc) return rc;
+  if (c.num_seqs == 0) return PKV_OK;
+  rc = hip_status(launch_decode(a, stream), "paged_attention_decode launch");
+  if (rc || !reduce || c.partition_tokens == 0) return rc;
+  return hip_status(launch_splitk_reduce(c.out, a.ws, c.partition_offsets, c.num_seqs,
+                                         c.num_q_heads, c.head_dim, c.total_partitions,
+                                         c.q_dtype, stream, 2,
+                                         max_partitions(a.max_blocks, a.BS, a.partition)),
+                    "paged_attention_splitk_reduce launch");
+}
+
 }  // namespace pkv
 
 using namespace pkv;
@@ -131,20 +126,6 @@ int paged_kv_write(const void* key, const void* value, void* key_cache, void* va
                                     num_kv_heads, head_dim, block_size, num_blocks, src_dtype,
                                     cache_dtype, k_inv, v_inv, stream),
                     "paged_kv_write launch");
-}
-
-static int decode_common(const DecodeCall& c, bool reduce, void* stream) {
-  DecodeArgs a;
-  int rc = check_decode(c, &a);
-  if (rc) return rc;
-  if (c.num_seqs == 0) return PKV_OK;
-  rc = hip_status(launch_decode(a, stream), "paged_attention_decode launch");
-  if (rc || !reduce || c.partition_tokens == 0) return rc;
-  return hip_status(launch_splitk_reduce(c.out, a.ws, c.partition_offsets, c.num_seqs,
-                                         c.num_q_heads, c.head_dim, c.total_partitions,
-                                         c.q_dtype, stream, 2,
-                                         max_partitions(a.max_blocks, a.BS, a.partition)),
-                    "paged_attention_splitk_reduce launch");
 }
 
 int paged_attention_decode(void* out, const void* query, const void* key_cache,

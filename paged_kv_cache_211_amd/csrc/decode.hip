@@ -207,9 +207,11 @@ __device__ __forceinline__ void merge_heads(void* __restrict__ out, size_t oi0,
 }
 
 // Split-K reduce: one workgroup per (sequence, group of HG query heads);
-// sequences with one partition are left alone.  WIDE: sequences of up to
-// kReduceRowsInFlight * PL partials also load everything at once (a larger
-// register budget, so it is launched only where such sequences can occur).
+// sequences with one partition are left alone, and a sequence the offsets
+// give no partition (inconsistent offsets: no decode workgroup wrote it)
+// gets NaN rows.  WIDE: sequences of up to kReduceRowsInFlight * PL partials
+// also load everything at once (a larger register budget, so it is launched
+// only where such sequences can occur).
 template <int D, bool F32OUT, int HG, bool WIDE>
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(void* __restrict__ out,
                                                             const float* __restrict__ ws,
@@ -218,7 +220,17 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(void* __restrict__ o
   const int s = blockIdx.x, qh0 = blockIdx.y * HG;
   const int p0 = part_off[s];
   const int n = part_off[s + 1] - p0;
-  if (n < min_parts || n <= 0) return;
+  if (n <= 0) {
+    const size_t oi0 = ((size_t)s * Hq + qh0) * D;
+    for (int i = threadIdx.x; i < HG * D; i += 256) {
+      if constexpr (F32OUT)
+        ((float*)out)[oi0 + i] = NAN;
+      else
+        ((uint16_t*)out)[oi0 + i] = 0x7fc0;
+    }
+    return;
+  }
+  if (n < min_parts) return;
   merge_heads<D, F32OUT, HG, WIDE>(out, ((size_t)s * Hq + qh0) * D, ws, ws + (size_t)total_parts * Hq * D,
                              (size_t)p0 * Hq + qh0, Hq, n);
 }

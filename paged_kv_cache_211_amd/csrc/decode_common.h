@@ -46,8 +46,16 @@ constexpr int kBufs = PKV_DECODE_DEPTH + 1;      // tiles in registers per wave 
 // head, whose query takes few registers, and a tile is at most 4 KiB (32
 // VGPRs for its key and value loads).  One kv head per query head: 3 tiles
 // in flight measured 2.5% faster; 4 heads per wave: slower, at 244 VGPRs.
+// A 16 KiB tile (fp32, head_dim 128, block 32) takes 128 VGPRs for its key
+// and value loads, so such tiles go one at a time (no register ring; the
+// other waves of the compute unit keep loads in flight).
 template <int HPW, int TILE>
-constexpr int valu_bufs() { return HPW == 1 && TILE <= 4096 ? PKV_DECODE_DEPTH_1H + 1 : kBufs; }
+constexpr int valu_bufs() {
+  return TILE > 8192 ? 1 : HPW == 1 && TILE <= 4096 ? PKV_DECODE_DEPTH_1H + 1 : kBufs;
+}
+// Same for the stream-K vector-ALU kernel.
+template <int TILE>
+constexpr int sk_bufs() { return TILE > 8192 ? 1 : kBufs; }
 constexpr int kMfmaBufs = PKV_MFMA_DEPTH + 1;    // same, matrix-core kernel
 
 // Number of i in [1, S] with part_off[i] <= idx, i.e. the sequence owning
@@ -174,6 +182,11 @@ __device__ __forceinline__ u32x4 load16(const uint8_t* p) {
 #endif
 }
 
+// Split-K partitions of a sequence of L tokens: ceil(L / P), at least one.
+__device__ __forceinline__ int split_parts(int L, int P) {
+  return L > 0 ? (int)(((int64_t)L + P - 1) / P) : 1;
+}
+
 // What one workgroup works on.
 struct Work {
   int s;       // sequence
@@ -225,6 +238,9 @@ __device__ __forceinline__ Work locate(const DecodeArgs& a, int hpw, int lane, i
   wk.bad = false;
   if (L < 0) { L = 0; wk.bad = true; }
   if (L > a.max_blocks * BS) { L = a.max_blocks * BS; wk.bad = true; }
+  // split-K offsets must describe this length: ceil(L / P) partitions (one
+  // for L = 0); stale offsets would drop tokens or leave rows unwritten
+  if (SPLIT && !a.t_start && wk.nparts != split_parts(L, a.partition)) wk.bad = true;
   wk.L = L;
   wk.t0 = SPLIT ? tstart + part * a.partition : 0;
   wk.t1 = SPLIT ? min(L, wk.t0 + a.partition) : L;

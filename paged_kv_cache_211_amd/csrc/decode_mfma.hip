@@ -246,6 +246,7 @@ void decode_mfma_fp8_kernel(const DecodeArgs a) {
   bool bad = false;
   if (L < 0) { L = 0; bad = true; }
   if (L > a.max_blocks * BS) { L = a.max_blocks * BS; bad = true; }
+  if (SPLIT && nparts != split_parts(L, a.partition)) bad = true;   // stale offsets
   const int t0 = SPLIT ? part * a.partition : 0;
   const int t1 = SPLIT ? min(L, t0 + a.partition) : L;
   const int jend = (t1 + BS - 1) / BS;

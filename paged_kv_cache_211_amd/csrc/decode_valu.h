@@ -526,14 +526,17 @@ __global__ __launch_bounds__(NW * 64) void decode_sk_kernel(const DecodeArgs a) 
 
 // Heads per workgroup: the largest power of two (at most 8) dividing G whose
 // per-head registers fit the budget: the query dims of the lane's key chunks
-// (64 VGPRs in all) when q lives in VGPRs, else the accumulators and the
-// probabilities of a value load (48 VGPRs in all).
+// when q lives in VGPRs (64 VGPRs in all for tiles of up to 4 KiB, 32 for
+// larger tiles, whose two buffers of key and value loads take 128 VGPRs or
+// more: with two heads the kernel would exceed 256 VGPRs and spill into
+// accumulation registers at one wave per SIMD), else the accumulators and
+// the probabilities of a value load (48 VGPRs in all).
 template <int KV, int D, int BS>
 constexpr int max_hpw() {
   using Gm = Geo<KV, D, BS>;
   constexpr int per_head = kQLds ? Gm::NLOAD + (Gm::F32 ? 4 : Gm::PPC)
                                  : (Gm::F32 ? Gm::NLOAD * 4 : Gm::NLOAD * Gm::PPC);
-  constexpr int budget = kQLds ? 48 : 64;
+  constexpr int budget = kQLds ? 48 : Gm::TILE <= 4096 ? 64 : 32;
   return budget / per_head >= 8 ? 8 : budget / per_head >= 4 ? 4 : budget / per_head >= 2 ? 2 : 1;
 }
 
@@ -574,9 +577,9 @@ int launch_sk_t(const DecodeArgs& a, bool store, hipStream_t st) {
   if (store && groups != 1) return (int)hipErrorInvalidValue;
   dim3 block(kSkWaves * 64), grid((a.sk_workers + kSkWaves - 1) / kSkWaves);
   if (store)
-    hipLaunchKernelGGL((decode_sk_kernel<KV, D, BS, HPW, kSkWaves, kBufs, true>), grid, block, 0, st, a);
+    hipLaunchKernelGGL((decode_sk_kernel<KV, D, BS, HPW, kSkWaves, sk_bufs<Geo<KV, D, BS>::TILE>(), true>), grid, block, 0, st, a);
   else
-    hipLaunchKernelGGL((decode_sk_kernel<KV, D, BS, HPW, kSkWaves, kBufs, false>), grid, block, 0, st, a);
+    hipLaunchKernelGGL((decode_sk_kernel<KV, D, BS, HPW, kSkWaves, sk_bufs<Geo<KV, D, BS>::TILE>(), false>), grid, block, 0, st, a);
   return (int)hipGetLastError();
 }
 
@@ -588,7 +591,7 @@ int sk_workers_t() {
   if (hipGetDevice(&dev) != hipSuccess) return -1;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return -1;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-          &per_cu, reinterpret_cast<const void*>(&decode_sk_kernel<KV, D, BS, HPW, kSkWaves, kBufs, false>),
+          &per_cu, reinterpret_cast<const void*>(&decode_sk_kernel<KV, D, BS, HPW, kSkWaves, sk_bufs<Geo<KV, D, BS>::TILE>(), false>),
           kSkWaves * 64, 0) != hipSuccess)
     return -1;
   return max(1, per_cu) * cus * kSkWaves;

@@ -52,6 +52,30 @@ struct DecodeArgs {
   int ws_rows = 0;   // partial rows of the workspace when not total_parts
 };
 
+// The arguments of a decode entry point, as the C ABI receives them.
+struct DecodeCall {
+  void* out;
+  const void* query;
+  const void* key_cache;
+  const void* value_cache;
+  const int32_t* block_tables;
+  int max_blocks_per_seq;
+  const int32_t* context_lens;
+  int num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks;
+  float scale;
+  pkv_dtype q_dtype, cache_dtype;
+  float k_scale, v_scale;
+  int partition_tokens;
+  const int32_t* partition_offsets;
+  int total_partitions;
+  void* workspace;
+  size_t workspace_bytes;
+};
+
+// paged_attention_decode's checks and launches (api.cpp): the decode
+// kernel, then (reduce, partition_tokens > 0) the split-K reduce.
+int decode_common(const DecodeCall& c, bool reduce, void* stream);
+
 // Shared-prefix decode: groups of consecutive sequences (group_off[g] ..
 // group_off[g+1]) share their first group_blocks[g] blocks; prefix work items
 // (waves) of group g are pre_off[g] .. pre_off[g+1]; per sequence, rows

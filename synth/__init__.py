@@ -16,8 +16,12 @@ Recipe (per workload, seed ``seed``):
     ``default_rng([seed, 2, s])`` (keys drawn first, then values), and those
     of a shared prompt prefix from ``default_rng([seed, 3])``: fp32 N(0, 1)
     rounded to nearest even into the written dtype (bf16 also for an fp8
-    cache, which quantises on write with a fixed per-tensor scale of 8/448,
-    i.e. +-8 standard deviations map to the largest finite E4M3FN value).
+    cache, which quantises on write with fixed per-tensor scales: 8/448 for
+    keys and for values in the full-size workload, i.e. +-8 standard
+    deviations map to the largest finite E4M3FN value; the small skewed
+    workload keeps 8/448 for keys and takes 2/448 for values, so that
+    routing one pool's scale to the other changes every output by a factor
+    of about four and the parity tests see it).
 
 Operations: every sequence is added, prefilled with all but its last token,
 and then one decode step appends exactly one token per sequence, so the
@@ -42,6 +46,7 @@ import torch
 
 STORAGE = {"f32": np.float32, "bf16": np.uint16, "fp8": np.uint8}
 FP8_KV_SCALE = float(np.float32(8.0 / 448.0))
+FP8_V_SCALE_SMALL = float(np.float32(2.0 / 448.0))
 
 
 @dataclass(frozen=True)
@@ -107,7 +112,7 @@ SMALL = {
     4: replace(CONFIGS[4], key="bf16-prefix-small", S=8, seed=104, prefix=70, suffix_range=(5, 60),
                partition=64),
     5: replace(CONFIGS[5], key="fp8-skewed-small", S=8, seed=105, long=(2, 1500, 3000),
-               short=(6, 10, 100), partition=512),
+               short=(6, 10, 100), partition=512, v_scale=FP8_V_SCALE_SMALL),
 }
 
 

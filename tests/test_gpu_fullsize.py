@@ -8,9 +8,13 @@ stored (its slot holds the NaN poison until the step stores it); the oracle
 recomputes sampled sequences one by one (the first and last, the longest and
 shortest, and a few seeded others): their tables, slots and cache bits must
 match exactly and their outputs within tolerance.  For every sequence,
-properties that hold at any size are checked: outputs are finite and lie
-within the range of the values attended over (softmax weights are a convex
-combination).
+properties that hold at any size are checked: outputs are finite and each
+output element lies within the range of the value elements attended over
+(softmax weights are non-negative and sum to one, so out[s, g, i] is a
+convex combination of V_s[t, g // G, i] over the sequence's tokens t).  The
+value rows are read back through the block tables with the library's
+gather, and the range is taken per (sequence, kv head, dim), widened by the
+element type's tolerance.
 """
 
 import numpy as np
@@ -36,6 +40,37 @@ def _gpu():
         pytest.skip("needs a GPU")
 
 
+def value_ranges(cache, wl):
+    """Per (sequence, query head, dim): min and max of the dequantised value
+    elements of that sequence over its tokens, for the query head's kv head
+    (numpy [S, H_q, d] each).  The values are read back with paged_kv_gather
+    and reduced on the device one sequence at a time."""
+    from paged_kv_cache_211_amd import paged_kv_gather
+    c = wl.cfg
+    lens = wl.context_lens.astype(np.int32)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    T = int(cu[-1])
+    tabs = cache.block_tables(range(c.S))
+    ko = torch.empty((T, c.H_kv, c.d), dtype=cache.dtype, device="cuda")
+    vo = torch.empty_like(ko)
+    paged_kv_gather(ko, vo, cache.key_cache, cache.value_cache, tabs, torch.from_numpy(cu).cuda(), T)
+    del ko
+    if c.kv_dtype == "fp8":
+        vals = vo.view(torch.float8_e4m3fn)
+        mult = float(np.float32(c.v_scale))
+    else:
+        vals, mult = vo, 1.0
+    lo = torch.empty((c.S, c.H_kv, c.d), dtype=torch.float64, device="cuda")
+    hi = torch.empty_like(lo)
+    for s in range(c.S):
+        v = vals[cu[s]:cu[s + 1]].to(torch.float64) * mult
+        lo[s], hi[s] = v.amin(0), v.amax(0)
+    G = c.H_q // c.H_kv
+    lo = lo.repeat_interleave(G, dim=1).cpu().numpy()
+    hi = hi.repeat_interleave(G, dim=1).cpu().numpy()
+    return lo, hi
+
+
 @pytest.mark.parametrize("cfg_id", [1, 2, 3, 4, 5])
 def test_full_size_sampled(cfg_id):
     wl = synth.make(cfg_id)
@@ -55,7 +90,6 @@ def test_full_size_sampled(cfg_id):
                                 cache_dtype=c.kv_dtype, scale=c.scale, k_scale=c.k_scale,
                                 v_scale=c.v_scale, seqs=seqs)
     assert np.abs(wsum[seqs] - 1).max() < 1e-12
-    vmax = 8.0 if c.kv_dtype == "fp8" else 7.0   # |N(0,1)| draws stay far below 7 sigma here
     # the decode step as bench.py times it, then the plain decode over the stored cache
     inp = cache.decode_inputs(range(c.S), c.partition)
     out = torch.full_like(step["query"], float("nan"))
@@ -67,9 +101,13 @@ def test_full_size_sampled(cfg_id):
     if cfg_id in SPECIFIED_PARTITION and SPECIFIED_PARTITION[cfg_id] != c.partition:
         p = SPECIFIED_PARTITION[cfg_id]
         checks.append((f"decode, partition {p}", gpu_decode(cache, step, wl, p)))
+    lo, hi = value_ranges(cache, wl)
     for name, got in checks:
         assert np.isfinite(got).all(), name
-        assert np.abs(got).max() <= vmax, name
+        below = (got < lo - H.TOL[c.kv_dtype]).sum()
+        above = (got > hi + H.TOL[c.kv_dtype]).sum()
+        print(f"  {name}: outputs outside their sequence's value range: {below + above}", flush=True)
+        assert below == 0 and above == 0, name
         err = np.abs(got[seqs] - ref[seqs]).max()
         print(f"  {name}, sampled seqs {seqs}: max abs err {err:.3e} (tol {H.TOL[c.kv_dtype]})",
               flush=True)

@@ -275,3 +275,46 @@ def test_bad_block_id_poisons_only_its_sequence():
         torch.cuda.synchronize()
         o = out.double().cpu().numpy()
         assert np.isnan(o[1]).all() and np.isfinite(np.delete(o, 1, axis=0)).all()
+
+
+@pytest.mark.parametrize("cfg_id", [3, 5])
+def test_stale_partition_offsets_poison_only_their_sequences(cfg_id):
+    """Split-K offsets that disagree with the device lengths -- here taken
+    from the lengths one token earlier, so sequences whose previous length
+    was a whole number of partitions are one partition short -- give those
+    sequences NaN rows instead of silently dropping their last tokens, and a
+    sequence that the offsets give no partition gets NaN rows from the
+    reduce; the other sequences are still correct (vector-ALU kernel for the
+    GQA shape, matrix-core kernel for the fp8 shape)."""
+    from paged_kv_cache_211_amd import paged_attention_partition_offsets
+    P = 512
+    lens = [P + 1, 2 * P + 1, 700, 100, 3 * P]
+    wl = _custom(cfg_id, lens, seed=17)
+    c = wl.cfg
+    _case(f"stale partition offsets, config {cfg_id}")
+    st, _ = replay.build(wl)
+    ref, _ = oracle_out(wl, st)
+    cache, step = H.build(wl, poison=True)
+    tol = H.TOL[c.kv_dtype]
+
+    def run(off, tot):
+        inp = cache.decode_inputs(range(c.S), P)
+        inp["partition_offsets"] = torch.from_numpy(np.asarray(off, np.int32)).cuda()
+        inp["total_partitions"] = int(tot)
+        out = torch.zeros_like(step["query"])
+        cache.decode(step["query"], inp, c.scale, out=out)
+        torch.cuda.synchronize()
+        return out.double().cpu().numpy()
+
+    stale, tot = paged_attention_partition_offsets(np.asarray(lens) - 1, P)
+    got = run(stale, tot)
+    for s, L in enumerate(lens):
+        if -(-(L - 1) // P) != -(-L // P):
+            assert np.isnan(got[s]).all(), s
+        else:
+            assert np.abs(got[s] - ref[s]).max() <= tol, s
+    # sequence 1 given no partition, sequence 2 given three instead of two
+    got = run([0, 2, 2, 5, 6, 9], 9)
+    assert np.isnan(got[1]).all() and np.isnan(got[2]).all()
+    for s in (0, 3, 4):
+        assert np.abs(got[s] - ref[s]).max() <= tol, s

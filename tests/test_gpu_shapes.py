@@ -1,0 +1,110 @@
+"""Every decode shape the library accepts, against the fp64 oracle, through
+the C ABI.
+
+The library accepts (query, cache) element pairs (fp32, fp32), (bf16, bf16)
+and (bf16, fp8 E4M3FN), head_dim 64 or 128, block size 16 or 32, and any
+number G >= 1 of query heads per kv head.  Which kernel serves a call
+depends on G only through the heads one wave holds (the largest power of two
+dividing G that the registers allow: 1, 2, 4 or 8) and on whether G/that is
+1 (the decode step then stores inside the decode launch) or more, and for
+fp8 with head_dim 128 and block size 32 on whether 8 divides G (matrix
+cores, one or more groups of 8).  G in {1, 2, 3, 4, 6, 8, 12, 16} reaches
+every such combination for every (pair, head_dim, block size).
+
+Per shape: one pass, split-K with two partition lengths, stream-K, and the
+decode step (new token stored by the library from an unstored, NaN-poisoned
+slot) all within the element type's tolerance of the oracle (fp32 1e-5, bf16
+2e-2, fp8 6e-2), with the cache bits after the step equal to the oracle's.
+fp8 shapes run with distinct key and value scales (8/448 and 2/448).
+Context lengths 1, bs + 3, 5 bs + 7 and 23 bs + 5 give single-token, ragged
+and multi-partition sequences.
+"""
+
+import dataclasses
+import itertools
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import replay
+from paged_kv_cache_211_amd import workload as H
+
+from .test_gpu_parity import check_cache_bits, gpu_decode, oracle_out
+from .test_gpu_step import step_once
+
+pytestmark = pytest.mark.gpu
+
+PAIRS = [("f32", "f32"), ("bf16", "bf16"), ("bf16", "fp8")]
+GS = [1, 2, 3, 4, 6, 8, 12, 16]
+SHAPES = [(q, kv, d, bs, G) for (q, kv), d, bs, G in itertools.product(PAIRS, (64, 128), (16, 32), GS)]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    import paged_kv_cache_211_amd  # noqa: F401  (fails loudly if libpkv.so is missing)
+
+
+def shape_workload(q, kv, d, bs, G, seed):
+    fp8 = kv == "fp8"
+    c = synth.Config(
+        key=f"shape-{q}-{kv}-d{d}-bs{bs}-G{G}", S=4, H_q=2 * G, H_kv=2, d=d, bs=bs, q_dtype=q,
+        kv_dtype=kv, scale=float(np.float32(1.0 / math.sqrt(d))), partition=2 * bs, seed=seed,
+        lens=(1, bs + 3, 5 * bs + 7, 23 * bs + 5),
+        k_scale=synth.FP8_KV_SCALE if fp8 else 1.0,
+        v_scale=synth.FP8_V_SCALE_SMALL if fp8 else 1.0)
+    return synth.make(c)
+
+
+@pytest.mark.parametrize("q,kv,d,bs,G", SHAPES, ids=[f"{q}-{kv}-d{d}-bs{bs}-G{G}" for q, kv, d, bs, G in SHAPES])
+def test_every_accepted_decode_shape(q, kv, d, bs, G):
+    import paged_kv_cache_211_amd as pkv
+    seed = 5000 + SHAPES.index((q, kv, d, bs, G))
+    wl = shape_workload(q, kv, d, bs, G, seed)
+    c = wl.cfg
+    print(f"\n[case] shape {c.key} seed {seed}", flush=True)
+    st, oslots = replay.build(wl)
+    ref, _ = oracle_out(wl, st)
+    tol = H.TOL[kv]
+    cache, step = H.build(wl, poison=True)
+    assert np.array_equal(step["slots"].astype(np.int64), oslots)
+    results = {}
+    for P in (0, 2 * c.bs, 8 * c.bs):
+        results[f"partition {P}"] = gpu_decode(cache, step, wl, P)
+    inp = cache.decode_inputs(range(c.S), streamk=True, num_q_heads=c.H_q,
+                              q_dtype=H.TORCH_CACHE[q])
+    out = torch.full_like(step["query"], float("nan"))
+    cache.decode(step["query"], inp, c.scale, out=out)
+    torch.cuda.synchronize()
+    results["stream-K"] = out.double().cpu().numpy()
+    # the decode step from an unstored (NaN-poisoned) new slot
+    cs, ss = H.build(wl, poison=True, write_step=False)
+    results["decode step"] = step_once(cs, ss, wl, 2 * c.bs)
+    check_cache_bits(cs, st, wl, np.arange(c.S))
+    launches = pkv.paged_attention_decode_step_launches(c.H_q, c.H_kv, d, bs, H.TORCH_CACHE[q],
+                                                         cache.dtype, 2 * c.bs)
+    for name, got in results.items():
+        assert np.isfinite(got).all(), name
+        err = float(np.abs(got - ref).max())
+        print(f"  {name}: max abs err {err:.3e} (tol {tol})", flush=True)
+        assert err <= tol, (name, err)
+    print(f"  decode step launches: {launches}", flush=True)
+
+
+def test_shape_list_covers_every_kernel_choice():
+    """The G values above reach heads-per-wave 1, 2, 4 and 8 with one group
+    and with several groups per kv head, and on the fp8 matrix-core shape one
+    and two groups of 8 (host-side arithmetic only)."""
+    import paged_kv_cache_211_amd as pkv
+    seen = set()
+    for q, kv, d, bs, G in SHAPES:
+        n = pkv.paged_attention_decode_step_launches(2 * G, 2, d, bs, H.TORCH_CACHE[q],
+                                                     H.TORCH_CACHE[kv], 0)
+        seen.add((q, kv, d, bs, n))
+    for (q, kv), d, bs in itertools.product(PAIRS, (64, 128), (16, 32)):
+        # both forms of the step: the store inside the decode (1 launch) and before it (2)
+        assert (q, kv, d, bs, 1) in seen and (q, kv, d, bs, 2) in seen, (q, kv, d, bs)

@@ -48,15 +48,18 @@ def test_write_mixed_slot_mapping(cache, bs, D):
     x32 = rng.standard_normal((2, T, Hkv, D), dtype=np.float32)
     kb = torch.from_numpy(x32[0]).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
     vb = torch.from_numpy(x32[1]).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
-    scale = float(np.float32(8.0 / 448.0)) if cache == "fp8" else 1.0
+    # distinct key and value scales: a kernel that routed one pool's scale to
+    # the other would store other codes
+    ks = float(np.float32(8.0 / 448.0)) if cache == "fp8" else 1.0
+    vs = float(np.float32(2.0 / 448.0)) if cache == "fp8" else 1.0
     okc, ovc = OL.empty_pools(NB, Hkv, D, bs, cache, fill=0)
     OL.write_kv(okc, ovc, kb, vb, slots, bs=bs, src_dtype="bf16", cache_dtype=cache,
-                k_scale=scale, v_scale=scale)
+                k_scale=ks, v_scale=vs)
     kc, vc = empty_pools(NB, Hkv, D, bs, H.TORCH_CACHE[cache], "cuda")
     kc.view(torch.uint8).zero_()
     vc.view(torch.uint8).zero_()
     paged_kv_write(H.to_dev(kb, "bf16"), H.to_dev(vb, "bf16"), kc, vc,
-                   torch.from_numpy(slots).cuda(), k_scale=scale, v_scale=scale)
+                   torch.from_numpy(slots).cuda(), k_scale=ks, v_scale=vs)
     torch.cuda.synchronize()
     gk = kc.view(torch.uint8).cpu().numpy()
     gv = vc.view(torch.uint8).cpu().numpy()

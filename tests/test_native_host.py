@@ -317,7 +317,6 @@ def test_decode_argument_validation_needs_no_gpu(pkv):
     assert call(P=32, off=fake, tot=2, ws=fake, wsb=10) == -3
     assert call(P=32, off=None, tot=2, ws=fake, wsb=1 << 30) == -1
     assert call(scale=float("nan")) == -1
-    assert b"workspace" in L.pkv_last_error() or L.pkv_last_error() != b""
     w = L.paged_kv_write(fake, fake, fake, fake, fake, 4, 2, 96, 16, 10, 1, 1, 1.0, 1.0, None)
     assert w == -2
     w = L.paged_kv_write(fake, fake, fake, fake, fake, 4, 2, 128, 16, 10, 1, 2, -1.0, 1.0, None)

@@ -36,6 +36,17 @@ def _sdpa(q, Ks, Vs, scale):
     return np.stack(outs)
 
 
+def _torch_fp8_roundtrip(bf16_bits, scale):
+    """bf16 rows -> E4M3FN by torch -> fp64 values, with a per-tensor scale:
+    x * fp32(1 / scale) in fp32, clamped to the format's +-448 (torch's cast
+    does not saturate), cast to float8_e4m3fn (round to nearest even), then
+    widened and multiplied by the scale in fp64."""
+    x = torch.from_numpy(np.ascontiguousarray(bf16_bits).view(np.int16)).view(torch.bfloat16)
+    inv = torch.tensor(np.float32(1.0) / np.float32(scale), dtype=torch.float32)
+    y = torch.clamp(x.float() * inv, -448.0, 448.0)
+    return y.to(torch.float8_e4m3fn).to(torch.float64).numpy() * float(np.float32(scale))
+
+
 def _pyloop(q, K, V, scale):
     """Tiny pure-Python decode attention, math.fsum accumulation."""
     L = len(K)
@@ -56,7 +67,9 @@ def test_paged_oracle_matches_sdpa_on_contiguous_cache(cfg_id):
                                bs=c.bs, cache_dtype=c.kv_dtype, scale=c.scale,
                                k_scale=c.k_scale, v_scale=c.v_scale)
     # contiguous cache straight from the value streams (never paged); fp8
-    # values go through the same quantise-on-write rule first
+    # values are quantised and dequantised by torch's float8_e4m3fn type with
+    # each pool's own scale (keys and values have different scales in the
+    # small skewed workload)
     Ks, Vs = [], []
     for s in range(c.S):
         parts = []
@@ -66,10 +79,12 @@ def test_paged_oracle_matches_sdpa_on_contiguous_cache(cfg_id):
         parts.append(wl.values(("seq", s), 0, own))
         kb = np.concatenate([p[0] for p in parts])
         vb = np.concatenate([p[1] for p in parts])
-        kq = Lx.encode_for_cache(kb, c.src_dtype, c.kv_dtype, c.k_scale)
-        vq = Lx.encode_for_cache(vb, c.src_dtype, c.kv_dtype, c.v_scale)
-        Ks.append(A.dequant(kq, c.kv_dtype, c.k_scale))
-        Vs.append(A.dequant(vq, c.kv_dtype, c.v_scale))
+        if c.kv_dtype == "fp8":
+            Ks.append(_torch_fp8_roundtrip(kb, c.k_scale))
+            Vs.append(_torch_fp8_roundtrip(vb, c.v_scale))
+        else:
+            Ks.append(decode(kb, c.kv_dtype))
+            Vs.append(decode(vb, c.kv_dtype))
     ref = _sdpa(decode(wl.q, c.q_dtype), Ks, Vs, c.scale)
     assert np.abs(out - ref).max() < 1e-12
     assert np.abs(wsum - 1.0).max() < 1e-12

@@ -107,3 +107,35 @@ def test_fp8_write_quantises():
     gk, gv = Lx.gather_seq(kc, vc, [0, 1], 34, bs=32)
     assert (gk[33] == quantize_fp8(bits[0], "bf16", 0.05)).all()
     assert (gv[33] == quantize_fp8(bits[0], "bf16", 0.5)).all()
+
+
+def test_move_blocks_between_pools():
+    """move_blocks (swapping sequences between a device pool and a host pool)
+    on pools where every byte of block b in pool p holds a known value: the
+    listed destination blocks take their sources' bytes, every other block
+    keeps its own, the source pool is unchanged, and moving back with the
+    pairs reversed restores the original destination contents."""
+    H, d, bs = 2, 64, 16
+    dev_k, dev_v = Lx.empty_pools(5, H, d, bs, "bf16", fill=0)
+    host_k, host_v = Lx.empty_pools(4, H, d, bs, "bf16", fill=0)
+    for b in range(5):
+        dev_k[b], dev_v[b] = 0x1000 + b, 0x2000 + b
+    for b in range(4):
+        host_k[b], host_v[b] = 0x3000 + b, 0x4000 + b
+    d0 = (dev_k.copy(), dev_v.copy())
+    h0 = (host_k.copy(), host_v.copy())
+    pairs = [(3, 0), (0, 2), (4, 1)]           # (device block, host slot)
+    Lx.move_blocks(host_k, host_v, dev_k, dev_v, pairs)
+    assert [int(host_k[h].flat[0]) for h in range(4)] == [0x1003, 0x1004, 0x1000, 0x3003]
+    assert [int(host_v[h].flat[0]) for h in range(4)] == [0x2003, 0x2004, 0x2000, 0x4003]
+    for h in range(4):                         # whole blocks move, not just their first element
+        assert (host_k[h] == host_k[h].flat[0]).all() and (host_v[h] == host_v[h].flat[0]).all()
+    assert (dev_k == d0[0]).all() and (dev_v == d0[1]).all()
+    # into a fresh device pool and back out: the round trip restores the host pool
+    new_k, new_v = Lx.empty_pools(5, H, d, bs, "bf16", fill=0)
+    Lx.move_blocks(new_k, new_v, host_k, host_v, [(h, b) for b, h in pairs])
+    assert [int(new_k[b].flat[0]) for b in range(5)] == [0x1000, 0, 0, 0x1003, 0x1004]
+    host_k[...], host_v[...] = h0
+    Lx.move_blocks(host_k, host_v, new_k, new_v, pairs)
+    Lx.move_blocks(host_k, host_v, *h0, [(3, 3)])
+    assert [int(host_k[h].flat[0]) for h in range(4)] == [0x1003, 0x1004, 0x1000, 0x3003]
