@@ -39,8 +39,9 @@ FLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
          "-Wno-unused-command-line-argument"]
 
 
-def compile_cmd(src: str, obj: str) -> list[str]:
-    return [hipcc(), *FLAGS, "-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, src), "-o", obj]
+def compile_cmd(src: str, obj: str, defines=()) -> list[str]:
+    return [hipcc(), *FLAGS, *[f"-D{d}" for d in defines], "-I", INCLUDE, "-I", CSRC, "-c",
+            os.path.join(CSRC, src), "-o", obj]
 
 
 def _run(cmd: list[str], verbose: bool) -> None:
@@ -54,21 +55,34 @@ def _run(cmd: list[str], verbose: bool) -> None:
         print("\n".join(noise), file=sys.stderr)
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source (in parallel) and link libpkv.so; always recompiles."""
+def build(verbose: bool = False, out: str | None = None, defines=()) -> str:
+    """Compile every source (in parallel) and link libpkv.so; always recompiles.
+
+    out: where to put the library (default: in-tree, where the package loads
+    it from); defines: extra NAME=VALUE macros for a measurement build, e.g.
+    PKV_DECODE_MFMA=0 to serve every fp8 shape with the vector-ALU kernels
+    (such a build is loaded through PKV_LIBRARY, never in-tree)."""
     from concurrent.futures import ThreadPoolExecutor
+    if defines and out is None:
+        raise ValueError("a build with extra defines needs its own output path")
+    dst = os.path.abspath(out) if out else LIB
     with tempfile.TemporaryDirectory(prefix="pkv_build.", dir=PKG) as tmpdir:
         objs = [os.path.join(tmpdir, os.path.splitext(src)[0] + ".o") for src in SOURCES]
         workers = max(1, min(len(SOURCES), os.cpu_count() or 1, 16))
         with ThreadPoolExecutor(workers) as pool:
-            for f in [pool.submit(_run, compile_cmd(src, obj), verbose)
+            for f in [pool.submit(_run, compile_cmd(src, obj, defines), verbose)
                       for src, obj in zip(SOURCES, objs)]:
                 f.result()
         tmp = os.path.join(tmpdir, "libpkv.so")
         _run([hipcc(), *FLAGS, "-shared", *objs, "-o", tmp], verbose)
-        os.replace(tmp, LIB)
-    return LIB
+        os.replace(tmp, dst)
+    return dst
 
 
 if __name__ == "__main__":
-    print(build(verbose=True))
+    import argparse
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--out", default=None, help="library path (default: in-tree)")
+    ap.add_argument("-D", dest="defines", action="append", default=[], metavar="NAME=VALUE")
+    a = ap.parse_args()
+    print(build(verbose=True, out=a.out, defines=a.defines))

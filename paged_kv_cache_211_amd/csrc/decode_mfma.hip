@@ -307,9 +307,15 @@ void decode_mfma_sk_kernel(const DecodeArgs a) {
 
 }  // namespace
 
+// PKV_DECODE_MFMA=0 (a measurement build only) leaves every shape to the
+// vector-ALU kernels, for comparing the two on the same fp8 shape.
+#ifndef PKV_DECODE_MFMA
+#define PKV_DECODE_MFMA 1
+#endif
+
 bool decode_mfma_eligible(const DecodeArgs& a) {
-  return a.kv_dtype == PKV_FP8_E4M3 && a.q_dtype == PKV_BF16 && a.D == 128 && a.BS == 32 &&
-         (a.Hq / a.Hkv) % 8 == 0;
+  return PKV_DECODE_MFMA && a.kv_dtype == PKV_FP8_E4M3 && a.q_dtype == PKV_BF16 && a.D == 128 &&
+         a.BS == 32 && (a.Hq / a.Hkv) % 8 == 0;
 }
 
 int launch_decode_mfma(const DecodeArgs& a, void* stream, bool store) {
