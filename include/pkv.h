@@ -168,6 +168,36 @@ int paged_attention_decode(void* out, const void* query, const void* key_cache,
                            const int32_t* partition_offsets, int total_partitions,
                            void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * paged_attention_decode_noalloc -- paged_attention_decode for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc.  Same arguments, result and
+ * launches as paged_attention_decode without workspace / workspace_bytes:
+ * the split-K partials go to a device array inside the library,
+ * PKV_NOALLOC_WORKSPACE_BYTES (64 MiB) per GPU, which each GPU the library
+ * runs on holds until the process ends.  The call allocates nothing: its
+ * first call on a device looks up that device's copy of the array
+ * (hipGetSymbolAddress), every call launches the decode and the reduce on
+ * `stream`.
+ *  - partition_tokens > 0 with paged_attention_workspace_bytes(
+ *    total_partitions, num_q_heads, head_dim) > PKV_NOALLOC_WORKSPACE_BYTES
+ *    returns PKV_ERR_WORKSPACE and launches nothing; other errors as
+ *    paged_attention_decode.
+ *  - All calls on one GPU share the array, which keeps the last call's
+ *    partials; nothing in it needs clearing (every partial a call reads, the
+ *    same call writes first).  Calls that overlap on one GPU (two streams,
+ *    two threads) race: order them on one stream or with events.
+ * ------------------------------------------------------------------------- */
+#define PKV_NOALLOC_WORKSPACE_BYTES ((size_t)64 << 20)
+int paged_attention_decode_noalloc(void* out, const void* query, const void* key_cache,
+                                   const void* value_cache, const int32_t* block_tables,
+                                   int max_blocks_per_seq, const int32_t* context_lens,
+                                   int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                                   int block_size, int num_blocks, float scale, pkv_dtype q_dtype,
+                                   pkv_dtype cache_dtype, float k_scale, float v_scale,
+                                   int partition_tokens, const int32_t* partition_offsets,
+                                   int total_partitions, void* stream);
+
 /* paged_attention_decode_partials -- the first of the two launches above on
  * its own: writes `out` for sequences with a single partition and partials
  * (m, l, unnormalised o) into `workspace` for the others.  Same arguments as

@@ -153,6 +153,33 @@ def paged_attention_decode(out, query, key_cache, value_cache, block_tables, con
     check(lib().paged_attention_decode(*args, _stream(stream)))
 
 
+def paged_attention_decode_noalloc(out, query, key_cache, value_cache, block_tables, context_lens,
+                                   scale, k_scale=1.0, v_scale=1.0, partition_tokens=0,
+                                   partition_offsets=None, total_partitions=0, stream=None):
+    """paged_attention_decode with the split-K partials in the library's own
+    static device array (PKV_NOALLOC_WORKSPACE_BYTES per GPU): no workspace
+    argument, nothing allocated.  Calls that overlap on one GPU race."""
+    nb, H, D, bs = _pool_shape(key_cache, value_cache)
+    for t, n in ((out, "out"), (query, "query"), (key_cache, "key_cache"), (value_cache, "value_cache")):
+        _need(t, n)
+    _need(block_tables, "block_tables", torch.int32)
+    _need(context_lens, "context_lens", torch.int32)
+    S, Hq, Dq = query.shape
+    if Dq != D or tuple(out.shape) != (S, Hq, D) or out.dtype != query.dtype:
+        raise PkvError(-1, "query/out must be [S, H_q, head_dim] of one dtype")
+    if block_tables.dim() != 2 or block_tables.shape[0] != S or context_lens.numel() != S:
+        raise PkvError(-1, "block_tables must be [S, max_blocks] and context_lens [S]")
+    if partition_tokens:
+        if partition_offsets is None:
+            raise PkvError(-1, "split-K needs partition_offsets")
+        _need(partition_offsets, "partition_offsets", torch.int32)
+    check(lib().paged_attention_decode_noalloc(
+        _ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache), _ptr(block_tables),
+        block_tables.shape[1], _ptr(context_lens), S, Hq, H, D, bs, nb, float(scale),
+        cache_dtype_code(query), cache_dtype_code(key_cache), float(k_scale), float(v_scale),
+        int(partition_tokens), _ptr(partition_offsets), int(total_partitions), _stream(stream)))
+
+
 def paged_attention_decode_partials(out, query, key_cache, value_cache, block_tables, context_lens,
                                     scale, k_scale=1.0, v_scale=1.0, partition_tokens=0,
                                     partition_offsets=None, total_partitions=0, workspace=None,

@@ -15,6 +15,7 @@ LIB_PATH = os.environ.get("PKV_LIBRARY") or os.path.join(
     os.path.dirname(os.path.abspath(__file__)), "libpkv.so")
 
 PKV_F32, PKV_BF16, PKV_FP8_E4M3 = 0, 1, 2
+PKV_NOALLOC_WORKSPACE_BYTES = 64 << 20   # include/pkv.h
 PKV_OK = 0
 ERRORS = {
     -1: "PKV_ERR_INVALID",
@@ -38,6 +39,8 @@ SIGNATURES = {
     "paged_attention_workspace_bytes": (sz, [i32, i32, i32]),
     "paged_attention_decode": (i32, [vp, vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, i32, i32, f32,
                                      i32, i32, f32, f32, i32, vp, i32, vp, sz, vp]),
+    "paged_attention_decode_noalloc": (i32, [vp, vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, i32,
+                                             i32, f32, i32, i32, f32, f32, i32, vp, i32, vp]),
     "paged_attention_decode_partials": (i32, [vp, vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, i32,
                                               i32, f32, i32, i32, f32, f32, i32, vp, i32, vp, sz,
                                               vp]),

@@ -317,6 +317,15 @@ def test_decode_argument_validation_needs_no_gpu(pkv):
     assert call(P=32, off=fake, tot=2, ws=fake, wsb=10) == -3
     assert call(P=32, off=None, tot=2, ws=fake, wsb=1 << 30) == -1
     assert call(scale=float("nan")) == -1
+    # the no-alloc decode refuses partials beyond its static array before
+    # touching any device
+    rows = _native.PKV_NOALLOC_WORKSPACE_BYTES // (8 * 130 * 4) + 1
+    assert L.paged_attention_decode_noalloc(fake, fake, fake, fake, fake, 4, fake, 2, 8, 2, 128, 16,
+                                            10, 0.1, 1, 1, 1.0, 1.0, 32, fake, rows, None) == -3
+    assert b"static workspace" in L.pkv_last_error()
+    assert L.paged_attention_decode_noalloc(None, fake, fake, fake, fake, 4, fake, 2, 8, 2, 128, 16,
+                                            10, 0.1, 1, 1, 1.0, 1.0, 0, None, 0, None) == -1
+    assert b"workspace" in L.pkv_last_error() or L.pkv_last_error() != b""
     w = L.paged_kv_write(fake, fake, fake, fake, fake, 4, 2, 96, 16, 10, 1, 1, 1.0, 1.0, None)
     assert w == -2
     w = L.paged_kv_write(fake, fake, fake, fake, fake, 4, 2, 128, 16, 10, 1, 2, -1.0, 1.0, None)

@@ -1,0 +1,88 @@
+"""paged_attention_decode_noalloc (split-K partials in the library's static
+device array) against paged_attention_decode (the same kernels with a
+caller-owned workspace), through the C ABI: two calls in a row, the second
+on a smaller input, each bit-identical to the workspace entry point and
+within tolerance of the fp64 oracle; a request beyond the static size is
+refused before anything is launched."""
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import replay
+from paged_kv_cache_211_amd import workload as H
+
+from .test_gpu_parity import oracle_out
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    import paged_kv_cache_211_amd  # noqa: F401  (fails loudly if libpkv.so is missing)
+
+
+def _both(cache, step, wl, seqs, P):
+    """(no-alloc output, workspace output) for the sequences `seqs`."""
+    import paged_kv_cache_211_amd as pkv
+    c = wl.cfg
+    inp = cache.decode_inputs(seqs, P)
+    q = step["query"][list(seqs)].contiguous()
+    kw = dict(k_scale=c.k_scale, v_scale=c.v_scale, partition_tokens=P,
+              partition_offsets=inp["partition_offsets"], total_partitions=inp["total_partitions"])
+    a = torch.full_like(q, float("nan"))
+    pkv.paged_attention_decode_noalloc(a, q, cache.key_cache, cache.value_cache,
+                                       inp["block_tables"], inp["context_lens"], c.scale, **kw)
+    b = torch.full_like(q, float("nan"))
+    ws = torch.empty(max(pkv.paged_attention_workspace_bytes(inp["total_partitions"], c.H_q, c.d), 16),
+                     dtype=torch.uint8, device="cuda")
+    pkv.paged_attention_decode(b, q, cache.key_cache, cache.value_cache, inp["block_tables"],
+                               inp["context_lens"], c.scale, workspace=ws, **kw)
+    torch.cuda.synchronize()
+    return a.double().cpu().numpy(), b.double().cpu().numpy()
+
+
+@pytest.mark.parametrize("cfg_id", [3, 5])
+def test_noalloc_matches_workspace_entry_point(cfg_id):
+    wl = synth.make(synth.SMALL[cfg_id])
+    c = wl.cfg
+    print(f"\n[case] no-alloc decode {c.key}", flush=True)
+    st, _ = replay.build(wl)
+    ref, _ = oracle_out(wl, st)
+    cache, step = H.build(wl, poison=True)
+    # first call: every sequence, short partitions (many partials); second
+    # call: fewer sequences and longer partitions (fewer partials), so it
+    # reads only rows it wrote itself over the first call's leftovers
+    for seqs, P in ((list(range(c.S)), 2 * c.bs), (list(range(1, c.S, 2)), 8 * c.bs)):
+        got, want = _both(cache, step, wl, seqs, P)
+        assert np.isfinite(got).all()
+        assert np.array_equal(got, want), (seqs, P)
+        assert np.abs(got - ref[seqs]).max() <= H.TOL[c.kv_dtype], (seqs, P)
+    # one pass: no partials at all
+    got, want = _both(cache, step, wl, list(range(c.S)), 0)
+    assert np.array_equal(got, want)
+
+
+def test_noalloc_refuses_partials_beyond_its_array():
+    import paged_kv_cache_211_amd as pkv
+    from paged_kv_cache_211_amd import PkvError, _native
+    wl = synth.make(synth.SMALL[3])
+    c = wl.cfg
+    cache, step = H.build(wl, poison=True)
+    inp = cache.decode_inputs(range(c.S), 2 * c.bs)
+    # a partition count whose partials exceed the static array (offsets are
+    # never read: the call is refused on the host)
+    rows = _native.PKV_NOALLOC_WORKSPACE_BYTES // (c.H_q * (c.d + 2) * 4) + 1
+    out = torch.zeros_like(step["query"])
+    with pytest.raises(PkvError) as e:
+        pkv.paged_attention_decode_noalloc(out, step["query"], cache.key_cache, cache.value_cache,
+                                           inp["block_tables"], inp["context_lens"], c.scale,
+                                           partition_tokens=2 * c.bs,
+                                           partition_offsets=inp["partition_offsets"],
+                                           total_partitions=rows)
+    assert e.value.code == -3
+    torch.cuda.synchronize()
+    assert (out == 0).all()
