@@ -226,7 +226,7 @@ def main_prefill(args):
 
     import synth
     import paged_kv_cache_211_amd as pkv
-    from paged_kv_cache_211_amd import workload as W
+    from synth import device as W
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
@@ -330,7 +330,7 @@ def main_swap(args):
 
     import synth
     import paged_kv_cache_211_amd as pkv
-    from paged_kv_cache_211_amd import workload as W
+    from synth import device as W
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
@@ -427,7 +427,7 @@ def main():
 
     import synth
     import paged_kv_cache_211_amd as pkv
-    from paged_kv_cache_211_amd import workload as W
+    from synth import device as W
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")

@@ -1,5 +1,7 @@
 """Loads a workload description onto the device through the library's own
-allocator, copy and write calls.
+allocator, copy and write calls (the HIP side of a test or of the bench; the
+oracle side never imports this module, and it does none of the method's
+arithmetic: it orders calls to the C ABI).
 
 A workload is any object with ``cfg`` (S, H_kv, d, bs, dtypes, fp8 scales),
 ``num_blocks``, ``free_order``, ``q`` (query bits), ``prefill`` / ``decode``
@@ -17,7 +19,6 @@ TORCH_CACHE = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.uint8}
 # a byte whose repetition is NaN in every cache format: fp32 0xFFFFFFFF, bf16
 # 0xFFFF, fp8 0xFF (S.1111.111)
 POISON_BYTE = 0xFF
-TOL = {"f32": 1e-5, "bf16": 2e-2, "fp8": 6e-2}
 
 
 def to_dev(bits: np.ndarray, dtype: str, device="cuda") -> torch.Tensor:
@@ -69,7 +70,7 @@ def build(wl, poison=True, device="cuda", write_step=True):
     Returns (cache, step) where step holds the decode-step slot mapping and
     new key/value rows (device, row s = sequence s) and the query.
     """
-    from .engine import PagedKVCache
+    from paged_kv_cache_211_amd.engine import PagedKVCache
     c = wl.cfg
     cache = PagedKVCache(wl.num_blocks, c.H_kv, c.d, c.bs, TORCH_CACHE[c.kv_dtype], device,
                          free_order=wl.free_order, k_scale=c.k_scale, v_scale=c.v_scale,

@@ -16,7 +16,9 @@ import torch
 import synth
 from oracle import attention as OA
 from oracle import replay
-from paged_kv_cache_211_amd import workload as H
+from synth import device as H
+
+from .tolerances import TOL
 
 pytestmark = pytest.mark.gpu
 
@@ -71,7 +73,7 @@ def test_prefill_parity(G):
     c = wl.cfg
     st, _ = replay.build(wl)
     cache, _ = H.build(wl, poison=True)
-    tol = H.TOL[c.kv_dtype]
+    tol = TOL[c.kv_dtype]
     for name, chunks in _chunk_sets(wl).items():
         _case(f"prefill G={G} chunks {name} {chunks.tolist()}")
         q_bits = synth.prefill_queries(wl, chunks)
@@ -101,7 +103,7 @@ def test_prefill_many_sequences_dispatch_order(S, tie):
     assert np.isfinite(got).all()
     err = np.abs(got - ref).max()
     print(f"  max abs err {err:.3e}", flush=True)
-    assert err <= H.TOL[c.kv_dtype]
+    assert err <= TOL[c.kv_dtype]
 
 
 def test_prefill_one_row_chunks_match_decode():
@@ -120,7 +122,7 @@ def test_prefill_one_row_chunks_match_decode():
     paged_attention_decode(dec, q, cache.key_cache, cache.value_cache, inp["block_tables"],
                            inp["context_lens"], c.scale)
     torch.cuda.synchronize()
-    assert np.abs(got - dec.double().cpu().numpy()).max() <= 2 * H.TOL[c.kv_dtype]
+    assert np.abs(got - dec.double().cpu().numpy()).max() <= 2 * TOL[c.kv_dtype]
 
 
 def test_prefill_bad_inputs_give_nan_rows():
@@ -140,14 +142,14 @@ def test_prefill_bad_inputs_give_nan_rows():
     got, _, _ = gpu_prefill(cache, wl, chunks, q_bits, tables=tab)
     assert np.isnan(got[qs[1]:qs[2]]).all()
     keep = np.r_[0:qs[1], qs[2]:qs[-1]]
-    assert np.abs(got[keep] - ref[keep]).max() <= H.TOL[c.kv_dtype]
+    assert np.abs(got[keep] - ref[keep]).max() <= TOL[c.kv_dtype]
     # sequence 3's context made shorter than its chunk
     lens = inp["context_lens"].clone()
     lens[3] = int(chunks[3]) - 1
     got, _, _ = gpu_prefill(cache, wl, chunks, q_bits, lens=lens)
     assert np.isnan(got[qs[3]:qs[4]]).all()
     keep = np.r_[0:qs[3], qs[4]:qs[-1]]
-    assert np.abs(got[keep] - ref[keep]).max() <= H.TOL[c.kv_dtype]
+    assert np.abs(got[keep] - ref[keep]).max() <= TOL[c.kv_dtype]
 
 
 def test_prefill_argument_checks():
@@ -188,4 +190,4 @@ def test_prefill_full_size_sampled():
     rows = np.concatenate([np.arange(qs[s], qs[s + 1]) for s in seqs])
     err = np.abs(got[rows] - ref[rows]).max()
     print(f"  sampled seqs {seqs}: max abs err {err:.3e}", flush=True)
-    assert err <= H.TOL[c.kv_dtype]
+    assert err <= TOL[c.kv_dtype]

@@ -11,8 +11,9 @@ import torch
 
 import synth
 from oracle import replay
-from paged_kv_cache_211_amd import workload as H
+from synth import device as H
 
+from .tolerances import TOL
 from .test_gpu_parity import oracle_out
 
 pytestmark = pytest.mark.gpu
@@ -71,7 +72,7 @@ def test_prefix_detected_groups(G):
         assert np.isfinite(got).all()
         err = np.abs(got - ref).max()
         print(f"  partition {P}: max abs err {err:.3e}", flush=True)
-        assert err <= H.TOL[c.kv_dtype], (P, err)
+        assert err <= TOL[c.kv_dtype], (P, err)
 
 
 @pytest.mark.parametrize("G,S", [(4, 11), (8, 5), (1, 3)])
@@ -91,7 +92,7 @@ def test_prefix_several_pieces(G, S):
         assert np.isfinite(got).all()
         err = np.abs(got - ref).max()
         print(f"  partition {P}: max abs err {err:.3e}", flush=True)
-        assert err <= H.TOL[c.kv_dtype], (P, err)
+        assert err <= TOL[c.kv_dtype], (P, err)
 
 
 @pytest.mark.parametrize("groups", [
@@ -110,7 +111,7 @@ def test_prefix_explicit_groups(groups):
     for P in (c.bs, c.partition):
         got, _ = prefix_decode(cache, step, wl, P, groups=(np.array(groups[0]), np.array(groups[1])))
         assert np.isfinite(got).all()
-        assert np.abs(got - ref).max() <= H.TOL[c.kv_dtype], P
+        assert np.abs(got - ref).max() <= TOL[c.kv_dtype], P
 
 
 def test_prefix_bad_block_poisons_the_group():
@@ -145,4 +146,4 @@ def test_prefix_full_size_sampled():
     ref, _ = oracle_out(wl, st, seqs=seqs)
     err = np.abs(got[seqs] - ref[seqs]).max()
     print(f"  sampled seqs {seqs}: max abs err {err:.3e}", flush=True)
-    assert err <= H.TOL[c.kv_dtype]
+    assert err <= TOL[c.kv_dtype]

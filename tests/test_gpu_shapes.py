@@ -30,8 +30,9 @@ import torch
 
 import synth
 from oracle import replay
-from paged_kv_cache_211_amd import workload as H
+from synth import device as H
 
+from .tolerances import TOL
 from .test_gpu_parity import check_cache_bits, gpu_decode, oracle_out
 from .test_gpu_step import step_once
 
@@ -69,7 +70,7 @@ def test_every_accepted_decode_shape(q, kv, d, bs, G):
     print(f"\n[case] shape {c.key} seed {seed}", flush=True)
     st, oslots = replay.build(wl)
     ref, _ = oracle_out(wl, st)
-    tol = H.TOL[kv]
+    tol = TOL[kv]
     cache, step = H.build(wl, poison=True)
     assert np.array_equal(step["slots"].astype(np.int64), oslots)
     results = {}

@@ -16,8 +16,9 @@ import torch
 
 import synth
 from oracle import replay
-from paged_kv_cache_211_amd import workload as H
+from synth import device as H
 
+from .tolerances import TOL
 from .test_gpu_parity import check_cache_bits, gpu_decode, oracle_out
 
 pytestmark = pytest.mark.gpu
@@ -59,7 +60,7 @@ def test_step_parity(variant):
     _case(f"decode step {c.key} S={c.S} G={c.H_q // c.H_kv}")
     st, oslots = replay.build(wl)
     ref, _ = oracle_out(wl, st)
-    tol = H.TOL[c.kv_dtype]
+    tol = TOL[c.kv_dtype]
     for P in sorted({0, c.partition, 2 * c.bs}):
         cache, step = H.build(wl, poison=True, write_step=False)
         assert np.array_equal(step["slots"].astype(np.int64), oslots)
@@ -90,7 +91,7 @@ def test_repeated_steps():
     # storing the same rows again is idempotent, so every call must agree
     for P in (2 * c.bs, c.partition, c.bs, 2 * c.bs):
         got = step_once(cache, step, wl, P)
-        assert np.abs(got - ref).max() <= H.TOL[c.kv_dtype], P
+        assert np.abs(got - ref).max() <= TOL[c.kv_dtype], P
 
 
 def test_step_zero_length_sequence():
@@ -116,7 +117,7 @@ def test_step_zero_length_sequence():
         o = out.double().cpu().numpy()
         assert (o[2] == 0).all()
         keep = np.delete(np.arange(c.S), 2)
-        assert np.abs(o[keep] - ref[keep]).max() <= H.TOL[c.kv_dtype]
+        assert np.abs(o[keep] - ref[keep]).max() <= TOL[c.kv_dtype]
 
 
 def test_step_argument_checks():

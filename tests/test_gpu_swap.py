@@ -15,8 +15,9 @@ import torch
 import synth
 from oracle import layout as OL
 from oracle import replay
-from paged_kv_cache_211_amd import workload as H
+from synth import device as H
 
+from .tolerances import TOL
 from .test_gpu_parity import check_cache_bits, gpu_decode, oracle_out
 
 pytestmark = pytest.mark.gpu
@@ -109,7 +110,7 @@ def test_swap_round_trip(cfg_id, n_out):
     ref, _ = oracle_out(wl, st)
     got = gpu_decode(cache, step, wl, c.partition)
     assert np.isfinite(got).all()
-    assert np.abs(got - ref).max() <= H.TOL[c.kv_dtype]
+    assert np.abs(got - ref).max() <= TOL[c.kv_dtype]
 
 
 def test_swap_refuses_shared_blocks():

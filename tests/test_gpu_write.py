@@ -8,7 +8,9 @@ import pytest
 import torch
 
 from oracle import layout as OL
-from paged_kv_cache_211_amd import workload as H
+from synth import device as H
+
+from .tolerances import TOL
 
 pytestmark = pytest.mark.gpu
 

@@ -282,7 +282,7 @@ def test_partition_offsets_and_workspace(pkv):
         off, tot = pkv.paged_attention_partition_offsets(lens, P)
         n = np.maximum(1, -(-lens // P))
         assert list(off) == [0] + list(np.cumsum(n)) and tot == int(n.sum())
-    assert pkv.paged_attention_workspace_bytes(10, 32, 128) == 10 * 32 * 130 * 4
+    assert pkv.paged_attention_workspace_bytes(10, 32, 128) == 10 * 32 * 130 * 4 + 256
     from paged_kv_cache_211_amd import PkvError
     with pytest.raises(PkvError):
         pkv.paged_attention_partition_offsets([5, -1], 16)

@@ -11,8 +11,9 @@ import torch
 
 import synth
 from oracle import replay
-from paged_kv_cache_211_amd import workload as H
+from synth import device as H
 
+from .tolerances import TOL
 from .test_gpu_parity import oracle_out
 
 pytestmark = pytest.mark.gpu
@@ -60,7 +61,7 @@ def test_noalloc_matches_workspace_entry_point(cfg_id):
         got, want = _both(cache, step, wl, seqs, P)
         assert np.isfinite(got).all()
         assert np.array_equal(got, want), (seqs, P)
-        assert np.abs(got - ref[seqs]).max() <= H.TOL[c.kv_dtype], (seqs, P)
+        assert np.abs(got - ref[seqs]).max() <= TOL[c.kv_dtype], (seqs, P)
     # one pass: no partials at all
     got, want = _both(cache, step, wl, list(range(c.S)), 0)
     assert np.array_equal(got, want)
