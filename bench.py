@@ -26,8 +26,10 @@ Prints ONE JSON line on stdout; details go to stderr.
     python bench.py --swap
 
 --swap times moving whole sequences of the GQA workload to a pinned host
-pool and back (paged_kv_swap_blocks driven by the allocator's swap pairs);
-its roofline is the host link (PCIe 5.0 x16, 64 GB/s each way).
+pool and back: staged through a device pool and moved by the copy engines
+(the headline), and by the block-move kernel straight to the host; then
+each form on a second stream beside a split-K decode of the other
+sequences.  Its roofline is the host link (PCIe 5.0 x16, 64 GB/s each way).
 """
 
 from __future__ import annotations
@@ -74,9 +76,11 @@ def parse():
                    help="token budget of the oracle's timed sample")
     p.add_argument("--traffic-file", default=None)
     p.add_argument("--mode", choices=("fused", "separate"), default="fused")
-    p.add_argument("--schedule", choices=("splitk", "streamk", "prefix"), default="splitk",
-                   help="split-K partitions of --partition tokens, stream-K persistent waves, or "
-                        "the shared-prefix decode (shared blocks read once per 32 query rows)")
+    p.add_argument("--schedule", choices=("splitk", "streamk", "prefix", "queue"), default="splitk",
+                   help="split-K partitions of --partition tokens, stream-K persistent waves, "
+                        "the shared-prefix decode (shared blocks read once per 32 query rows), or "
+                        "split-K with items taken from a work counter (fp8 matrix-core shape; "
+                        "no step form: the store, then the decode and its reduce)")
     p.add_argument("--workers", type=int, default=0, help="stream-K waves (0 = resident count)")
     p.add_argument("--prefill", action="store_true",
                    help="time chunked prefill (store + causal attention) instead of decode")
@@ -337,7 +341,7 @@ def main_swap(args):
     torch.cuda.set_device(dev)
     wl = synth.make(3)
     c = wl.cfg
-    cache, _ = W.build(wl, poison=False, device=dev)
+    cache, step = W.build(wl, poison=False, device=dev)
     n = min(args.swap_seqs, c.S)
     seqs = list(range(n))
     nblocks = sum(len(cache.alloc.block_table(s)) for s in seqs)
@@ -351,31 +355,53 @@ def main_swap(args):
     hslot = np.arange(nblocks, dtype=np.int32)
     out_pairs = torch.from_numpy(np.stack([dblk, hslot], 1).copy()).to(dev)
     in_pairs = torch.from_numpy(np.stack([hslot, dblk], 1).copy()).to(dev)
-    e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    # the staged form: device blocks <-> a contiguous device staging pool (one
+    # launch, HBM to HBM), staging pool <-> host slots by the copy engines
+    stage_k, stage_v = pkv.empty_pools(nblocks, c.H_kv, c.d, c.bs, cache.dtype, dev)
+    gather_pairs = torch.from_numpy(np.stack([dblk, hslot], 1).copy()).to(dev)   # dev -> stage
+    scatter_pairs = torch.from_numpy(np.stack([hslot, dblk], 1).copy()).to(dev)  # stage -> dev
+    ident = np.stack([hslot, hslot], 1).copy()                                  # stage <-> host
 
-    def d2h():
-        pkv.paged_kv_swap_blocks(cache.host_key, cache.host_value, cache.key_cache,
-                                 cache.value_cache, out_pairs)
+    def d2h(stream=None, dma=False):
+        if dma:
+            pkv.paged_kv_swap_blocks(stage_k, stage_v, cache.key_cache, cache.value_cache,
+                                     gather_pairs, stream=stream)
+            pkv.paged_kv_swap_blocks_dma(cache.host_key, cache.host_value, stage_k, stage_v,
+                                         ident, stream=stream)
+        else:
+            pkv.paged_kv_swap_blocks(cache.host_key, cache.host_value, cache.key_cache,
+                                     cache.value_cache, out_pairs, stream=stream)
 
-    def h2d():
-        pkv.paged_kv_swap_blocks(cache.key_cache, cache.value_cache, cache.host_key,
-                                 cache.host_value, in_pairs)
+    def h2d(stream=None, dma=False):
+        if dma:
+            pkv.paged_kv_swap_blocks_dma(stage_k, stage_v, cache.host_key, cache.host_value,
+                                         ident, stream=stream)
+            pkv.paged_kv_swap_blocks(cache.key_cache, cache.value_cache, stage_k, stage_v,
+                                     scatter_pairs, stream=stream)
+        else:
+            pkv.paged_kv_swap_blocks(cache.key_cache, cache.value_cache, cache.host_key,
+                                     cache.host_value, in_pairs, stream=stream)
 
-    for _ in range(args.warmup):
-        d2h()
-        h2d()
-    torch.cuda.synchronize()
-    e[0].record()
-    for _ in range(args.steps):
-        d2h()
-    e[1].record()
-    for _ in range(args.steps):
-        h2d()
-    e[2].record()
-    torch.cuda.synchronize()
-    out_us = e[0].elapsed_time(e[1]) / args.steps * 1e3
-    in_us = e[1].elapsed_time(e[2]) / args.steps * 1e3
-    # the whole call path: allocator swap pairs, their upload, the kernel
+    def time_alone(dma):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        for _ in range(args.warmup):
+            d2h(dma=dma)
+            h2d(dma=dma)
+        torch.cuda.synchronize()
+        e[0].record()
+        for _ in range(args.steps):
+            d2h(dma=dma)
+        e[1].record()
+        for _ in range(args.steps):
+            h2d(dma=dma)
+        e[2].record()
+        torch.cuda.synchronize()
+        return (e[0].elapsed_time(e[1]) / args.steps * 1e3,
+                e[1].elapsed_time(e[2]) / args.steps * 1e3)
+
+    out_us, in_us = time_alone(False)
+    dma_out_us, dma_in_us = time_alone(True)
+    # the whole call path: allocator swap pairs, the staging copy, the copy engines
     t0 = time.perf_counter()
     steps = max(1, args.steps // 5)
     for _ in range(steps):
@@ -387,23 +413,98 @@ def main_swap(args):
     rt_us = (time.perf_counter() - t0) / steps * 1e6
     gbps_out, gbps_in = moved / (out_us * 1e-6) / 1e9, moved / (in_us * 1e-6) / 1e9
     log(f"[bench] swap kernel: device->host {out_us:.1f} us = {gbps_out:.1f} GB/s, host->device "
-        f"{in_us:.1f} us = {gbps_in:.1f} GB/s; per-sequence calls round trip {rt_us:.0f} us")
-    slow = min(gbps_out, gbps_in)
+        f"{in_us:.1f} us = {gbps_in:.1f} GB/s; per-sequence engine calls round trip {rt_us:.0f} us")
+    log(f"[bench] swap staged through a device pool, copy engines on the host link: "
+        f"device->host {dma_out_us:.1f} us = "
+        f"{moved / (dma_out_us * 1e-6) / 1e9:.1f} GB/s, host->device {dma_in_us:.1f} us = "
+        f"{moved / (dma_in_us * 1e-6) / 1e9:.1f} GB/s")
+
+    # overlap: the other sequences decode (split-K) on the main stream while
+    # the victims' blocks go to the host pool and back on a second stream of
+    # the same (default) priority
+    main_st, side = torch.cuda.current_stream(), torch.cuda.Stream()
+    residents = list(range(n, c.S))
+    rin = cache.decode_inputs(residents, c.partition)
+    rq = step["query"][residents].contiguous()
+    rout = torch.empty_like(rq)
+
+    def decode_residents():
+        cache.decode(rq, rin, c.scale, out=rout)
+
+    for _ in range(args.warmup):
+        decode_residents()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+    ev[0].record(main_st)
+    for _ in range(5):
+        decode_residents()
+    ev[1].record(main_st)
+    torch.cuda.synchronize()
+    # enough decode steps to span one swap round trip
+    n_dec = max(1, math.ceil((out_us + in_us) / (ev[0].elapsed_time(ev[1]) * 1e3 / 5)))
+    ev[0].record(main_st)
+    for _ in range(n_dec):
+        decode_residents()
+    ev[1].record(main_st)
+    torch.cuda.synchronize()
+    dec_alone = ev[0].elapsed_time(ev[1]) * 1e3 / n_dec
+
+    def overlap_of(dma, rt_alone):
+        # both at once: the side stream starts when the main stream does
+        ev[2].record(main_st)
+        side.wait_event(ev[2])
+        d2h(side, dma)
+        h2d(side, dma)
+        ev[3].record(side)
+        for _ in range(n_dec):
+            decode_residents()
+        ev[4].record(main_st)
+        main_st.wait_event(ev[3])
+        ev[5].record(main_st)
+        torch.cuda.synchronize()
+        dec_during = ev[2].elapsed_time(ev[4]) * 1e3 / n_dec
+        swap_during = ev[2].elapsed_time(ev[3]) * 1e3
+        both = ev[2].elapsed_time(ev[5]) * 1e3
+        serial = dec_alone * n_dec + rt_alone
+        log(f"[bench] overlap ({'staged, copy engines' if dma else 'swap kernel'}): {n_dec} decode steps "
+            f"of {len(residents)} sequences {dec_alone:.1f} us each alone, {dec_during:.1f} us while "
+            f"swapping; swap round trip {rt_alone:.0f} us alone, {swap_during:.0f} us beside the "
+            f"decode; both {both:.0f} us vs {serial:.0f} us one after the other")
+        return {"decode_us_alone": round(dec_alone, 2), "decode_us_during_swap": round(dec_during, 2),
+                "swap_round_trip_us_alone": round(rt_alone, 1),
+                "swap_round_trip_us_during_decode": round(swap_during, 1),
+                "both_us": round(both, 1), "serial_us": round(serial, 1),
+                "hidden_fraction": round((serial - both) / min(dec_alone * n_dec, rt_alone), 3)}
+
+    overlap = {"decode_steps": n_dec, "decode_sequences": len(residents),
+               "swap_kernel": overlap_of(False, out_us + in_us),
+               "staged_copy_engines": overlap_of(True, dma_out_us + dma_in_us)}
+    # the headline is the staged form (the engine's swap path)
+    rt = dma_out_us + dma_in_us
+    dma_gbps_out, dma_gbps_in = moved / (dma_out_us * 1e-6) / 1e9, moved / (dma_in_us * 1e-6) / 1e9
+    slow = min(dma_gbps_out, dma_gbps_in)
     line = {
-        "metric": SWAP_METRIC, "value": round(out_us + in_us, 2), "unit": "us/round-trip",
+        "metric": SWAP_METRIC, "value": round(rt, 2), "unit": "us/round-trip",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-        "ms_per_step": round((out_us + in_us) / 1e3, 5), "higher_is_better": False,
+        "ms_per_step": round(rt / 1e3, 5), "higher_is_better": False,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": f"{c.key}: sequences 0..{n - 1} ({nblocks} blocks of "
-                               f"{block_bytes * 2} bytes) to a pinned host pool and back",
+                               f"{block_bytes * 2} bytes) to a pinned host pool and back, "
+                               f"staged through a device pool, copy engines on the host link",
                    "parallelism": "single GPU"},
         "kernel_us": {"swap_device_to_host": round(out_us, 2), "swap_host_to_device": round(in_us, 2),
-                      "swap_calls_round_trip": round(rt_us, 1)},
+                      "swap_calls_round_trip": round(rt_us, 1),
+                      "staged_copy_engines_device_to_host": round(dma_out_us, 2),
+                      "staged_copy_engines_host_to_device": round(dma_in_us, 2)},
+        "overlap_with_decode": overlap,
         "roofline": {"bound": "host-link", "achieved": round(slow, 2), "peak": HOST_LINK_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(slow / HOST_LINK_PEAK_GBPS, 4), "traffic": None,
-                     "kernel": "swap_blocks_kernel (slower direction)",
+                     "kernel": "staging copy + copy engines (slower direction)",
                      "algorithmic_bytes_per_launch": moved,
-                     "device_to_host_GBps": round(gbps_out, 2), "host_to_device_GBps": round(gbps_in, 2)},
+                     "device_to_host_GBps": round(dma_gbps_out, 2),
+                     "host_to_device_GBps": round(dma_gbps_in, 2),
+                     "swap_kernel_device_to_host_GBps": round(gbps_out, 2),
+                     "swap_kernel_host_to_device_GBps": round(gbps_in, 2)},
         "cpu_baseline": None,
     }
     print(json.dumps(line), flush=True)
@@ -454,6 +555,9 @@ def main():
 
     SK = args.schedule == "streamk"
     PF = args.schedule == "prefix"
+    QU = args.schedule == "queue"
+    if QU and not P:
+        raise SystemExit("--schedule queue needs split-K partitions (--partition > 0)")
     if PF:
         inp = cache.decode_inputs(range(c.S), P, prefix=True, num_q_heads=c.H_q)
         ws = cache.workspace(inp["prefix_totals"][0], c.H_q, c.d)
@@ -474,8 +578,8 @@ def main():
     tab, lens = inp["block_tables"], inp["context_lens"]
     # longest sequence's partition count: sizes the standalone reduce's launch
     max_parts = int(-(-int(inp["lens_host"].max()) // P)) if P else 0
-    if PF:
-        n_launch = 3   # the store, the fused prefix + suffix pass, the reduce
+    if PF or QU:
+        n_launch = 3   # the store, the decode (prefix + suffix pass, or work counter), the reduce
     elif SK:
         n_launch = 2 if pkv.paged_attention_decode_step_launches(c.H_q, c.H_kv, c.d, c.bs, q.dtype,
                                                                  cache.dtype, 0) == 1 else 3
@@ -487,6 +591,10 @@ def main():
         pkv.paged_attention_decode_prefix(out, q, kc, vc, tab, lens, c.scale, P, inp["prefix"],
                                           inp["prefix_totals"], ws, c.k_scale, c.v_scale)
 
+    def run_queue(kc, vc):
+        pkv.paged_attention_decode_queue(out, q, kc, vc, tab, lens, c.scale, c.k_scale, c.v_scale,
+                                         P, inp["partition_offsets"], inp["total_partitions"], ws)
+
     def run_fused(i, ev=None):
         kc, vc = layers[i % R]
         if ev:
@@ -494,6 +602,9 @@ def main():
         if PF:   # no in-kernel store on this schedule: the store, then the decode
             pkv.paged_kv_write(key, value, kc, vc, slots, k_scale=c.k_scale, v_scale=c.v_scale)
             run_prefix(kc, vc)
+        elif QU:
+            pkv.paged_kv_write(key, value, kc, vc, slots, k_scale=c.k_scale, v_scale=c.v_scale)
+            run_queue(kc, vc)
         elif SK:
             pkv.paged_attention_decode_step_streamk(out, q, key, value, kc, vc, tab, lens, c.scale,
                                                     inp["tile_offsets"], inp["total_tiles"],
@@ -512,8 +623,8 @@ def main():
         pkv.paged_kv_write(key, value, kc, vc, slots, k_scale=c.k_scale, v_scale=c.v_scale)
         if ev:
             ev[1].record()
-        if PF:
-            run_prefix(kc, vc)
+        if PF or QU:
+            run_prefix(kc, vc) if PF else run_queue(kc, vc)
             if ev:
                 ev[2].record()
         elif SK:
@@ -615,6 +726,8 @@ def main():
         kc, vc = layers[i % R]
         if PF:
             run_prefix(kc, vc)
+        elif QU:
+            run_queue(kc, vc)
         elif SK:
             pkv.paged_attention_decode_streamk_partials(out, q, kc, vc, tab, lens, c.scale,
                                                         inp["tile_offsets"], inp["total_tiles"],
@@ -644,6 +757,9 @@ def main():
     elif PF:
         # the three launches of the shared-prefix decode, over the unique bytes
         kernel, kern_us, kern_bytes = "decode (shared prefix + suffix + reduce)", dec_only_us, ab["decode_unique"]
+    elif QU:
+        # the work-counter decode and its reduce (no partials-only form)
+        kernel, kern_us, kern_bytes = "decode (work-counter split-K + reduce)", dec_only_us, ab["decode"]
     else:
         kernel = ("decode (stream-K)" if SK else "decode (split-K partials)" if P else "decode")
         kern_us, kern_bytes = dec_only_us, ab["decode"]
@@ -682,7 +798,8 @@ def main():
             "workload": f"{c.key}: {c.S} seqs, {c.H_q}/{c.H_kv} heads, head_dim {c.d}, "
                         f"block_size {c.bs}, {c.kv_dtype} KV, context {wl.total_tokens} tokens "
                         f"(seed {c.seed}), "
-                        + (f"stream-K {inp['workers']} waves" if SK else f"split-K {P}")
+                        + (f"stream-K {inp['workers']} waves" if SK else
+                           f"split-K {P} from a work counter" if QU else f"split-K {P}")
                         + f", {R} pool layers, {args.mode} step",
             "global_batch": c.S,
             "seq_len": int(wl.context_lens.max()),

@@ -124,8 +124,11 @@ int paged_attention_partition_offsets(const int32_t* context_lens_host, int num_
  * (the partials of "PagedAttention Kernel：大模型推理优化的显存管理革新"
  * §3.2's split work, combined by the reduce): one fp32 row of head_dim
  * unnormalised outputs and one (max, sum) pair per (partition, query head),
- * total_partitions * num_q_heads * (head_dim + 2) * 4 bytes.  Returns 0 when
- * an argument is not positive.  Pure arithmetic, no device access. */
+ * then 256 bytes for the work counter of the persistent decode (§3.2's
+ * atomic page counter):
+ * total_partitions * num_q_heads * (head_dim + 2) * 4 + 256 bytes.  The
+ * workspace must be 16-byte aligned.  Returns 0 when an argument is not
+ * positive.  Pure arithmetic, no device access. */
 size_t paged_attention_workspace_bytes(int total_partitions, int num_q_heads, int head_dim);
 
 /* ---------------------------------------------------------------------------
@@ -157,7 +160,9 @@ size_t paged_attention_workspace_bytes(int total_partitions, int num_q_heads, in
  *                 unspecified
  *  total_partitions host copy of partition_offsets[num_seqs]
  *  workspace      device scratch of >= paged_attention_workspace_bytes()
- *                 bytes (caller-owned; contents need no initialisation)
+ *                 bytes, 16-byte aligned (caller-owned; contents need no
+ *                 initialisation; two calls that run at the same time need
+ *                 two workspaces)
  * ------------------------------------------------------------------------- */
 int paged_attention_decode(void* out, const void* query, const void* key_cache,
                            const void* value_cache, const int32_t* block_tables,
@@ -197,6 +202,35 @@ int paged_attention_decode_noalloc(void* out, const void* query, const void* key
                                    pkv_dtype cache_dtype, float k_scale, float v_scale,
                                    int partition_tokens, const int32_t* partition_offsets,
                                    int total_partitions, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * paged_attention_decode_queue -- paged_attention_decode's split-K with its
+ * work items handed out by a device work counter: a grid of resident waves,
+ * each taking (sequence, partition, kv head) items one after another in the
+ * same longest-first order, and loading the next item's table entries, query
+ * and first tile while the current one streams ("PagedAttention Kernel：大模型
+ * 推理优化的显存管理革新" §3.2: an atomic page counter in a persistent loop;
+ * §2.2: prefetch of the next page).  Same arguments, result (bit for bit)
+ * and errors as paged_attention_decode, plus:
+ *  - only an fp8 E4M3 cache with bf16 queries, head_dim 128, block_size 32,
+ *    a multiple of 8 query heads per kv head, 0 < partition_tokens <= 2048
+ *    and num_seqs <= 512; anything else returns PKV_ERR_UNSUPPORTED and
+ *    launches nothing;
+ *  - the counter lives in the workspace's last bytes (inside
+ *    paged_attention_workspace_bytes) and is reset by the launch itself, so
+ *    the workspace still needs no initialisation.
+ * paged_attention_decode's hardware-dispatched waves are faster on MI355X;
+ * this schedule exists for comparison and for callers that want it.
+ * ------------------------------------------------------------------------- */
+int paged_attention_decode_queue(void* out, const void* query, const void* key_cache,
+                                 const void* value_cache, const int32_t* block_tables,
+                                 int max_blocks_per_seq, const int32_t* context_lens, int num_seqs,
+                                 int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                                 int num_blocks, float scale, pkv_dtype q_dtype,
+                                 pkv_dtype cache_dtype, float k_scale, float v_scale,
+                                 int partition_tokens, const int32_t* partition_offsets,
+                                 int total_partitions, void* workspace, size_t workspace_bytes,
+                                 void* stream);
 
 /* paged_attention_decode_partials -- the first of the two launches above on
  * its own: writes `out` for sequences with a single partition and partials
@@ -461,6 +495,25 @@ int paged_kv_copy_blocks(void* key_cache, void* value_cache, const int32_t* pair
 int paged_kv_swap_blocks(void* dst_key_cache, void* dst_value_cache, const void* src_key_cache,
                          const void* src_value_cache, const int32_t* pairs, int num_pairs,
                          size_t block_bytes, int src_blocks, int dst_blocks, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * paged_kv_swap_blocks_dma -- paged_kv_swap_blocks with the copies made by
+ * the GPU's copy engines instead of a kernel, so that no compute unit works
+ * on them while a decode runs on another stream ("PagedAttention Kernel：大
+ * 模型推理优化的显存管理革新" §6: asynchronous copies on a stream of their
+ * own, beside the compute stream).  Same pools, pair semantics (ids out of
+ * range skip the pair) and errors, except:
+ *  pairs_host     [num_pairs][2] int32 in HOST memory, read during the call
+ *  Each run of pairs whose source and destination ids both step by one
+ *  becomes one asynchronous copy per pool on `stream` (a swap of a sequence
+ *  whose blocks were allocated together is a few long copies).  The call
+ *  returns once the copies are queued; the pools must stay alive until
+ *  `stream` reaches them.
+ * ------------------------------------------------------------------------- */
+int paged_kv_swap_blocks_dma(void* dst_key_cache, void* dst_value_cache,
+                             const void* src_key_cache, const void* src_value_cache,
+                             const int32_t* pairs_host, int num_pairs, size_t block_bytes,
+                             int src_blocks, int dst_blocks, void* stream);
 
 /* Device pointer of pinned host memory (hipHostGetDevicePointer); fails with
  * PKV_ERR_HIP for memory that is not pinned.  Host memory is only ever

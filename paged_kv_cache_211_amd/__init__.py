@@ -25,6 +25,7 @@ from ._native import PKV_BF16, PKV_F32, PKV_FP8_E4M3, PkvError, check, lib
 
 __all__ = [
     "PkvError", "paged_kv_write", "paged_attention_decode", "paged_attention_decode_partials",
+    "paged_attention_decode_queue", "paged_kv_swap_blocks_dma",
     "paged_attention_splitk_reduce", "paged_kv_copy_blocks", "paged_kv_gather",
     "paged_attention_partition_offsets", "paged_attention_workspace_bytes", "BlockAllocator",
     "empty_pools", "cache_dtype_code", "pkv_hbm_read_probe",
@@ -178,6 +179,18 @@ def paged_attention_decode_noalloc(out, query, key_cache, value_cache, block_tab
         block_tables.shape[1], _ptr(context_lens), S, Hq, H, D, bs, nb, float(scale),
         cache_dtype_code(query), cache_dtype_code(key_cache), float(k_scale), float(v_scale),
         int(partition_tokens), _ptr(partition_offsets), int(total_partitions), _stream(stream)))
+
+
+def paged_attention_decode_queue(out, query, key_cache, value_cache, block_tables, context_lens,
+                                 scale, k_scale=1.0, v_scale=1.0, partition_tokens=0,
+                                 partition_offsets=None, total_partitions=0, workspace=None,
+                                 stream=None):
+    """paged_attention_decode's split-K with items handed out by a device
+    work counter (fp8 matrix-core shape only; same result bit for bit)."""
+    args = _decode_args(out, query, key_cache, value_cache, block_tables, context_lens, scale,
+                        k_scale, v_scale, partition_tokens, partition_offsets, total_partitions,
+                        workspace)
+    check(lib().paged_attention_decode_queue(*args, _stream(stream)))
 
 
 def paged_attention_decode_partials(out, query, key_cache, value_cache, block_tables, context_lens,
@@ -449,6 +462,22 @@ def paged_kv_swap_blocks(dst_key, dst_value, src_key, src_value, pairs, stream=N
         _pool_ptr(dst_key, "dst_key"), _pool_ptr(dst_value, "dst_value"),
         _pool_ptr(src_key, "src_key"), _pool_ptr(src_value, "src_value"), _ptr(pairs),
         pairs.numel() // 2, block_bytes, nbs, nbd, _stream(stream)))
+
+
+def paged_kv_swap_blocks_dma(dst_key, dst_value, src_key, src_value, pairs, stream=None):
+    """paged_kv_swap_blocks by the copy engines: pairs is a host int32 array
+    [n][2]; each run of consecutive (src, dst) ids is one asynchronous copy
+    per pool on `stream`."""
+    nbs, H, D, bs = _pool_shape(src_key, src_value)
+    nbd, Hd, Dd, bsd = _pool_shape(dst_key, dst_value)
+    if (H, D, bs) != (Hd, Dd, bsd) or src_key.dtype != dst_key.dtype:
+        raise PkvError(-1, "source and destination pools differ in layout")
+    p = np.ascontiguousarray(np.asarray(pairs, dtype=np.int32).reshape(-1, 2))
+    block_bytes = H * bs * D * src_key.element_size()
+    check(lib().paged_kv_swap_blocks_dma(
+        _pool_ptr(dst_key, "dst_key"), _pool_ptr(dst_value, "dst_value"),
+        _pool_ptr(src_key, "src_key"), _pool_ptr(src_value, "src_value"),
+        p.ctypes.data_as(_native.pi32), p.shape[0], block_bytes, nbs, nbd, _stream(stream)))
 
 
 def paged_kv_gather(k_out, v_out, key_cache, value_cache, block_tables, cu_ctx, total_tokens,

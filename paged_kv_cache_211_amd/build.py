@@ -34,8 +34,12 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (expected /opt/rocm/bin/hipcc)")
 
 
+# -amdgpu-atomic-optimizer-strategy=None: the persistent decode's work-counter
+# add must not be rewritten into a wave-aggregated add whose result is
+# broadcast (and so waited for) right away; its result is read a tile later.
 FLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
          "-Wno-unused-command-line-argument"]
 
 

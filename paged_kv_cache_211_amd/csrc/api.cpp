@@ -48,6 +48,8 @@ static int check_decode(const DecodeCall& c, DecodeArgs* a) {
     const size_t need = paged_attention_workspace_bytes(c.total_partitions, c.num_q_heads, c.head_dim);
     if (!c.workspace || c.workspace_bytes < need)
       return fail(PKV_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", need, c.workspace_bytes);
+    if ((uintptr_t)c.workspace % 16 != 0)
+      return fail(PKV_ERR_WORKSPACE, "workspace must be 16-byte aligned");
   }
   if ((size_t)c.num_blocks * c.block_size > (size_t)INT32_MAX)
     return fail(PKV_ERR_INVALID, "num_blocks * block_size exceeds int32 slots");
@@ -80,8 +82,14 @@ int decode_common(const DecodeCall& c, bool reduce, void* stream) {
   DecodeArgs a;
   int rc = check_decode(c, &a);
   if (rc) return rc;
+  if (c.queue && !decode_queue_supported(a))
+    return fail(PKV_ERR_UNSUPPORTED,
+                "the work-counter decode needs an fp8 E4M3 cache, bf16 queries, head_dim 128, "
+                "block_size 32, a multiple of 8 query heads per kv head, split-K partitions of "
+                "at most 2048 tokens and at most 512 sequences");
   if (c.num_seqs == 0) return PKV_OK;
-  rc = hip_status(launch_decode(a, stream), "paged_attention_decode launch");
+  rc = hip_status(c.queue ? launch_decode_mfma_queue(a, stream) : launch_decode(a, stream),
+                  "paged_attention_decode launch");
   if (rc || !reduce || c.partition_tokens == 0) return rc;
   return hip_status(launch_splitk_reduce(c.out, a.ws, c.partition_offsets, c.num_seqs,
                                          c.num_q_heads, c.head_dim, c.total_partitions,
@@ -140,6 +148,22 @@ int paged_attention_decode(void* out, const void* query, const void* key_cache,
                num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, scale,
                q_dtype, cache_dtype, k_scale, v_scale, partition_tokens, partition_offsets,
                total_partitions, workspace, workspace_bytes};
+  return decode_common(c, true, stream);
+}
+
+int paged_attention_decode_queue(void* out, const void* query, const void* key_cache,
+                                 const void* value_cache, const int32_t* block_tables,
+                                 int max_blocks_per_seq, const int32_t* context_lens, int num_seqs,
+                                 int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                                 int num_blocks, float scale, pkv_dtype q_dtype,
+                                 pkv_dtype cache_dtype, float k_scale, float v_scale,
+                                 int partition_tokens, const int32_t* partition_offsets,
+                                 int total_partitions, void* workspace, size_t workspace_bytes,
+                                 void* stream) {
+  DecodeCall c{out, query, key_cache, value_cache, block_tables, max_blocks_per_seq, context_lens,
+               num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, scale,
+               q_dtype, cache_dtype, k_scale, v_scale, partition_tokens, partition_offsets,
+               total_partitions, workspace, workspace_bytes, true};
   return decode_common(c, true, stream);
 }
 
@@ -528,6 +552,51 @@ int paged_kv_swap_blocks(void* dst_key_cache, void* dst_value_cache, const void*
                                        src_value_cache, pairs, num_pairs, block_bytes, src_blocks,
                                        dst_blocks, stream),
                     "paged_kv_swap_blocks launch");
+}
+
+int paged_kv_swap_blocks_dma(void* dst_key_cache, void* dst_value_cache,
+                             const void* src_key_cache, const void* src_value_cache,
+                             const int32_t* pairs_host, int num_pairs, size_t block_bytes,
+                             int src_blocks, int dst_blocks, void* stream) {
+  if (num_pairs < 0 || src_blocks <= 0 || dst_blocks <= 0) return fail(PKV_ERR_INVALID, "bad sizes");
+  if (num_pairs == 0) {
+    clear_error();
+    return PKV_OK;
+  }
+  if (!dst_key_cache || !dst_value_cache || !src_key_cache || !src_value_cache || !pairs_host)
+    return fail(PKV_ERR_INVALID, "null pointer argument");
+  if (block_bytes == 0 || block_bytes % 16 != 0)
+    return fail(PKV_ERR_INVALID, "block_bytes must be a positive multiple of 16");
+  hipStream_t st = (hipStream_t)stream;
+  // runs of pairs whose source and destination ids both step by one: one
+  // copy per run and pool
+  int i = 0;
+  while (i < num_pairs) {
+    const int s0 = pairs_host[2 * i], d0 = pairs_host[2 * i + 1];
+    if ((unsigned)s0 >= (unsigned)src_blocks || (unsigned)d0 >= (unsigned)dst_blocks) {
+      ++i;
+      continue;
+    }
+    int n = 1;
+    while (i + n < num_pairs && pairs_host[2 * (i + n)] == s0 + n &&
+           pairs_host[2 * (i + n) + 1] == d0 + n && s0 + n < src_blocks && d0 + n < dst_blocks)
+      ++n;
+    const size_t off_s = (size_t)s0 * block_bytes, off_d = (size_t)d0 * block_bytes;
+    const size_t bytes = (size_t)n * block_bytes;
+    int rc = hip_status(hipMemcpyAsync((uint8_t*)dst_key_cache + off_d,
+                                       (const uint8_t*)src_key_cache + off_s, bytes,
+                                       hipMemcpyDefault, st),
+                        "paged_kv_swap_blocks_dma copy");
+    if (!rc)
+      rc = hip_status(hipMemcpyAsync((uint8_t*)dst_value_cache + off_d,
+                                     (const uint8_t*)src_value_cache + off_s, bytes,
+                                     hipMemcpyDefault, st),
+                      "paged_kv_swap_blocks_dma copy");
+    if (rc) return rc;
+    i += n;
+  }
+  clear_error();
+  return PKV_OK;
 }
 
 int pkv_host_device_pointer(const void* host, void** device_out) {

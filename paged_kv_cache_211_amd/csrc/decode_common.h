@@ -87,16 +87,22 @@ __device__ __forceinline__ int find_seq(const int32_t* __restrict__ part_off, in
 // part_off[s] + part.
 constexpr int kOrderChunks = 8;
 
+// part_off / lens: the partition offsets and lengths to read (the
+// arguments' device arrays, or a copy of them in LDS).
 template <int BS>
 __device__ __forceinline__ void split_slot(const DecodeArgs& a, int x, int lane, int& s,
-                                           int& part) {
+                                           int& part, const int32_t* __restrict__ part_off,
+                                           const int32_t* __restrict__ lens) {
   const int S = a.S;
   const int F = a.total_parts - S;
   auto in_order = [&] {
-    s = __builtin_amdgcn_readfirstlane(find_seq(a.part_off, S, x, lane));
-    part = x - a.part_off[s];
+    // clamped: offsets that end below total_parts leave slots past the last
+    // sequence's partitions, which then cover no tokens (their partial rows
+    // are never read)
+    s = min(__builtin_amdgcn_readfirstlane(find_seq(part_off, S, x, lane)), S - 1);
+    part = x - part_off[s];
   };
-  if (S > 64 * kOrderChunks || F < 0 || a.part_off[S] != a.total_parts) {
+  if (S > 64 * kOrderChunks || F < 0 || part_off[S] != a.total_parts) {
     in_order();
     return;
   }
@@ -106,7 +112,7 @@ __device__ __forceinline__ void split_slot(const DecodeArgs& a, int x, int lane,
     bool empty = false;   // a sequence without partitions
     for (int base = 1; base <= S; base += 64) {
       const int i = base + lane;
-      const int hi = i <= S ? a.part_off[i] : 0, lo = i <= S ? a.part_off[i - 1] : 0;
+      const int hi = i <= S ? part_off[i] : 0, lo = i <= S ? part_off[i - 1] : 0;
       c += __popcll(__ballot(i <= S && hi - i <= x));
       empty |= __ballot(i <= S && hi - lo < 1) != 0;
     }
@@ -115,7 +121,7 @@ __device__ __forceinline__ void split_slot(const DecodeArgs& a, int x, int lane,
       return;
     }
     s = __builtin_amdgcn_readfirstlane(c);
-    part = x - (a.part_off[s] - s);
+    part = x - (part_off[s] - s);
     return;
   }
   const int r = x - F;                      // rank among the last partitions, < S
@@ -128,9 +134,9 @@ __device__ __forceinline__ void split_slot(const DecodeArgs& a, int x, int lane,
     key[ch] = -1;                           // no sequence: never counted
     int n = 1;
     if (ch * 64 < S && i < S) {
-      int L = a.lens[i];
+      int L = lens[i];
       L = L < 0 ? 0 : min(L, a.max_blocks * BS);
-      n = a.part_off[i + 1] - a.part_off[i];
+      n = part_off[i + 1] - part_off[i];
       const int t = L - (n - 1) * a.partition;
       key[ch] = min(max((t + BS - 1) / BS, 0), kmax);
     }
@@ -170,7 +176,7 @@ __device__ __forceinline__ void split_slot(const DecodeArgs& a, int x, int lane,
     }
   }
   s = __builtin_amdgcn_readfirstlane(found);
-  part = a.part_off[s + 1] - a.part_off[s] - 1;
+  part = part_off[s + 1] - part_off[s] - 1;
 }
 
 // One 16-byte load of streamed key/value data.
@@ -215,10 +221,10 @@ __device__ __forceinline__ Work locate(const DecodeArgs& a, int hpw, int lane, i
   int tstart = 0;
   if constexpr (SPLIT) {
     if (a.t_start) {
-      wk.s = __builtin_amdgcn_readfirstlane(find_seq(a.part_off, a.S, item, lane));
+      wk.s = min(__builtin_amdgcn_readfirstlane(find_seq(a.part_off, a.S, item, lane)), a.S - 1);
       part = item - a.part_off[wk.s];
     } else {
-      split_slot<BS>(a, item, lane, wk.s, part);
+      split_slot<BS>(a, item, lane, wk.s, part, a.part_off, a.lens);
     }
     wk.p0 = a.part_off[wk.s];
     wk.item = wk.p0 + part;

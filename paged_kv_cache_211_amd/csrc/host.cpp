@@ -55,7 +55,7 @@ int paged_attention_partition_offsets(const int32_t* context_lens_host, int num_
 
 size_t paged_attention_workspace_bytes(int total_partitions, int num_q_heads, int head_dim) {
   if (total_partitions <= 0 || num_q_heads <= 0 || head_dim <= 0) return 0;
-  return (size_t)total_partitions * num_q_heads * (head_dim + 2) * sizeof(float);
+  return (size_t)total_partitions * num_q_heads * (head_dim + 2) * sizeof(float) + kWorkspaceTail;
 }
 
 int paged_attention_tile_offsets(const int32_t* context_lens_host, int num_seqs, int block_size,

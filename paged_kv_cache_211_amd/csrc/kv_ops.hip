@@ -191,34 +191,37 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(uint8_t* __restrict__ 
   for (size_t i = threadIdx.x; i < n; i += 256) d[i] = s[i];
 }
 
-// Whole blocks between two pools of one layout (a device pool and a pinned
-// host pool reached through its device pointer): workgroup (i, pool) copies
-// src block pairs[i][0] to dst block pairs[i][1], four 16-byte units per
-// thread in flight (loads from host memory cross the host link, so many
-// must be outstanding).  Ids out of range skip the pair.
+// Whole-block moves between two pools: unit u = (pair u / 2, pool u % 2)
+// copies src block pairs[i][0] to dst block pairs[i][1] of the key (pool 0)
+// or value (pool 1) pool.  A bounded grid walks the units (grid stride),
+// four 16-byte units per thread in flight, and leaves most wave slots to
+// kernels of other streams.  Ids out of range skip the pair.
 __global__ __launch_bounds__(256) void swap_blocks_kernel(uint8_t* __restrict__ dk,
                                                           uint8_t* __restrict__ dv,
                                                           const uint8_t* __restrict__ sk,
                                                           const uint8_t* __restrict__ sv,
                                                           const int32_t* __restrict__ pairs,
-                                                          size_t block_bytes, int src_nb,
-                                                          int dst_nb) {
-  const int src = pairs[2 * blockIdx.x], dst = pairs[2 * blockIdx.x + 1];
-  if ((unsigned)src >= (unsigned)src_nb || (unsigned)dst >= (unsigned)dst_nb) return;
-  const u32x4* s = (const u32x4*)((blockIdx.y == 0 ? sk : sv) + (size_t)src * block_bytes);
-  u32x4* d = (u32x4*)((blockIdx.y == 0 ? dk : dv) + (size_t)dst * block_bytes);
+                                                          int n_pairs, size_t block_bytes,
+                                                          int src_nb, int dst_nb) {
   const size_t n = block_bytes / 16;
-  for (size_t i0 = threadIdx.x; i0 < n; i0 += 4 * 256) {
-    u32x4 v[4];
+  for (int unit = blockIdx.x; unit < 2 * n_pairs; unit += gridDim.x) {
+    const int i = unit >> 1, pool = unit & 1;
+    const int src = pairs[2 * i], dst = pairs[2 * i + 1];
+    if ((unsigned)src >= (unsigned)src_nb || (unsigned)dst >= (unsigned)dst_nb) continue;
+    const u32x4* s = (const u32x4*)((pool == 0 ? sk : sv) + (size_t)src * block_bytes);
+    u32x4* d = (u32x4*)((pool == 0 ? dk : dv) + (size_t)dst * block_bytes);
+    for (size_t i0 = threadIdx.x; i0 < n; i0 += 4 * 256) {
+      u32x4 v[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const size_t i = i0 + (size_t)u * 256;
-      if (i < n) v[u] = s[i];
-    }
+      for (int u = 0; u < 4; ++u) {
+        const size_t j = i0 + (size_t)u * 256;
+        if (j < n) v[u] = s[j];
+      }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const size_t i = i0 + (size_t)u * 256;
-      if (i < n) d[i] = v[u];
+      for (int u = 0; u < 4; ++u) {
+        const size_t j = i0 + (size_t)u * 256;
+        if (j < n) d[j] = v[u];
+      }
     }
   }
 }
@@ -341,11 +344,19 @@ int launch_copy_blocks(void* kc, void* vc, const int32_t* pairs, int n, size_t b
   return (int)hipGetLastError();
 }
 
+// Workgroups of a swap launch: 256 x 16 KiB in flight, which streams an
+// HBM-to-HBM move (the staging copy of a swap) at HBM rates and covers the
+// host link's bandwidth-delay product many times over.  With a host pool on
+// one side, 8 to 256 workgroups all reach ~55 GB/s on MI355X and all slow a
+// decode running beside them (2x to 2.3x); the copy engines do not.
+constexpr int kSwapWorkgroups = 256;
+
 int launch_swap_blocks(void* dk, void* dv, const void* sk, const void* sv, const int32_t* pairs,
                        int n, size_t block_bytes, int src_nb, int dst_nb, void* stream) {
   if (n == 0) return 0;
-  hipLaunchKernelGGL(swap_blocks_kernel, dim3(n, 2), dim3(256), 0, (hipStream_t)stream,
-                     (uint8_t*)dk, (uint8_t*)dv, (const uint8_t*)sk, (const uint8_t*)sv, pairs,
+  const int wgs = (int)std::min<long long>(2ll * n, kSwapWorkgroups);
+  hipLaunchKernelGGL(swap_blocks_kernel, dim3(wgs), dim3(256), 0, (hipStream_t)stream,
+                     (uint8_t*)dk, (uint8_t*)dv, (const uint8_t*)sk, (const uint8_t*)sv, pairs, n,
                      block_bytes, src_nb, dst_nb);
   return (int)hipGetLastError();
 }

@@ -50,7 +50,14 @@ struct DecodeArgs {
   const int32_t* t_start = nullptr;
   const int32_t* row_off = nullptr;
   int ws_rows = 0;   // partial rows of the workspace when not total_parts
+  // Work-counter split-K launches: a number unique to the launch, which tags
+  // the counter in the workspace's last bytes (after the partials).
+  unsigned long long epoch = 0;
 };
+
+// Bytes after the split-K partials in a workspace: the work counter of the
+// work-counter decode (one 64-bit word, padded).
+constexpr size_t kWorkspaceTail = 256;
 
 // The arguments of a decode entry point, as the C ABI receives them.
 struct DecodeCall {
@@ -70,6 +77,7 @@ struct DecodeCall {
   int total_partitions;
   void* workspace;
   size_t workspace_bytes;
+  bool queue = false;   // paged_attention_decode_queue: the work-counter schedule
 };
 
 // paged_attention_decode's checks and launches (api.cpp): the decode
@@ -139,6 +147,10 @@ int launch_prefill(const PrefillArgs& a, void* stream);
 // (decode_mfma.hip); launch_decode routes eligible calls there.
 bool decode_mfma_eligible(const DecodeArgs& a);
 int launch_decode_mfma(const DecodeArgs& a, void* stream, bool store = false);
+// The work-counter split-K schedule (fp8 matrix-core shape only): whether a
+// call qualifies, and its launch.
+bool decode_queue_supported(const DecodeArgs& a);
+int launch_decode_mfma_queue(const DecodeArgs& a, void* stream);
 int launch_decode_mfma_sk(const DecodeArgs& a, void* stream, bool store);
 int decode_mfma_sk_workers();
 // min_parts: sequences with fewer rows are left alone (2 for split-K, whose

@@ -13,11 +13,13 @@ import numpy as np
 import torch
 
 from . import (BlockAllocator, empty_pools, paged_attention_decode, paged_attention_decode_prefix,
+               paged_attention_decode_queue,
                paged_attention_decode_step, paged_attention_prefix_plan,
                paged_attention_decode_step_streamk, paged_attention_decode_streamk,
                paged_attention_partition_offsets, paged_attention_streamk_workers,
                paged_attention_streamk_workspace_bytes, paged_attention_tile_offsets,
                paged_attention_workspace_bytes, paged_kv_copy_blocks, paged_kv_swap_blocks,
+               paged_kv_swap_blocks_dma,
                paged_kv_write)
 
 
@@ -35,6 +37,7 @@ class PagedKVCache:
             self.key_cache.view(torch.uint8).fill_(fill_byte)
             self.value_cache.view(torch.uint8).fill_(fill_byte)
         self._ws = None
+        self._stage = None
 
     # -- allocation and writes ------------------------------------------------
     def add_seq(self, seq: int):
@@ -77,23 +80,72 @@ class PagedKVCache:
                                                      self.dtype, "cpu", pin=True)
         self.alloc.set_host_pool(num_host_blocks)
 
-    def swap_out(self, seq: int, stream=None):
-        """Move seq's blocks to host slots; its device blocks become free
-        (later writes to them are ordered after this copy on the stream)."""
+    def _pairs(self, pairs, stream):
+        """The pair list on the device, uploaded on the stream that reads it
+        (so the caching allocator never hands its memory to another stream
+        while the copy may still read it)."""
+        p = torch.from_numpy(np.ascontiguousarray(np.asarray(pairs, dtype=np.int32)))
+        if stream is None:
+            return p.to(self.device)
+        with torch.cuda.stream(stream):
+            return p.to(self.device)
+
+    def swap_out(self, seq: int, stream=None, dma: bool = True):
+        """Move seq's blocks to host slots; its device blocks become free.
+        With a stream of its own the copy overlaps work on other streams
+        (a decode of the sequences that stay); the caller orders any later
+        write into the freed blocks after it (an event).  dma=True (the
+        default): the blocks are gathered into a device staging pool (one
+        launch, HBM to HBM) and the copy engines move that to the host
+        slots, one copy per run of consecutive slots, so no compute unit
+        waits on the host link (a decode beside it keeps its speed); swaps
+        that use the staging pool must run on one stream.  dma=False: one
+        kernel moves the blocks straight to the host slots."""
         pairs = self.alloc.swap_out(seq)
         if pairs:
-            p = torch.tensor(pairs, dtype=torch.int32).to(self.device)
-            paged_kv_swap_blocks(self.host_key, self.host_value, self.key_cache, self.value_cache,
-                                 p, stream=stream)
+            if dma:
+                p = np.asarray(pairs, dtype=np.int32).reshape(-1, 2)
+                sk, sv = self._staging(len(p), stream)
+                idx = np.arange(len(p), dtype=np.int32)
+                paged_kv_swap_blocks(sk, sv, self.key_cache, self.value_cache,
+                                     self._pairs(np.stack([p[:, 0], idx], 1), stream), stream=stream)
+                paged_kv_swap_blocks_dma(self.host_key, self.host_value, sk, sv,
+                                         np.stack([idx, p[:, 1]], 1), stream=stream)
+            else:
+                paged_kv_swap_blocks(self.host_key, self.host_value, self.key_cache,
+                                     self.value_cache, self._pairs(pairs, stream), stream=stream)
         return pairs
 
-    def swap_in(self, seq: int, stream=None):
+    def swap_in(self, seq: int, stream=None, dma: bool = True):
+        """Move seq back into free device blocks; with a stream of its own,
+        the caller orders seq's next decode after the copy (an event).
+        dma=True: the copy engines bring the host slots into the staging
+        pool, one launch scatters them to the device blocks."""
         pairs = self.alloc.swap_in(seq)
         if pairs:
-            p = torch.tensor(pairs, dtype=torch.int32).to(self.device)
-            paged_kv_swap_blocks(self.key_cache, self.value_cache, self.host_key, self.host_value,
-                                 p, stream=stream)
+            if dma:
+                p = np.asarray(pairs, dtype=np.int32).reshape(-1, 2)
+                sk, sv = self._staging(len(p), stream)
+                idx = np.arange(len(p), dtype=np.int32)
+                paged_kv_swap_blocks_dma(sk, sv, self.host_key, self.host_value,
+                                         np.stack([p[:, 0], idx], 1), stream=stream)
+                paged_kv_swap_blocks(self.key_cache, self.value_cache, sk, sv,
+                                     self._pairs(np.stack([idx, p[:, 1]], 1), stream), stream=stream)
+            else:
+                paged_kv_swap_blocks(self.key_cache, self.value_cache, self.host_key,
+                                     self.host_value, self._pairs(pairs, stream), stream=stream)
         return pairs
+
+    def _staging(self, n, stream):
+        """Device staging pools of >= n blocks (grown on demand, reused), made
+        on the stream that uses them."""
+        if self._stage is None or self._stage[0].shape[0] < n:
+            if stream is None:
+                self._stage = empty_pools(n, self.H, self.D, self.bs, self.dtype, self.device)
+            else:
+                with torch.cuda.stream(stream):
+                    self._stage = empty_pools(n, self.H, self.D, self.bs, self.dtype, self.device)
+        return self._stage
 
     def write(self, key, value, slot_mapping, stream=None):
         paged_kv_write(key, value, self.key_cache, self.value_cache, slot_mapping,
@@ -231,7 +283,9 @@ class PagedKVCache:
                                     stream=stream)
         return out
 
-    def decode(self, query, inp, scale, out=None, stream=None):
+    def decode(self, query, inp, scale, out=None, stream=None, queue=False):
+        """Decode with the schedule inp describes; queue=True takes split-K's
+        work-counter form (paged_attention_decode_queue)."""
         S, Hq, D = query.shape
         out = torch.empty_like(query) if out is None else out
         if inp.get("prefix") is not None:
@@ -252,10 +306,9 @@ class PagedKVCache:
         ws = None
         if inp["partition_tokens"]:
             ws = self.workspace(inp["total_partitions"], Hq, D)
-        paged_attention_decode(out, query, self.key_cache, self.value_cache, inp["block_tables"],
-                               inp["context_lens"], scale, k_scale=self.k_scale,
-                               v_scale=self.v_scale, partition_tokens=inp["partition_tokens"],
-                               partition_offsets=inp["partition_offsets"],
-                               total_partitions=inp["total_partitions"], workspace=ws,
-                               stream=stream)
+        fn = paged_attention_decode_queue if queue else paged_attention_decode
+        fn(out, query, self.key_cache, self.value_cache, inp["block_tables"], inp["context_lens"],
+           scale, k_scale=self.k_scale, v_scale=self.v_scale,
+           partition_tokens=inp["partition_tokens"], partition_offsets=inp["partition_offsets"],
+           total_partitions=inp["total_partitions"], workspace=ws, stream=stream)
         return out

@@ -56,11 +56,12 @@ def check_host_pool(cache, hk, hv, st, wl, victims):
             assert np.array_equal(dv[h][:, :, :n * e], ov[h][:, :, :n * e]), (v, j, h)
 
 
+@pytest.mark.parametrize("dma", [False, True], ids=["kernel", "copy-engines"])
 @pytest.mark.parametrize("cfg_id,n_out", [(3, 1), (3, 2), (2, 3), (5, 2)])
-def test_swap_round_trip(cfg_id, n_out):
+def test_swap_round_trip(cfg_id, n_out, dma):
     wl = synth.make(synth.SMALL[cfg_id])
     c = wl.cfg
-    _case(f"swap {n_out} sequence(s) out and back, config {c.key}")
+    _case(f"swap {n_out} sequence(s) out and back, config {c.key}, {'dma' if dma else 'kernel'}")
     st, _ = replay.build(wl)
     cache, step = H.build(wl, poison=True)
     nh = int(sum(len(st.model.table(s)) for s in range(c.S)))
@@ -74,7 +75,7 @@ def test_swap_round_trip(cfg_id, n_out):
     for _ in range(n_out):
         v = cache.alloc.lru()
         assert v == st.model.lru()
-        pairs = cache.swap_out(v)
+        pairs = cache.swap_out(v, dma=dma)
         assert pairs == st.model.swap_out(v)
         OL.move_blocks(hk, hv, st.kc, st.vc, pairs)
         victims.append(v)
@@ -99,7 +100,7 @@ def test_swap_round_trip(cfg_id, n_out):
     st.model.free_seq(FILLER)
 
     for v in reversed(victims):
-        pairs = cache.swap_in(v)
+        pairs = cache.swap_in(v, dma=dma)
         assert pairs == st.model.swap_in(v)
         OL.move_blocks(st.kc, st.vc, hk, hv, pairs)
     torch.cuda.synchronize()
@@ -135,3 +136,71 @@ def test_host_pointer_needs_pinned_memory():
         host_device_pointer(torch.empty(16, dtype=torch.uint8))
     t = torch.empty(4096, dtype=torch.uint8, pin_memory=True)
     assert host_device_pointer(t) != 0
+
+
+@pytest.mark.parametrize("dma", [False, True], ids=["kernel", "copy-engines"])
+@pytest.mark.parametrize("cfg_id", [3, 5])
+def test_swap_on_a_second_stream_overlapped_with_decode(cfg_id, dma):
+    """Victims move to the host pool and back on a second stream (default
+    priority) while the other sequences decode on the main stream: the
+    residents' outputs, the host-pool bits and, after the swap back, every
+    sequence's cache bits and output match the oracle."""
+    wl = synth.make(synth.SMALL[cfg_id])
+    c = wl.cfg
+    _case(f"swap on a second stream during decode, config {c.key}, {'dma' if dma else 'kernel'}")
+    st, _ = replay.build(wl)
+    cache, step = H.build(wl, poison=True)
+    nh = int(sum(len(st.model.table(s)) for s in range(c.S)))
+    cache.host_pool(nh)
+    st.model.set_host_pool(nh)
+    hk, hv = OL.empty_pools(nh, c.H_kv, c.d, c.bs, c.kv_dtype, fill=0)
+    cache.host_key.zero_()
+    cache.host_value.zero_()
+    ref, _ = oracle_out(wl, st)
+    main, side = torch.cuda.current_stream(), torch.cuda.Stream()
+    start = torch.cuda.Event()
+    start.record(main)
+    side.wait_event(start)
+    victims = []
+    for _ in range(2):
+        v = cache.alloc.lru()
+        assert v == st.model.lru()
+        pairs = cache.swap_out(v, stream=side, dma=dma)
+        assert pairs == st.model.swap_out(v)
+        OL.move_blocks(hk, hv, st.kc, st.vc, pairs)
+        victims.append(v)
+    residents = [s for s in range(c.S) if s not in victims]
+    inp = cache.decode_inputs(residents, c.partition)
+    q = step["query"][residents].contiguous()
+
+    def decode_residents():
+        out = torch.full_like(q, float("nan"))
+        cache.decode(q, inp, c.scale, out=out)
+        return out
+
+    outs = [decode_residents() for _ in range(3)]       # on the main stream, beside the copies
+    done = torch.cuda.Event()
+    done.record(side)
+    main.wait_event(done)
+    torch.cuda.synchronize()
+    for o in outs:
+        got = o.double().cpu().numpy()
+        assert np.isfinite(got).all()
+        assert np.abs(got - ref[residents]).max() <= TOL[c.kv_dtype]
+    check_host_pool(cache, hk, hv, st, wl, victims)
+    # back in on the second stream, residents decoding meanwhile
+    start.record(main)
+    side.wait_event(start)
+    for v in reversed(victims):
+        pairs = cache.swap_in(v, stream=side, dma=dma)
+        assert pairs == st.model.swap_in(v)
+        OL.move_blocks(st.kc, st.vc, hk, hv, pairs)
+    outs = [decode_residents() for _ in range(3)]
+    done.record(side)
+    main.wait_event(done)
+    torch.cuda.synchronize()
+    for o in outs:
+        assert np.abs(o.double().cpu().numpy() - ref[residents]).max() <= TOL[c.kv_dtype]
+    check_cache_bits(cache, st, wl, np.arange(c.S))
+    got = gpu_decode(cache, step, wl, c.partition)
+    assert np.abs(got - ref).max() <= TOL[c.kv_dtype]

@@ -317,6 +317,25 @@ def test_decode_argument_validation_needs_no_gpu(pkv):
     assert call(P=32, off=fake, tot=2, ws=fake, wsb=10) == -3
     assert call(P=32, off=None, tot=2, ws=fake, wsb=1 << 30) == -1
     assert call(scale=float("nan")) == -1
+
+    # the work-counter decode takes only the fp8 matrix-core shape, split-K
+    # partitions of at most 2048 tokens and at most 512 sequences
+    def qcall(**kw):
+        a = dict(good, cd=2, Hq=16, Hkv=2, bs=32, P=512, off=fake, tot=600, ws=fake, wsb=1 << 30)
+        a.update(kw)
+        return L.paged_attention_decode_queue(a["out"], a["q"], a["kc"], a["vc"], a["tb"], a["mb"],
+                                              a["lens"], a["S"], a["Hq"], a["Hkv"], a["D"], a["bs"],
+                                              a["nb"], a["scale"], a["qd"], a["cd"], a["ks"], a["vs"],
+                                              a["P"], a["off"], a["tot"], a["ws"], a["wsb"], None)
+
+    assert qcall(cd=1) == -2                # bf16 cache
+    assert b"work-counter" in L.pkv_last_error()
+    assert qcall(bs=16) == -2
+    assert qcall(Hq=12, Hkv=2) == -2        # 6 query heads per kv head
+    assert qcall(P=0, off=None, tot=0, ws=None, wsb=0) == -2   # one pass
+    assert qcall(P=4096) == -2
+    assert qcall(S=513, tot=600) == -2
+    assert qcall(P=24) == -1                # the common checks come first
     # the no-alloc decode refuses partials beyond its static array before
     # touching any device
     rows = _native.PKV_NOALLOC_WORKSPACE_BYTES // (8 * 130 * 4) + 1
@@ -333,6 +352,11 @@ def test_decode_argument_validation_needs_no_gpu(pkv):
     w = L.paged_kv_write(fake, fake, fake, fake, fake, 4, 2, 128, 16, 10, 0, 1, 1.0, 1.0, None)
     assert w == -2
     assert L.paged_kv_copy_blocks(fake, fake, fake, 3, 100, 10, None) == -1
+    pairs = (ctypes.c_int32 * 6)(0, 1, 1, 2, 2, 3)
+    assert L.paged_kv_swap_blocks_dma(fake, fake, fake, fake, None, 3, 64, 10, 10, None) == -1
+    assert L.paged_kv_swap_blocks_dma(fake, fake, fake, fake, pairs, 3, 8, 10, 10, None) == -1
+    assert L.paged_kv_swap_blocks_dma(fake, fake, fake, fake, pairs, -1, 64, 10, 10, None) == -1
+    assert L.paged_kv_swap_blocks_dma(None, fake, fake, fake, pairs, 0, 64, 10, 10, None) == 0
     assert L.paged_attention_splitk_reduce(fake, fake, 16, fake, 2, 8, 128, 2, 0, 1, None) == -3
 
     # chunked prefill: the same host checks, bf16 / head_dim 128 / block 16 only
