@@ -55,7 +55,8 @@ constexpr int kReduceRowsInFlight = 32;
 // partitions), or kReduceRowsInFlight*PL, all loads -- the (m, l) pairs and
 // every partial row -- go out at once: the weights then come from registers
 // and the partial rows are already in flight while the maxima are reduced,
-// one memory round trip in all instead of three or more.
+// one memory round trip in all instead of three or more; up to twice
+// kReduceRowsInFlight*PL pieces take two.
 template <int D, bool F32OUT, int HG, bool WIDE = false>
 __device__ __forceinline__ void merge_heads(void* __restrict__ out, size_t oi0,
                                             const float* __restrict__ ws_o,
@@ -143,6 +144,71 @@ __device__ __forceinline__ void merge_heads(void* __restrict__ out, size_t oi0,
     __syncthreads();   // every thread has read red / w_lds before finish reuses red
     finish(acc, p_t < n ? l_own * w_own : 0.f);
   };
+  // up to twice that: the (m, l) pairs (two per thread) and the first half
+  // of the partial rows go out at once, the second half as soon as the
+  // first is summed -- two round trips
+  auto two_trips = [&]() {
+    constexpr int UNR = kReduceRowsInFlight;
+    float m_own[2], l_own[2], w_own[2];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int p = p_t + k * PSTEP;
+      m_own[k] = -INFINITY;
+      l_own[k] = 0.f;
+      if (p < n) {
+        const f32x2 ml = *(const f32x2*)(ws_ml + (row0 + (size_t)p * pstride + hh_t) * 2);
+        m_own[k] = ml.x;
+        l_own[k] = ml.y;
+      }
+    }
+    const float* op = ws_o + (row0 + hh_e) * D + d4;
+    const size_t ps = pstride * D;
+    f32x4 v[UNR];
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      const int p = pl + u * PL;
+      v[u] = p < n ? *(const f32x4*)(op + (size_t)p * ps) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    red[tid] = fmaxf(m_own[0], m_own[1]);
+    __syncthreads();
+    for (int k = NT / 2; k >= HG; k >>= 1) {
+      if (tid < k) red[tid] = fmaxf(red[tid], red[tid + k]);
+      __syncthreads();
+    }
+    const float M_t = red[hh_t];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int p = p_t + k * PSTEP;
+      w_own[k] = p < n && M_t != -INFINITY ? __builtin_amdgcn_exp2f(m_own[k] - M_t) : 0.f;
+      if (p < n) w_lds[p][hh_t] = w_own[k];
+    }
+    __syncthreads();
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int pb = half * UNR * PL;
+      if (half == 1) {
+#pragma unroll
+        for (int u = 0; u < UNR; ++u) {
+          const int p = pb + pl + u * PL;
+          v[u] = p < n ? *(const f32x4*)(op + (size_t)p * ps) : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < UNR; ++u) {
+        const int p = pb + pl + u * PL;
+        if (p < n) {
+          const float w = w_lds[p][hh_e];
+          acc.x = fmaf(v[u].x, w, acc.x);
+          acc.y = fmaf(v[u].y, w, acc.y);
+          acc.z = fmaf(v[u].z, w, acc.z);
+          acc.w = fmaf(v[u].w, w, acc.w);
+        }
+      }
+    }
+    __syncthreads();   // every thread has read red / w_lds before finish reuses red
+    finish(acc, l_own[0] * w_own[0] + l_own[1] * w_own[1]);
+  };
   if (n <= 4 * PL && n <= PSTEP) {
     one_trip(std::integral_constant<int, 4>());
     return;
@@ -150,6 +216,10 @@ __device__ __forceinline__ void merge_heads(void* __restrict__ out, size_t oi0,
   if constexpr (WIDE) {
     if (n <= kReduceRowsInFlight * PL && n <= PSTEP) {
       one_trip(std::integral_constant<int, kReduceRowsInFlight>());
+      return;
+    }
+    if (n <= 2 * kReduceRowsInFlight * PL && n <= 2 * PSTEP) {
+      two_trips();
       return;
     }
   }

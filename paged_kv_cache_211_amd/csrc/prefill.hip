@@ -127,11 +127,10 @@ void prefill_kernel(const PrefillArgs a) {
   const int pl = row_ok ? row / G : C - 1;       // chunk position (padding rows: the last)
   const int qh = hkv * G + (row_ok ? row % G : 0);
   const int p = L - C + pl;                       // tokens 0 .. p are visible to this row
-  // first and last row's positions of this wave and of the workgroup;
+  // first row's position of this wave and last row's of the workgroup;
   // uniform (the divisions expand on the vector ALUs, so their results are
   // moved back to scalar registers)
   const int p_min = __builtin_amdgcn_readfirstlane(L - C + min(row0, nrows - 1) / G);
-  const int p_max = __builtin_amdgcn_readfirstlane(L - C + min(nrows - 1, row0 + kRows - 1) / G);
   const int wg_last = min(nrows - 1, wg_row0 + kNW * kRows - 1);
   const int wg_p_max = __builtin_amdgcn_readfirstlane(L - C + wg_last / G);
   const int nblk = bad ? 0 : (wg_p_max + kBS) / kBS;   // blocks holding tokens 0 .. wg_p_max
@@ -186,6 +185,31 @@ void prefill_kernel(const PrefillArgs a) {
     }
   };
 
+  // Value tokens past the workgroup's last position (wg_p_max) exist only in
+  // its last pair; their probabilities are 0 for every row, but the bytes
+  // may lie past the context (anything, NaN included) or repeat the pair's
+  // first block.  Once that pair is in LDS, the workgroup zeroes them there
+  // (2 blocks x 128 dim rows x 2 halves = 512 units of 8 tokens), so the
+  // product loop needs no per-pair masking.  Tokens up to wg_p_max are
+  // context tokens, finite like every stored value.
+  auto zero_value_tail = [&](int st, int jp) {   // workgroup-uniform jp
+    const int zero_from = wg_p_max + 1 - 32 * jp;   // first pair token to zero
+    if (zero_from >= 32) return;
+    for (int u = threadIdx.x; u < 512; u += kNW * 64) {
+      const int b = u >> 8, d = (u >> 1) & 127, h = u & 1;
+      const int keep = min(max(zero_from - (16 * b + 8 * h), 0), 8);   // tokens kept, 0..8
+      if (keep == 8) continue;
+      u32x4* unit = (u32x4*)(ring[st] + (2 + b) * kTile + vunit(d, h) * 16);
+      u32x4 v = *unit;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int k2 = keep - 2 * e;   // tokens kept in this dword
+        v[e] &= k2 >= 2 ? 0xffffffffu : k2 == 1 ? 0x0000ffffu : 0u;
+      }
+      *unit = v;
+    }
+  };
+
   // ---- operands from LDS ----
   // key row of A for this lane: token sigma(col) of block col / 16
   const int kt = col & 15;
@@ -215,28 +239,37 @@ void prefill_kernel(const PrefillArgs a) {
     for (int r = 0; r < 16; ++r) acc[m][r] = 0.f;
   const bf16x2 ones = __builtin_bit_cast(bf16x2, 0x3f803f80u);
 
-  // Pipeline: pair jp + 2 streams into LDS while pair jp + 1's QK^T runs on
-  // the matrix cores and pair jp's softmax on the vector ALUs.  One barrier
-  // per pair: after it, pair jp + 1 is in LDS (every wave waited for its own
-  // quarter first) and every wave is done with pair jp - 1's stage, which
-  // pair jp + 2 then overwrites.
+  // Pipeline: pairs up to jp + kAhead stream into LDS while pair jp + 1's
+  // QK^T runs on the matrix cores and pair jp's softmax and PV on the
+  // vector ALUs and matrix cores.  One barrier per pair: before it, every
+  // wave waits until its own quarter of pair jp + 1 has landed (later pairs'
+  // loads may stay in flight: loads complete in order, 4 per pair), so after
+  // it pair jp + 1 is in LDS and every wave is done with pair jp - 1's
+  // stage, which pair jp + kAhead then overwrites.
+  constexpr int kAhead = kStages - 1;
+  static_assert(kAhead >= 2 && 4 * (kAhead - 2) <= 15, "stage count");
+  // s_waitcnt: vector loads <= 4 (kAhead - 2), LDS and scalar loads done
+  constexpr int kTopWait = 4 * (kAhead - 2) | (7 << 4);
   f32x16 sc = {};
   if (npairs > 0) {
-    stage_pair(0, 0);
-    if (npairs > 1) stage_pair(1, 1);
+#pragma unroll
+    for (int i = 0; i < kAhead; ++i)
+      if (i < npairs) stage_pair(i, i);
     __builtin_amdgcn_s_waitcnt(0);   // all loads, query rows included
     __syncthreads();
+    if (npairs == 1) zero_value_tail(0, 0);   // published by the loop's first barrier
     if (active) sc = qk_scores(0);
   }
   for (int jp = 0; jp < npairs; ++jp) {
     const int t0 = 32 * jp;   // first token of the pair
     const int st = jp % kStages;
-    __builtin_amdgcn_s_waitcnt(0);   // this wave's quarter of pair jp + 1
+    __builtin_amdgcn_s_waitcnt(kTopWait);   // this wave's quarter of pair jp + 1
     __syncthreads();
-    if (jp + 2 < npairs) stage_pair(jp + 2, (jp + 2) % kStages);
+    if (jp + kAhead < npairs) stage_pair(jp + kAhead, (jp + kAhead) % kStages);
+    // pair jp + 1 is in LDS (its keys are read below, its values next
+    // iteration, after the next barrier)
+    if (jp + 2 == npairs) zero_value_tail((jp + 1) % kStages, jp + 1);
     if (!active) continue;
-    f32x16 sn = {};
-    if (jp + 1 < npairs) sn = qk_scores((jp + 1) % kStages);   // next pair's scores
 
     // ---- tokens after the row's position are hidden (diagonal pairs only) ----
     // register 8b + i holds token t0 + 16b + 8g + i
@@ -266,48 +299,62 @@ void prefill_kernel(const PrefillArgs a) {
         for (int r = 0; r < 16; ++r) acc[m][r] *= c;
     }
     // P^T as the B operand: bf16 of exp2(qk s - m), eight tokens per block;
-    // the row sum adds the same bf16 values
+    // the row sum adds the same bf16 values.  In the same block, the next
+    // pair's scores (its stage is in LDS: the barrier above covers pair
+    // jp + 1; after the last pair the stage holds stale bytes whose scores
+    // are never used): each link of that dependent chain of 8 matrix-core
+    // products is followed by a share of the exponentials, so the vector ALU
+    // works while the matrix core does instead of after it.
     u32x4 pb[2];
+    // this block and the products below feed the matrix core: the wave asks
+    // for issue priority over the other waves of its SIMD until it is done
+    __builtin_amdgcn_s_setprio(1);
+    f32x16 sn;
+    {
+      const uint8_t* kp = ring[(jp + 1) % kStages] + koff;
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      uint32_t w4[4];
+      for (int r = 0; r < 16; ++r) sn[r] = 0.f;
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const f32x2 e = {__builtin_amdgcn_exp2f(__builtin_fmaf(sc[8 * b + 2 * k], qk, -m_run)),
-                         __builtin_amdgcn_exp2f(__builtin_fmaf(sc[8 * b + 2 * k + 1], qk, -m_run))};
-        const bf16x2 pk = __builtin_convertvector(e, bf16x2);
-        l_run = __builtin_amdgcn_fdot2_f32_bf16(pk, ones, l_run, false);
-        w4[k] = __builtin_bit_cast(uint32_t, pk);
+      for (int sl = 0; sl < 8; ++sl) {
+        const u32x4 k = *(const u32x4*)(kp + sl * 2 * kBS * 16);
+        sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(k), as_bf16x8(qv[sl]), sn, 0, 0, 0);
       }
-      pb[b] = u32x4{w4[0], w4[1], w4[2], w4[3]};
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        uint32_t w4[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const f32x2 e = {__builtin_amdgcn_exp2f(__builtin_fmaf(sc[8 * b + 2 * k], qk, -m_run)),
+                           __builtin_amdgcn_exp2f(__builtin_fmaf(sc[8 * b + 2 * k + 1], qk, -m_run))};
+          const bf16x2 pk = __builtin_convertvector(e, bf16x2);
+          l_run = __builtin_amdgcn_fdot2_f32_bf16(pk, ones, l_run, false);
+          w4[k] = __builtin_bit_cast(uint32_t, pk);
+        }
+        pb[b] = u32x4{w4[0], w4[1], w4[2], w4[3]};
+      }
+      // schedule: two key reads ahead, each product followed by 5 vector
+      // ops and the next key read
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+        if (i < 6) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
     }
 
     // ---- O^T += V^T P^T, block by block, value rows from LDS ----
-    // value rows of tokens past the wave's last position are zeroed: their
-    // probabilities are 0, but bytes past the context may hold anything
-    const bool tail = t0 + 31 > p_max;
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
       const uint8_t* vt = ring[st] + (2 + b) * kTile;
-      u32x4 vr[4];
 #pragma unroll
-      for (int m = 0; m < 4; ++m) vr[m] = *(const u32x4*)(vt + vunit(32 * m + col, g) * 16);
-      if (tail) {
-        const int first = t0 + 16 * b + 8 * g;   // token of the lane's first value
-        const int keep = min(max(p_max + 1 - first, 0), 8);   // tokens kept, 0..8
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int k2 = keep - 2 * e;   // tokens kept in this dword
-          const uint32_t msk = k2 >= 2 ? 0xffffffffu : k2 == 1 ? 0x0000ffffu : 0u;
-#pragma unroll
-          for (int m = 0; m < 4; ++m) vr[m][e] &= msk;
-        }
+      for (int m = 0; m < 4; ++m) {
+        const u32x4 vr = *(const u32x4*)(vt + vunit(32 * m + col, g) * 16);
+        acc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vr), as_bf16x8(pb[b]), acc[m],
+                                                         0, 0, 0);
       }
-#pragma unroll
-      for (int m = 0; m < 4; ++m)
-        acc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vr[m]), as_bf16x8(pb[b]),
-                                                         acc[m], 0, 0, 0);
     }
+    __builtin_amdgcn_s_setprio(0);
     sc = sn;
   }
 

@@ -320,3 +320,41 @@ def test_stale_partition_offsets_poison_only_their_sequences(cfg_id):
     assert np.isnan(got[1]).all() and np.isnan(got[2]).all()
     for s in (0, 3, 4):
         assert np.abs(got[s] - ref[s]).max() <= tol, s
+
+
+@pytest.mark.parametrize("cfg_id", [3, 5])
+def test_many_partials_every_reduce_path(cfg_id):
+    """Sequences of 1, 16, 17, 128, 129, 256 and 257 partitions of one block
+    each (the reduce's one-trip, wide one-trip, two-trip and chunked paths,
+    with their boundaries) against the oracle, through decode + reduce and
+    through the standalone reduce."""
+    base = synth.SMALL[cfg_id]
+    bs = base.bs
+    counts = [1, 16, 17, 128, 129, 256, 257]
+    lens = [n * bs - (3 if n > 1 else 0) for n in counts]
+    wl = _custom(cfg_id, lens, seed=23)
+    c = wl.cfg
+    _case(f"many partials, config {cfg_id}: {counts} partitions of {bs} tokens")
+    st, _ = replay.build(wl)
+    ref, _ = oracle_out(wl, st)
+    cache, step = H.build(wl, poison=True)
+    got = gpu_decode(cache, step, wl, bs)
+    assert np.isfinite(got).all()
+    err = np.abs(got - ref).max(axis=(1, 2))
+    print(f"  per-sequence max abs err {err}", flush=True)
+    assert (err <= TOL[c.kv_dtype]).all()
+    # the two launches on their own: the reduce sized by the longest sequence
+    import paged_kv_cache_211_amd as pkv
+    inp = cache.decode_inputs(range(c.S), bs)
+    ws = cache.workspace(inp["total_partitions"], c.H_q, c.d)
+    out = torch.full_like(step["query"], float("nan"))
+    pkv.paged_attention_decode_partials(out, step["query"], cache.key_cache, cache.value_cache,
+                                        inp["block_tables"], inp["context_lens"], c.scale,
+                                        c.k_scale, c.v_scale, bs, inp["partition_offsets"],
+                                        inp["total_partitions"], ws)
+    pkv.paged_attention_splitk_reduce(out, ws, inp["partition_offsets"], inp["total_partitions"],
+                                      max(counts))
+    torch.cuda.synchronize()
+    # same kernels, same reduce build: the same bits (bf16 values are exact in fp64)
+    assert np.array_equal(out.view(torch.int16).cpu().numpy(),
+                          torch.from_numpy(got).to(out.dtype).view(torch.int16).numpy())
