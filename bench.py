@@ -117,7 +117,9 @@ def src_sha():
 
 def load_traffic(path, workload_key, kernel):
     """HBM bytes per launch of `kernel` from committed rocprofv3 counter runs,
-    or None when absent, for another kernel or taken on other sources."""
+    or None when absent, for another kernel or taken on other sources.
+    workload_key names the workload, with "-p<P>" when the launch uses
+    another split-K length than the workload's own."""
     path = path or os.path.join(ROOT, "profiles", f"traffic_{workload_key}.json")
     if not os.path.exists(path):
         return None
@@ -764,7 +766,8 @@ def main():
         kernel = ("decode (stream-K)" if SK else "decode (split-K partials)" if P else "decode")
         kern_us, kern_bytes = dec_only_us, ab["decode"]
     achieved = kern_bytes / (kern_us * 1e-6) / 1e9
-    traffic = load_traffic(args.traffic_file, c.key, kernel)
+    traffic = load_traffic(args.traffic_file,
+                           c.key if P == c.partition or SK or PF else f"{c.key}-p{P}", kernel)
     log(f"[bench] mode {args.mode}: step {us_step:.1f} us (wall {wall / args.steps * 1e6:.1f} us); "
         f"step entry {fused_us:.1f} us in {n_launch} launch(es); separate launches: "
         f"write {np.mean(t_write):.1f} us, decode {dec_us:.1f} us "
