@@ -26,8 +26,9 @@ Prints ONE JSON line on stdout; details go to stderr.
     python bench.py --swap
 
 --swap times moving whole sequences of the GQA workload to a pinned host
-pool and back: staged through a device pool and moved by the copy engines
-(the headline), and by the block-move kernel straight to the host; then
+pool and back: staged through a device pool and moved as whole-run
+asynchronous copies (the headline), and by the block-move kernel straight
+to the host; then
 each form on a second stream beside a split-K decode of the other
 sequences.  Its roofline is the host link (PCIe 5.0 x16, 64 GB/s each way).
 """
@@ -358,25 +359,25 @@ def main_swap(args):
     out_pairs = torch.from_numpy(np.stack([dblk, hslot], 1).copy()).to(dev)
     in_pairs = torch.from_numpy(np.stack([hslot, dblk], 1).copy()).to(dev)
     # the staged form: device blocks <-> a contiguous device staging pool (one
-    # launch, HBM to HBM), staging pool <-> host slots by the copy engines
+    # launch, HBM to HBM), staging pool <-> host slots as whole-run copies
     stage_k, stage_v = pkv.empty_pools(nblocks, c.H_kv, c.d, c.bs, cache.dtype, dev)
     gather_pairs = torch.from_numpy(np.stack([dblk, hslot], 1).copy()).to(dev)   # dev -> stage
     scatter_pairs = torch.from_numpy(np.stack([hslot, dblk], 1).copy()).to(dev)  # stage -> dev
     ident = np.stack([hslot, hslot], 1).copy()                                  # stage <-> host
 
-    def d2h(stream=None, dma=False):
-        if dma:
+    def d2h(stream=None, staged=False):
+        if staged:
             pkv.paged_kv_swap_blocks(stage_k, stage_v, cache.key_cache, cache.value_cache,
                                      gather_pairs, stream=stream)
-            pkv.paged_kv_swap_blocks_dma(cache.host_key, cache.host_value, stage_k, stage_v,
+            pkv.paged_kv_swap_blocks_memcpy(cache.host_key, cache.host_value, stage_k, stage_v,
                                          ident, stream=stream)
         else:
             pkv.paged_kv_swap_blocks(cache.host_key, cache.host_value, cache.key_cache,
                                      cache.value_cache, out_pairs, stream=stream)
 
-    def h2d(stream=None, dma=False):
-        if dma:
-            pkv.paged_kv_swap_blocks_dma(stage_k, stage_v, cache.host_key, cache.host_value,
+    def h2d(stream=None, staged=False):
+        if staged:
+            pkv.paged_kv_swap_blocks_memcpy(stage_k, stage_v, cache.host_key, cache.host_value,
                                          ident, stream=stream)
             pkv.paged_kv_swap_blocks(cache.key_cache, cache.value_cache, stage_k, stage_v,
                                      scatter_pairs, stream=stream)
@@ -384,26 +385,26 @@ def main_swap(args):
             pkv.paged_kv_swap_blocks(cache.key_cache, cache.value_cache, cache.host_key,
                                      cache.host_value, in_pairs, stream=stream)
 
-    def time_alone(dma):
+    def time_alone(staged):
         e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
         for _ in range(args.warmup):
-            d2h(dma=dma)
-            h2d(dma=dma)
+            d2h(staged=staged)
+            h2d(staged=staged)
         torch.cuda.synchronize()
         e[0].record()
         for _ in range(args.steps):
-            d2h(dma=dma)
+            d2h(staged=staged)
         e[1].record()
         for _ in range(args.steps):
-            h2d(dma=dma)
+            h2d(staged=staged)
         e[2].record()
         torch.cuda.synchronize()
         return (e[0].elapsed_time(e[1]) / args.steps * 1e3,
                 e[1].elapsed_time(e[2]) / args.steps * 1e3)
 
     out_us, in_us = time_alone(False)
-    dma_out_us, dma_in_us = time_alone(True)
-    # the whole call path: allocator swap pairs, the staging copy, the copy engines
+    staged_out_us, staged_in_us = time_alone(True)
+    # the whole call path: allocator swap pairs, the staging launch, the copies
     t0 = time.perf_counter()
     steps = max(1, args.steps // 5)
     for _ in range(steps):
@@ -416,10 +417,10 @@ def main_swap(args):
     gbps_out, gbps_in = moved / (out_us * 1e-6) / 1e9, moved / (in_us * 1e-6) / 1e9
     log(f"[bench] swap kernel: device->host {out_us:.1f} us = {gbps_out:.1f} GB/s, host->device "
         f"{in_us:.1f} us = {gbps_in:.1f} GB/s; per-sequence engine calls round trip {rt_us:.0f} us")
-    log(f"[bench] swap staged through a device pool, copy engines on the host link: "
-        f"device->host {dma_out_us:.1f} us = "
-        f"{moved / (dma_out_us * 1e-6) / 1e9:.1f} GB/s, host->device {dma_in_us:.1f} us = "
-        f"{moved / (dma_in_us * 1e-6) / 1e9:.1f} GB/s")
+    log(f"[bench] swap staged through a device pool, whole-run copies on the host link: "
+        f"device->host {staged_out_us:.1f} us = "
+        f"{moved / (staged_out_us * 1e-6) / 1e9:.1f} GB/s, host->device {staged_in_us:.1f} us = "
+        f"{moved / (staged_in_us * 1e-6) / 1e9:.1f} GB/s")
 
     # overlap: the other sequences decode (split-K) on the main stream while
     # the victims' blocks go to the host pool and back on a second stream of
@@ -451,12 +452,12 @@ def main_swap(args):
     torch.cuda.synchronize()
     dec_alone = ev[0].elapsed_time(ev[1]) * 1e3 / n_dec
 
-    def overlap_of(dma, rt_alone):
+    def overlap_of(staged, rt_alone):
         # both at once: the side stream starts when the main stream does
         ev[2].record(main_st)
         side.wait_event(ev[2])
-        d2h(side, dma)
-        h2d(side, dma)
+        d2h(side, staged)
+        h2d(side, staged)
         ev[3].record(side)
         for _ in range(n_dec):
             decode_residents()
@@ -468,7 +469,7 @@ def main_swap(args):
         swap_during = ev[2].elapsed_time(ev[3]) * 1e3
         both = ev[2].elapsed_time(ev[5]) * 1e3
         serial = dec_alone * n_dec + rt_alone
-        log(f"[bench] overlap ({'staged, copy engines' if dma else 'swap kernel'}): {n_dec} decode steps "
+        log(f"[bench] overlap ({'staged, whole-run copies' if staged else 'swap kernel'}): {n_dec} decode steps "
             f"of {len(residents)} sequences {dec_alone:.1f} us each alone, {dec_during:.1f} us while "
             f"swapping; swap round trip {rt_alone:.0f} us alone, {swap_during:.0f} us beside the "
             f"decode; both {both:.0f} us vs {serial:.0f} us one after the other")
@@ -480,11 +481,11 @@ def main_swap(args):
 
     overlap = {"decode_steps": n_dec, "decode_sequences": len(residents),
                "swap_kernel": overlap_of(False, out_us + in_us),
-               "staged_copy_engines": overlap_of(True, dma_out_us + dma_in_us)}
+               "staged": overlap_of(True, staged_out_us + staged_in_us)}
     # the headline is the staged form (the engine's swap path)
-    rt = dma_out_us + dma_in_us
-    dma_gbps_out, dma_gbps_in = moved / (dma_out_us * 1e-6) / 1e9, moved / (dma_in_us * 1e-6) / 1e9
-    slow = min(dma_gbps_out, dma_gbps_in)
+    rt = staged_out_us + staged_in_us
+    staged_gbps_out, staged_gbps_in = moved / (staged_out_us * 1e-6) / 1e9, moved / (staged_in_us * 1e-6) / 1e9
+    slow = min(staged_gbps_out, staged_gbps_in)
     line = {
         "metric": SWAP_METRIC, "value": round(rt, 2), "unit": "us/round-trip",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -492,19 +493,19 @@ def main_swap(args):
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": f"{c.key}: sequences 0..{n - 1} ({nblocks} blocks of "
                                f"{block_bytes * 2} bytes) to a pinned host pool and back, "
-                               f"staged through a device pool, copy engines on the host link",
+                               f"staged through a device pool, whole-run copies on the host link",
                    "parallelism": "single GPU"},
         "kernel_us": {"swap_device_to_host": round(out_us, 2), "swap_host_to_device": round(in_us, 2),
                       "swap_calls_round_trip": round(rt_us, 1),
-                      "staged_copy_engines_device_to_host": round(dma_out_us, 2),
-                      "staged_copy_engines_host_to_device": round(dma_in_us, 2)},
+                      "staged_device_to_host": round(staged_out_us, 2),
+                      "staged_host_to_device": round(staged_in_us, 2)},
         "overlap_with_decode": overlap,
         "roofline": {"bound": "host-link", "achieved": round(slow, 2), "peak": HOST_LINK_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(slow / HOST_LINK_PEAK_GBPS, 4), "traffic": None,
-                     "kernel": "staging copy + copy engines (slower direction)",
+                     "kernel": "staging launch + whole-run copies (slower direction)",
                      "algorithmic_bytes_per_launch": moved,
-                     "device_to_host_GBps": round(dma_gbps_out, 2),
-                     "host_to_device_GBps": round(dma_gbps_in, 2),
+                     "device_to_host_GBps": round(staged_gbps_out, 2),
+                     "host_to_device_GBps": round(staged_gbps_in, 2),
                      "swap_kernel_device_to_host_GBps": round(gbps_out, 2),
                      "swap_kernel_host_to_device_GBps": round(gbps_in, 2)},
         "cpu_baseline": None,

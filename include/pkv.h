@@ -497,20 +497,23 @@ int paged_kv_swap_blocks(void* dst_key_cache, void* dst_value_cache, const void*
                          size_t block_bytes, int src_blocks, int dst_blocks, void* stream);
 
 /* ---------------------------------------------------------------------------
- * paged_kv_swap_blocks_dma -- paged_kv_swap_blocks with the copies made by
- * the GPU's copy engines instead of a kernel, so that no compute unit works
- * on them while a decode runs on another stream ("PagedAttention Kernel：大
- * 模型推理优化的显存管理革新" §6: asynchronous copies on a stream of their
- * own, beside the compute stream).  Same pools, pair semantics (ids out of
- * range skip the pair) and errors, except:
+ * paged_kv_swap_blocks_memcpy -- paged_kv_swap_blocks as asynchronous copies
+ * of whole runs: each run of pairs whose source and destination ids both
+ * step by one becomes one hipMemcpyAsync per pool on `stream` ("PagedAttention
+ * Kernel：大模型推理优化的显存管理革新" §6: asynchronous copies on a stream of
+ * their own, beside the compute stream).  For a swap, the engine first
+ * gathers a sequence's scattered blocks into a contiguous device staging
+ * pool with paged_kv_swap_blocks (HBM to HBM), so the host-link copy is a
+ * few long runs; on MI355X a decode running beside those copies keeps its
+ * speed, where beside paged_kv_swap_blocks straight to the host it slows
+ * down 2.3x.  Same pools, pair semantics (ids out of range skip the pair)
+ * and errors as paged_kv_swap_blocks, except:
  *  pairs_host     [num_pairs][2] int32 in HOST memory, read during the call
- *  Each run of pairs whose source and destination ids both step by one
- *  becomes one asynchronous copy per pool on `stream` (a swap of a sequence
- *  whose blocks were allocated together is a few long copies).  The call
- *  returns once the copies are queued; the pools must stay alive until
- *  `stream` reaches them.
+ *  The call returns once the copies are queued; the pools must stay alive
+ *  until `stream` reaches them.  How the runtime carries out a copy (its
+ *  copy kernels or a DMA engine) is the runtime's choice.
  * ------------------------------------------------------------------------- */
-int paged_kv_swap_blocks_dma(void* dst_key_cache, void* dst_value_cache,
+int paged_kv_swap_blocks_memcpy(void* dst_key_cache, void* dst_value_cache,
                              const void* src_key_cache, const void* src_value_cache,
                              const int32_t* pairs_host, int num_pairs, size_t block_bytes,
                              int src_blocks, int dst_blocks, void* stream);

@@ -25,7 +25,7 @@ from ._native import PKV_BF16, PKV_F32, PKV_FP8_E4M3, PkvError, check, lib
 
 __all__ = [
     "PkvError", "paged_kv_write", "paged_attention_decode", "paged_attention_decode_partials",
-    "paged_attention_decode_queue", "paged_kv_swap_blocks_dma",
+    "paged_attention_decode_queue", "paged_kv_swap_blocks_memcpy",
     "paged_attention_splitk_reduce", "paged_kv_copy_blocks", "paged_kv_gather",
     "paged_attention_partition_offsets", "paged_attention_workspace_bytes", "BlockAllocator",
     "empty_pools", "cache_dtype_code", "pkv_hbm_read_probe",
@@ -464,17 +464,17 @@ def paged_kv_swap_blocks(dst_key, dst_value, src_key, src_value, pairs, stream=N
         pairs.numel() // 2, block_bytes, nbs, nbd, _stream(stream)))
 
 
-def paged_kv_swap_blocks_dma(dst_key, dst_value, src_key, src_value, pairs, stream=None):
-    """paged_kv_swap_blocks by the copy engines: pairs is a host int32 array
-    [n][2]; each run of consecutive (src, dst) ids is one asynchronous copy
-    per pool on `stream`."""
+def paged_kv_swap_blocks_memcpy(dst_key, dst_value, src_key, src_value, pairs, stream=None):
+    """paged_kv_swap_blocks as asynchronous copies: pairs is a host int32
+    array [n][2]; each run of consecutive (src, dst) ids is one
+    hipMemcpyAsync per pool on `stream`."""
     nbs, H, D, bs = _pool_shape(src_key, src_value)
     nbd, Hd, Dd, bsd = _pool_shape(dst_key, dst_value)
     if (H, D, bs) != (Hd, Dd, bsd) or src_key.dtype != dst_key.dtype:
         raise PkvError(-1, "source and destination pools differ in layout")
     p = np.ascontiguousarray(np.asarray(pairs, dtype=np.int32).reshape(-1, 2))
     block_bytes = H * bs * D * src_key.element_size()
-    check(lib().paged_kv_swap_blocks_dma(
+    check(lib().paged_kv_swap_blocks_memcpy(
         _pool_ptr(dst_key, "dst_key"), _pool_ptr(dst_value, "dst_value"),
         _pool_ptr(src_key, "src_key"), _pool_ptr(src_value, "src_value"),
         p.ctypes.data_as(_native.pi32), p.shape[0], block_bytes, nbs, nbd, _stream(stream)))

@@ -554,7 +554,7 @@ int paged_kv_swap_blocks(void* dst_key_cache, void* dst_value_cache, const void*
                     "paged_kv_swap_blocks launch");
 }
 
-int paged_kv_swap_blocks_dma(void* dst_key_cache, void* dst_value_cache,
+int paged_kv_swap_blocks_memcpy(void* dst_key_cache, void* dst_value_cache,
                              const void* src_key_cache, const void* src_value_cache,
                              const int32_t* pairs_host, int num_pairs, size_t block_bytes,
                              int src_blocks, int dst_blocks, void* stream) {
@@ -586,12 +586,12 @@ int paged_kv_swap_blocks_dma(void* dst_key_cache, void* dst_value_cache,
     int rc = hip_status(hipMemcpyAsync((uint8_t*)dst_key_cache + off_d,
                                        (const uint8_t*)src_key_cache + off_s, bytes,
                                        hipMemcpyDefault, st),
-                        "paged_kv_swap_blocks_dma copy");
+                        "paged_kv_swap_blocks_memcpy copy");
     if (!rc)
       rc = hip_status(hipMemcpyAsync((uint8_t*)dst_value_cache + off_d,
                                      (const uint8_t*)src_value_cache + off_s, bytes,
                                      hipMemcpyDefault, st),
-                      "paged_kv_swap_blocks_dma copy");
+                      "paged_kv_swap_blocks_memcpy copy");
     if (rc) return rc;
     i += n;
   }

@@ -348,7 +348,8 @@ int launch_copy_blocks(void* kc, void* vc, const int32_t* pairs, int n, size_t b
 // HBM-to-HBM move (the staging copy of a swap) at HBM rates and covers the
 // host link's bandwidth-delay product many times over.  With a host pool on
 // one side, 8 to 256 workgroups all reach ~55 GB/s on MI355X and all slow a
-// decode running beside them (2x to 2.3x); the copy engines do not.
+// decode running beside them (1.9x to 2.3x); whole-run asynchronous copies
+// of a staged sequence do not (paged_kv_swap_blocks_memcpy).
 constexpr int kSwapWorkgroups = 256;
 
 int launch_swap_blocks(void* dk, void* dv, const void* sk, const void* sv, const int32_t* pairs,

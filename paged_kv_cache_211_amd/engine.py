@@ -19,7 +19,7 @@ from . import (BlockAllocator, empty_pools, paged_attention_decode, paged_attent
                paged_attention_partition_offsets, paged_attention_streamk_workers,
                paged_attention_streamk_workspace_bytes, paged_attention_tile_offsets,
                paged_attention_workspace_bytes, paged_kv_copy_blocks, paged_kv_swap_blocks,
-               paged_kv_swap_blocks_dma,
+               paged_kv_swap_blocks_memcpy,
                paged_kv_write)
 
 
@@ -90,44 +90,44 @@ class PagedKVCache:
         with torch.cuda.stream(stream):
             return p.to(self.device)
 
-    def swap_out(self, seq: int, stream=None, dma: bool = True):
+    def swap_out(self, seq: int, stream=None, staged: bool = True):
         """Move seq's blocks to host slots; its device blocks become free.
         With a stream of its own the copy overlaps work on other streams
         (a decode of the sequences that stay); the caller orders any later
-        write into the freed blocks after it (an event).  dma=True (the
+        write into the freed blocks after it (an event).  staged=True (the
         default): the blocks are gathered into a device staging pool (one
-        launch, HBM to HBM) and the copy engines move that to the host
-        slots, one copy per run of consecutive slots, so no compute unit
-        waits on the host link (a decode beside it keeps its speed); swaps
-        that use the staging pool must run on one stream.  dma=False: one
-        kernel moves the blocks straight to the host slots."""
+        launch, HBM to HBM) and moved to the host slots by one asynchronous
+        copy per run of consecutive slots (paged_kv_swap_blocks_memcpy), so
+        a decode beside it keeps its speed; swaps that use the staging pool
+        must run on one stream.  staged=False: one kernel moves the blocks
+        straight to the host slots."""
         pairs = self.alloc.swap_out(seq)
         if pairs:
-            if dma:
+            if staged:
                 p = np.asarray(pairs, dtype=np.int32).reshape(-1, 2)
                 sk, sv = self._staging(len(p), stream)
                 idx = np.arange(len(p), dtype=np.int32)
                 paged_kv_swap_blocks(sk, sv, self.key_cache, self.value_cache,
                                      self._pairs(np.stack([p[:, 0], idx], 1), stream), stream=stream)
-                paged_kv_swap_blocks_dma(self.host_key, self.host_value, sk, sv,
+                paged_kv_swap_blocks_memcpy(self.host_key, self.host_value, sk, sv,
                                          np.stack([idx, p[:, 1]], 1), stream=stream)
             else:
                 paged_kv_swap_blocks(self.host_key, self.host_value, self.key_cache,
                                      self.value_cache, self._pairs(pairs, stream), stream=stream)
         return pairs
 
-    def swap_in(self, seq: int, stream=None, dma: bool = True):
+    def swap_in(self, seq: int, stream=None, staged: bool = True):
         """Move seq back into free device blocks; with a stream of its own,
         the caller orders seq's next decode after the copy (an event).
-        dma=True: the copy engines bring the host slots into the staging
-        pool, one launch scatters them to the device blocks."""
+        staged=True: asynchronous copies bring the host slots into the
+        staging pool, one launch scatters them to the device blocks."""
         pairs = self.alloc.swap_in(seq)
         if pairs:
-            if dma:
+            if staged:
                 p = np.asarray(pairs, dtype=np.int32).reshape(-1, 2)
                 sk, sv = self._staging(len(p), stream)
                 idx = np.arange(len(p), dtype=np.int32)
-                paged_kv_swap_blocks_dma(sk, sv, self.host_key, self.host_value,
+                paged_kv_swap_blocks_memcpy(sk, sv, self.host_key, self.host_value,
                                          np.stack([p[:, 0], idx], 1), stream=stream)
                 paged_kv_swap_blocks(self.key_cache, self.value_cache, sk, sv,
                                      self._pairs(np.stack([idx, p[:, 1]], 1), stream), stream=stream)

@@ -56,12 +56,12 @@ def check_host_pool(cache, hk, hv, st, wl, victims):
             assert np.array_equal(dv[h][:, :, :n * e], ov[h][:, :, :n * e]), (v, j, h)
 
 
-@pytest.mark.parametrize("dma", [False, True], ids=["kernel", "copy-engines"])
+@pytest.mark.parametrize("staged", [False, True], ids=["kernel", "staged"])
 @pytest.mark.parametrize("cfg_id,n_out", [(3, 1), (3, 2), (2, 3), (5, 2)])
-def test_swap_round_trip(cfg_id, n_out, dma):
+def test_swap_round_trip(cfg_id, n_out, staged):
     wl = synth.make(synth.SMALL[cfg_id])
     c = wl.cfg
-    _case(f"swap {n_out} sequence(s) out and back, config {c.key}, {'dma' if dma else 'kernel'}")
+    _case(f"swap {n_out} sequence(s) out and back, config {c.key}, {'staged' if staged else 'kernel'}")
     st, _ = replay.build(wl)
     cache, step = H.build(wl, poison=True)
     nh = int(sum(len(st.model.table(s)) for s in range(c.S)))
@@ -75,7 +75,7 @@ def test_swap_round_trip(cfg_id, n_out, dma):
     for _ in range(n_out):
         v = cache.alloc.lru()
         assert v == st.model.lru()
-        pairs = cache.swap_out(v, dma=dma)
+        pairs = cache.swap_out(v, staged=staged)
         assert pairs == st.model.swap_out(v)
         OL.move_blocks(hk, hv, st.kc, st.vc, pairs)
         victims.append(v)
@@ -100,7 +100,7 @@ def test_swap_round_trip(cfg_id, n_out, dma):
     st.model.free_seq(FILLER)
 
     for v in reversed(victims):
-        pairs = cache.swap_in(v, dma=dma)
+        pairs = cache.swap_in(v, staged=staged)
         assert pairs == st.model.swap_in(v)
         OL.move_blocks(st.kc, st.vc, hk, hv, pairs)
     torch.cuda.synchronize()
@@ -138,16 +138,16 @@ def test_host_pointer_needs_pinned_memory():
     assert host_device_pointer(t) != 0
 
 
-@pytest.mark.parametrize("dma", [False, True], ids=["kernel", "copy-engines"])
+@pytest.mark.parametrize("staged", [False, True], ids=["kernel", "staged"])
 @pytest.mark.parametrize("cfg_id", [3, 5])
-def test_swap_on_a_second_stream_overlapped_with_decode(cfg_id, dma):
+def test_swap_on_a_second_stream_overlapped_with_decode(cfg_id, staged):
     """Victims move to the host pool and back on a second stream (default
     priority) while the other sequences decode on the main stream: the
     residents' outputs, the host-pool bits and, after the swap back, every
     sequence's cache bits and output match the oracle."""
     wl = synth.make(synth.SMALL[cfg_id])
     c = wl.cfg
-    _case(f"swap on a second stream during decode, config {c.key}, {'dma' if dma else 'kernel'}")
+    _case(f"swap on a second stream during decode, config {c.key}, {'staged' if staged else 'kernel'}")
     st, _ = replay.build(wl)
     cache, step = H.build(wl, poison=True)
     nh = int(sum(len(st.model.table(s)) for s in range(c.S)))
@@ -165,7 +165,7 @@ def test_swap_on_a_second_stream_overlapped_with_decode(cfg_id, dma):
     for _ in range(2):
         v = cache.alloc.lru()
         assert v == st.model.lru()
-        pairs = cache.swap_out(v, stream=side, dma=dma)
+        pairs = cache.swap_out(v, stream=side, staged=staged)
         assert pairs == st.model.swap_out(v)
         OL.move_blocks(hk, hv, st.kc, st.vc, pairs)
         victims.append(v)
@@ -192,7 +192,7 @@ def test_swap_on_a_second_stream_overlapped_with_decode(cfg_id, dma):
     start.record(main)
     side.wait_event(start)
     for v in reversed(victims):
-        pairs = cache.swap_in(v, stream=side, dma=dma)
+        pairs = cache.swap_in(v, stream=side, staged=staged)
         assert pairs == st.model.swap_in(v)
         OL.move_blocks(st.kc, st.vc, hk, hv, pairs)
     outs = [decode_residents() for _ in range(3)]

@@ -353,10 +353,10 @@ def test_decode_argument_validation_needs_no_gpu(pkv):
     assert w == -2
     assert L.paged_kv_copy_blocks(fake, fake, fake, 3, 100, 10, None) == -1
     pairs = (ctypes.c_int32 * 6)(0, 1, 1, 2, 2, 3)
-    assert L.paged_kv_swap_blocks_dma(fake, fake, fake, fake, None, 3, 64, 10, 10, None) == -1
-    assert L.paged_kv_swap_blocks_dma(fake, fake, fake, fake, pairs, 3, 8, 10, 10, None) == -1
-    assert L.paged_kv_swap_blocks_dma(fake, fake, fake, fake, pairs, -1, 64, 10, 10, None) == -1
-    assert L.paged_kv_swap_blocks_dma(None, fake, fake, fake, pairs, 0, 64, 10, 10, None) == 0
+    assert L.paged_kv_swap_blocks_memcpy(fake, fake, fake, fake, None, 3, 64, 10, 10, None) == -1
+    assert L.paged_kv_swap_blocks_memcpy(fake, fake, fake, fake, pairs, 3, 8, 10, 10, None) == -1
+    assert L.paged_kv_swap_blocks_memcpy(fake, fake, fake, fake, pairs, -1, 64, 10, 10, None) == -1
+    assert L.paged_kv_swap_blocks_memcpy(None, fake, fake, fake, pairs, 0, 64, 10, 10, None) == 0
     assert L.paged_attention_splitk_reduce(fake, fake, 16, fake, 2, 8, 128, 2, 0, 1, None) == -3
 
     # chunked prefill: the same host checks, bf16 / head_dim 128 / block 16 only
