@@ -12,8 +12,9 @@
 // bf16 blocks per step ("PagedAttention Kernel：大模型推理优化的显存管理革新"
 // §3.1: QK^T per block, softmax, PV; fp32 accumulation per §6).  Each wave
 // leaves one partial (m, l, unnormalised o) per row for its 8 blocks; the
-// sequences' own tokens are decoded by the split-K kernel from the end of the
-// prefix, and the split-K reduce combines both.
+// sequences' own tokens (from the end of the prefix) are decoded by one wave
+// per (sequence, kv head, split-K partition) with the vector-ALU per-tile
+// code, and the split-K reduce combines both.
 //
 // Lane layouts of the 32x32x16 bf16 MFMA (lane l, col = l % 32, g = l / 32):
 //   A[i][k]: lane holds row i = col, k = 8g .. 8g+7
@@ -231,18 +232,76 @@ void decode_prefix_kernel(const DecodeArgs a, PrefixArgs p) {
   prefix_body<NW>(a, p, blockIdx.x);
 }
 
+// The suffix pass with one wave per item: item x of the split-K schedule over
+// the sequences' own tokens (head group x % nhg, launch slot x / nhg, as in
+// decode_body), walked by this wave alone, its partial written to the row
+// the shared-prefix plan gives (row_off[s] + part).  The suffixes are short
+// (tens of blocks), so a wave that takes all of an item's tiles pays the
+// item's start (query, table, first tiles) once instead of four times and
+// needs no merge through LDS.
+template <int HPW>
+__device__ __forceinline__ void suffix_wave(const DecodeArgs& b, int x, int lane,
+                                            float (*p_w)[kPBS], u32x4* q_w) {
+  using St = valu::ValuHeads<PKV_BF16, kPD, kPBS, HPW, kQLds>;
+  constexpr int NLOAD = St::NLOAD, RU = St::RU, DPI = St::DPI, TILE = kPTile, D = kPD;
+  const int nhg = b.Hkv * (b.Hq / b.Hkv / HPW);
+  if (x >= b.total_parts * nhg) return;
+  const Work wk = locate<true, kPBS>(b, HPW, lane, x / nhg, x % nhg);
+  bool bad = wk.bad;
+  const int32_t* __restrict__ tbl = b.tables + (size_t)wk.s * b.max_blocks;
+  const size_t head_off = (size_t)wk.hkv * TILE;
+  St st;
+  if constexpr (kQLds) {
+    St::fill_q(b, wk.s, wk.qh0, q_w, lane, 64);
+    __builtin_amdgcn_wave_barrier();
+    st.qs = q_w;
+  } else {
+    st.load_q(b, wk.s, wk.qh0, lane);
+  }
+  st.reset();
+  const int t1 = wk.t1;
+  tile_loop<kBufs, NLOAD, 1>(tbl, wk.t0 / kPBS, wk.jend, b.nb,
+                             (const uint8_t*)b.kc + head_off + lane * 16,
+                             (const uint8_t*)b.vc + head_off + lane * 16, (size_t)b.Hkv * TILE,
+                             lane, bad, [&](int j, const u32x4* kr, const u32x4* vr) {
+                               st.tile(b.qk_mult, j, t1, kr, vr, p_w, lane);
+                             });
+  float* ws_o = b.ws;
+  float* ws_ml = b.ws + (size_t)b.ws_rows * b.Hq * D;
+#pragma unroll
+  for (int hh = 0; hh < HPW; ++hh) {
+    const float lt = valu::tile_sum<kPBS>(st.l_run[hh]);
+    const size_t pi = (size_t)wk.item * b.Hq + wk.qh0 + hh;
+#pragma unroll
+    for (int l = 0; l < NLOAD; ++l) {
+      const float v = st.dim_sum(hh, l);
+      if (lane % RU == 0) ws_o[pi * D + l * DPI + lane / RU] = bad ? NAN : v * b.v_mult;
+    }
+    if (lane == 0) {
+      ws_ml[pi * 2] = st.m_run[hh];
+      ws_ml[pi * 2 + 1] = bad ? NAN : lt;
+    }
+  }
+}
+
 // Both passes in one launch: workgroups [0, npre) run the prefix pass (args
-// a), the rest the split-K pass over each sequence's own tokens (args b).
+// a), the rest the suffix pass over each sequence's own tokens (args b), one
+// wave per item.
 // Both are bound by memory latency, not bandwidth, so side by side on the
 // same compute units they hide each other's waits; npre is a multiple of 8
 // so the split-K workgroups keep their XCD order.
 template <int HPW>
 __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void decode_prefix_fused_kernel(const DecodeArgs a, const DecodeArgs b, PrefixArgs p, int npre) {
-  if ((int)blockIdx.x < npre)
+  if ((int)blockIdx.x < npre) {
     prefix_body<kWaves>(a, p, blockIdx.x);
-  else
-    valu::decode_body<PKV_BF16, kPD, kPBS, HPW, kWaves, kBufs, true, false>(b, blockIdx.x - npre);
+  } else {
+    __shared__ float p_lds[kWaves][HPW][kPBS];
+    __shared__ u32x4 q_lds[kQLds ? kWaves : 1][kQLds ? HPW * kPD * 2 / 16 : 1];
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    suffix_wave<HPW>(b, ((int)blockIdx.x - npre) * kWaves + w, threadIdx.x & 63, p_lds[w],
+                     q_lds[kQLds ? w : 0]);
+  }
 }
 
 }  // namespace
@@ -253,7 +312,8 @@ int launch_decode_prefix_fused(const DecodeArgs& a, const DecodeArgs& b, const P
   return valu::with_hpw<PKV_BF16, kPD, kPBS>(a.Hq / a.Hkv, [&](auto h) {
     constexpr int HPW = decltype(h)::value;
     const int groups = b.Hq / b.Hkv / HPW;
-    dim3 block(kWaves * 64), grid(npre + b.total_parts * b.Hkv * groups);
+    const long long items = (long long)b.total_parts * b.Hkv * groups;   // one wave each
+    dim3 block(kWaves * 64), grid(npre + (unsigned)((items + kWaves - 1) / kWaves));
     hipLaunchKernelGGL(decode_prefix_fused_kernel<HPW>, grid, block, 0, (hipStream_t)stream, a, b,
                        p, npre);
     return (int)hipGetLastError();
