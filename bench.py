@@ -752,6 +752,32 @@ def main():
     torch.cuda.synchronize()
     dec_only_us = e0.elapsed_time(e1) / args.steps * 1e3
 
+    # the same reads without the arithmetic (split-K schedules): the rate the
+    # decode's access pattern itself reaches on this device
+    paged_probe_us = None
+    mfma_shape = c.kv_dtype == "fp8" and c.q_dtype == "bf16" and c.G % 8 == 0 and c.d == 128 \
+        and c.bs == 32   # the matrix-core kernel reads each tile once per kv head: another pattern
+    if P and not (PF or SK or mfma_shape):
+        psink = torch.zeros(4, dtype=torch.int32, device=dev)
+
+        def run_paged_probe(i):
+            kc, vc = layers[i % R]
+            pkv.pkv_paged_read_probe(kc, vc, tab, lens, c.H_q, q.dtype, P, inp["partition_offsets"],
+                                     inp["total_partitions"], psink)
+
+        for i in range(args.warmup):
+            run_paged_probe(i)
+        torch.cuda.synchronize()
+        e0.record()
+        for i in range(args.steps):
+            run_paged_probe(i)
+        e1.record()
+        torch.cuda.synchronize()
+        paged_probe_us = e0.elapsed_time(e1) / args.steps * 1e3
+        log(f"[bench] paged read probe (the decode's reads, no arithmetic): {paged_probe_us:.1f} us "
+            f"= {ab['kv'] / (paged_probe_us * 1e-6) / 1e9:.0f} GB/s of KV; decode kernel / probe time "
+            f"{dec_only_us / paged_probe_us:.3f}")
+
     us_step = ms_step * 1e3
     kv_gbps = ab["kv"] / (us_step * 1e-6) / 1e9
     if n_launch == 1:
@@ -826,7 +852,10 @@ def main():
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": traffic, "kernel": kernel,
                      "algorithmic_bytes_per_launch": kern_bytes,
-                     "frac_of_read_probe": round(achieved / probe_gbps, 4)},
+                     "frac_of_read_probe": round(achieved / probe_gbps, 4),
+                     "paged_read_probe_us": round(paged_probe_us, 2) if paged_probe_us else None,
+                     "paged_probe_over_kernel_time": round(paged_probe_us / kern_us, 4)
+                     if paged_probe_us else None},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -555,6 +555,23 @@ int paged_kv_gather(void* k_out, void* v_out, const void* key_cache, const void*
  * 1). */
 int pkv_hbm_read_probe(const void* buffer, size_t bytes, void* sink, int workgroups, void* stream);
 
+/* pkv_paged_read_probe -- measurement aid: the reads of paged_attention_
+ * decode's vector-ALU split-K kernel and nothing else (same grid, workgroup
+ * order, block-table walk and tile ring; no arithmetic, no partials, no
+ * reduce).  Arguments as paged_attention_decode without out, query, scale
+ * and the workspace (k/v scales do not matter); partition_tokens must be > 0.
+ * sink: 16-byte aligned device memory of which at most 4 bytes are written.
+ * Timing it gives the rate that the decode's access pattern (scattered
+ * blocks reached through the block table, 1 KiB-contiguous loads) reaches
+ * on the device ("Memory Systems" notes, core idea 1). */
+int pkv_paged_read_probe(const void* key_cache, const void* value_cache,
+                         const int32_t* block_tables, int max_blocks_per_seq,
+                         const int32_t* context_lens, int num_seqs, int num_q_heads,
+                         int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                         pkv_dtype q_dtype, pkv_dtype cache_dtype, int partition_tokens,
+                         const int32_t* partition_offsets, int total_partitions, void* sink,
+                         void* stream);
+
 /* ---------------------------------------------------------------------------
  * Host block allocator ("Day 6/90 of Inference Engineering", PagedAttention
  * notes): hands out one block at a time, takes a new block only when the

@@ -28,7 +28,7 @@ __all__ = [
     "paged_attention_decode_queue", "paged_kv_swap_blocks_memcpy",
     "paged_attention_splitk_reduce", "paged_kv_copy_blocks", "paged_kv_gather",
     "paged_attention_partition_offsets", "paged_attention_workspace_bytes", "BlockAllocator",
-    "empty_pools", "cache_dtype_code", "pkv_hbm_read_probe",
+    "empty_pools", "cache_dtype_code", "pkv_hbm_read_probe", "pkv_paged_read_probe",
 ]
 
 lib()  # fail at import if the library is missing or incomplete
@@ -478,6 +478,22 @@ def paged_kv_swap_blocks_memcpy(dst_key, dst_value, src_key, src_value, pairs, s
         _pool_ptr(dst_key, "dst_key"), _pool_ptr(dst_value, "dst_value"),
         _pool_ptr(src_key, "src_key"), _pool_ptr(src_value, "src_value"),
         p.ctypes.data_as(_native.pi32), p.shape[0], block_bytes, nbs, nbd, _stream(stream)))
+
+
+def pkv_paged_read_probe(key_cache, value_cache, block_tables, context_lens, num_q_heads, q_dtype,
+                         partition_tokens, partition_offsets, total_partitions, sink, stream=None):
+    """The split-K decode's reads alone (measurement aid); sink: device tensor
+    of >= 4 bytes, 16-byte aligned."""
+    nb, H, D, bs = _pool_shape(key_cache, value_cache)
+    _need(block_tables, "block_tables", torch.int32)
+    _need(context_lens, "context_lens", torch.int32)
+    _need(partition_offsets, "partition_offsets", torch.int32)
+    _need(sink, "sink")
+    check(lib().pkv_paged_read_probe(
+        _ptr(key_cache), _ptr(value_cache), _ptr(block_tables), block_tables.shape[1],
+        _ptr(context_lens), context_lens.numel(), int(num_q_heads), H, D, bs, nb,
+        _CODES[q_dtype], cache_dtype_code(key_cache), int(partition_tokens),
+        _ptr(partition_offsets), int(total_partitions), _ptr(sink), _stream(stream)))
 
 
 def paged_kv_gather(k_out, v_out, key_cache, value_cache, block_tables, cu_ctx, total_tokens,

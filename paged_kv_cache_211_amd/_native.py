@@ -74,6 +74,8 @@ SIGNATURES = {
     "paged_attention_splitk_reduce": (i32, [vp, vp, sz, vp, i32, i32, i32, i32, i32, i32, vp]),
     "paged_kv_copy_blocks": (i32, [vp, vp, vp, i32, sz, i32, vp]),
     "paged_kv_swap_blocks": (i32, [vp, vp, vp, vp, vp, i32, sz, i32, i32, vp]),
+    "pkv_paged_read_probe": (i32, [vp, vp, vp, i32, vp, i32, i32, i32, i32, i32, i32, i32, i32,
+                                   i32, vp, i32, vp, vp]),
     "paged_kv_swap_blocks_memcpy": (i32, [vp, vp, vp, vp, pi32, i32, sz, i32, i32, vp]),
     "pkv_host_device_pointer": (i32, [vp, ctypes.POINTER(vp)]),
     "paged_kv_gather": (i32, [vp, vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, i32, i32, i32, vp]),

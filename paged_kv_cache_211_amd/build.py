@@ -24,7 +24,7 @@ ARCH = "gfx950"
 
 SOURCES = ["api.cpp", "host.cpp", "allocator.cpp", "kv_ops.hip", "decode.hip", "decode_f32.hip",
            "decode_bf16.hip", "decode_fp8.hip", "decode_mfma.hip", "decode_prefix.hip", "noalloc.hip",
-           "prefill.hip"]
+           "prefill.hip", "paged_probe.hip"]
 
 
 def hipcc() -> str:

@@ -599,6 +599,28 @@ int paged_kv_swap_blocks_memcpy(void* dst_key_cache, void* dst_value_cache,
   return PKV_OK;
 }
 
+int pkv_paged_read_probe(const void* key_cache, const void* value_cache,
+                         const int32_t* block_tables, int max_blocks_per_seq,
+                         const int32_t* context_lens, int num_seqs, int num_q_heads,
+                         int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                         pkv_dtype q_dtype, pkv_dtype cache_dtype, int partition_tokens,
+                         const int32_t* partition_offsets, int total_partitions, void* sink,
+                         void* stream) {
+  // the decode's checks, with the sink standing in for the buffers the
+  // probe does not touch (query, output, workspace)
+  DecodeCall c{sink, sink, key_cache, value_cache, block_tables, max_blocks_per_seq, context_lens,
+               num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, 1.f,
+               q_dtype, cache_dtype, 1.f, 1.f, partition_tokens, partition_offsets,
+               total_partitions, sink, (size_t)-1};
+  if (partition_tokens <= 0) return fail(PKV_ERR_INVALID, "partition_tokens must be > 0");
+  if (!sink || (uintptr_t)sink % 16 != 0) return fail(PKV_ERR_INVALID, "sink must be 16-byte aligned");
+  DecodeArgs a;
+  const int rc = check_decode(c, &a);
+  if (rc) return rc;
+  if (num_seqs == 0) return PKV_OK;
+  return hip_status(launch_paged_read_probe(a, (uint32_t*)sink, stream), "pkv_paged_read_probe launch");
+}
+
 int pkv_host_device_pointer(const void* host, void** device_out) {
   if (!host || !device_out) return fail(PKV_ERR_INVALID, "null pointer argument");
   void* d = nullptr;

@@ -358,3 +358,25 @@ def test_many_partials_every_reduce_path(cfg_id):
     # same kernels, same reduce build: the same bits (bf16 values are exact in fp64)
     assert np.array_equal(out.view(torch.int16).cpu().numpy(),
                           torch.from_numpy(got).to(out.dtype).view(torch.int16).numpy())
+
+
+@pytest.mark.parametrize("cfg_id", [2, 3, 5])
+def test_paged_read_probe_runs_and_stores_nothing_else(cfg_id):
+    """The measurement aid that times the decode's reads: it runs on every
+    split-K shape of the workloads and writes nothing but (at most) its
+    4-byte sink."""
+    import paged_kv_cache_211_amd as pkv
+    wl = synth.make(synth.SMALL[cfg_id])
+    c = wl.cfg
+    _case(f"paged read probe, config {c.key}")
+    cache, step = H.build(wl, poison=True)
+    inp = cache.decode_inputs(range(c.S), c.partition)
+    sink = torch.zeros(8, dtype=torch.int32, device="cuda")
+    kb = cache.key_cache.view(torch.uint8).clone()
+    pkv.pkv_paged_read_probe(cache.key_cache, cache.value_cache, inp["block_tables"],
+                             inp["context_lens"], c.H_q, step["query"].dtype, c.partition,
+                             inp["partition_offsets"], inp["total_partitions"], sink)
+    torch.cuda.synchronize()
+    got = sink.cpu().numpy()
+    assert (got[1:] == 0).all() and got[0] in (0, np.int32(np.uint32(0x9E3779B9)))
+    assert torch.equal(cache.key_cache.view(torch.uint8), kb)

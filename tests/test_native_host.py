@@ -352,6 +352,13 @@ def test_decode_argument_validation_needs_no_gpu(pkv):
     w = L.paged_kv_write(fake, fake, fake, fake, fake, 4, 2, 128, 16, 10, 0, 1, 1.0, 1.0, None)
     assert w == -2
     assert L.paged_kv_copy_blocks(fake, fake, fake, 3, 100, 10, None) == -1
+    # the paged read probe checks like the decode, and needs split-K and an aligned sink
+    assert L.pkv_paged_read_probe(fake, fake, fake, 4, fake, 2, 8, 2, 128, 16, 10, 1, 1, 0, None, 0,
+                                  fake, None) == -1
+    assert L.pkv_paged_read_probe(fake, fake, fake, 4, fake, 2, 8, 2, 128, 16, 10, 1, 1, 32, fake, 2,
+                                  ctypes.c_void_p(4100), None) == -1
+    assert L.pkv_paged_read_probe(fake, fake, fake, 4, fake, 2, 8, 2, 96, 16, 10, 1, 1, 32, fake, 2,
+                                  fake, None) == -2
     pairs = (ctypes.c_int32 * 6)(0, 1, 1, 2, 2, 3)
     assert L.paged_kv_swap_blocks_memcpy(fake, fake, fake, fake, None, 3, 64, 10, 10, None) == -1
     assert L.paged_kv_swap_blocks_memcpy(fake, fake, fake, fake, pairs, 3, 8, 10, 10, None) == -1
