@@ -581,8 +581,14 @@ def main():
     tab, lens = inp["block_tables"], inp["context_lens"]
     # longest sequence's partition count: sizes the standalone reduce's launch
     max_parts = int(-(-int(inp["lens_host"].max()) // P)) if P else 0
-    if PF or QU:
-        n_launch = 3   # the store, the decode (prefix + suffix pass, or work counter), the reduce
+    if PF:
+        # the decode (prefix + suffix pass, storing the new tokens where each
+        # (sequence, kv head) has one suffix wave -- the criterion of the
+        # split-K step on these dtypes) and the reduce, or a store launch first
+        n_launch = pkv.paged_attention_decode_step_launches(c.H_q, c.H_kv, c.d, c.bs, q.dtype,
+                                                            cache.dtype, P)
+    elif QU:
+        n_launch = 3   # the store, the work-counter decode, the reduce
     elif SK:
         n_launch = 2 if pkv.paged_attention_decode_step_launches(c.H_q, c.H_kv, c.d, c.bs, q.dtype,
                                                                  cache.dtype, 0) == 1 else 3
@@ -602,9 +608,10 @@ def main():
         kc, vc = layers[i % R]
         if ev:
             ev[0].record()
-        if PF:   # no in-kernel store on this schedule: the store, then the decode
-            pkv.paged_kv_write(key, value, kc, vc, slots, k_scale=c.k_scale, v_scale=c.v_scale)
-            run_prefix(kc, vc)
+        if PF:
+            pkv.paged_attention_decode_prefix_step(out, q, key, value, kc, vc, tab, lens, c.scale,
+                                                   P, inp["prefix"], inp["prefix_totals"], ws,
+                                                   c.k_scale, c.v_scale)
         elif QU:
             pkv.paged_kv_write(key, value, kc, vc, slots, k_scale=c.k_scale, v_scale=c.v_scale)
             run_queue(kc, vc)

@@ -421,6 +421,35 @@ int paged_attention_decode_prefix(void* out, const void* query, const void* key_
                                   int total_prefix_items, void* workspace,
                                   size_t workspace_bytes, void* stream);
 
+/* paged_attention_decode_prefix_step -- the shared-prefix decode's whole
+ * decode step ("Day 6/90 of Inference Engineering": a step appends its token
+ * to the sequence's own last block, then attention reads every block of the
+ * table): store each sequence's new key/value row, then decode as
+ * paged_attention_decode_prefix.  The plan comes from the step's context
+ * lengths (the new token included).  new_key, new_value as in
+ * paged_attention_decode_step (row s is the token at position
+ * context_lens[s] - 1, stored into the slot the table gives; bf16);
+ * key_cache and value_cache are written.  A sequence whose new token lies in
+ * its group's shared blocks (context_lens[s] <= token_start[s], which a cache
+ * that copies shared blocks on write never produces) gets a NaN output row
+ * and no store.  The result is paged_kv_write of the new rows followed by
+ * paged_attention_decode_prefix, bit for bit.  Where the suffix pass gives
+ * each (sequence, kv head) one workgroup (query heads per kv head of 1, 2 or
+ * 4), the suffix workgroup that reads a sequence's last block stores the
+ * token first and the step is two launches (decode, reduce); otherwise a
+ * store launch precedes them.  Returns PKV_ERR_INVALID for a null new_key or
+ * new_value, else as paged_attention_decode_prefix. */
+int paged_attention_decode_prefix_step(
+    void* out, const void* query, const void* new_key, const void* new_value, void* key_cache,
+    void* value_cache, const int32_t* block_tables, int max_blocks_per_seq,
+    const int32_t* context_lens, int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+    int block_size, int num_blocks, float scale, pkv_dtype q_dtype, pkv_dtype cache_dtype,
+    float k_scale, float v_scale, int partition_tokens, const int32_t* group_offsets,
+    const int32_t* group_prefix_blocks, int num_groups, const int32_t* row_offsets,
+    const int32_t* suffix_offsets, const int32_t* token_start, const int32_t* prefix_item_offsets,
+    int total_rows, int total_suffix_partitions, int total_prefix_items, void* workspace,
+    size_t workspace_bytes, void* stream);
+
 /* ---------------------------------------------------------------------------
  * paged_attention_prefill -- chunked prefill over the paged cache.
  * The block table makes a sequence's scattered blocks read as one contiguous

@@ -360,6 +360,20 @@ def paged_attention_prefix_plan(context_lens_host, group_offsets, group_prefix_b
             "totals": tuple(int(t) for t in tot)}
 
 
+def _prefix_args(plan_dev, totals, workspace):
+    names = ("group_offsets", "group_prefix_blocks", "row_offsets", "suffix_offsets",
+             "token_start", "prefix_item_offsets")
+    for n in names:
+        _need(plan_dev[n], n, torch.int32)
+    _need(workspace, "workspace")
+    d = {n: _ptr(plan_dev[n]) for n in names}
+    n_groups = plan_dev["group_prefix_blocks"].numel()
+    return (d["group_offsets"], d["group_prefix_blocks"], n_groups, d["row_offsets"],
+            d["suffix_offsets"], d["token_start"], d["prefix_item_offsets"], int(totals[0]),
+            int(totals[1]), int(totals[2]), _ptr(workspace),
+            workspace.numel() * workspace.element_size())
+
+
 def paged_attention_decode_prefix(out, query, key_cache, value_cache, block_tables, context_lens,
                                   scale, partition_tokens, plan_dev, totals, workspace,
                                   k_scale=1.0, v_scale=1.0, stream=None):
@@ -369,18 +383,30 @@ def paged_attention_decode_prefix(out, query, key_cache, value_cache, block_tabl
     prefix_item_offsets); totals: the plan's host totals."""
     a = _decode_args(out, query, key_cache, value_cache, block_tables, context_lens, scale,
                      k_scale, v_scale, 0, None, 0, None)
-    names = ("group_offsets", "group_prefix_blocks", "row_offsets", "suffix_offsets",
-             "token_start", "prefix_item_offsets")
-    for n in names:
-        _need(plan_dev[n], n, torch.int32)
-    _need(workspace, "workspace")
-    d = {n: _ptr(plan_dev[n]) for n in names}
-    n_groups = plan_dev["group_prefix_blocks"].numel()
     check(lib().paged_attention_decode_prefix(
-        *a[:18], int(partition_tokens), d["group_offsets"], d["group_prefix_blocks"], n_groups,
-        d["row_offsets"], d["suffix_offsets"], d["token_start"], d["prefix_item_offsets"],
-        int(totals[0]), int(totals[1]), int(totals[2]), _ptr(workspace),
-        workspace.numel() * workspace.element_size(), _stream(stream)))
+        *a[:18], int(partition_tokens), *_prefix_args(plan_dev, totals, workspace),
+        _stream(stream)))
+
+
+def paged_attention_decode_prefix_step(out, query, new_key, new_value, key_cache, value_cache,
+                                       block_tables, context_lens, scale, partition_tokens,
+                                       plan_dev, totals, workspace, k_scale=1.0, v_scale=1.0,
+                                       stream=None):
+    """Store each sequence's new key/value row (position context_lens[s]-1),
+    then decode with the shared-prefix schedule, as paged_kv_write followed by
+    paged_attention_decode_prefix; the plan is the step's (new token
+    included)."""
+    a = _decode_args(out, query, key_cache, value_cache, block_tables, context_lens, scale,
+                     k_scale, v_scale, 0, None, 0, None)
+    S, Hq, D = query.shape
+    H = key_cache.shape[1]
+    for t, n in ((new_key, "new_key"), (new_value, "new_value")):
+        _need(t, n)
+        if tuple(t.shape) != (S, H, D) or t.dtype != query.dtype:
+            raise PkvError(-1, f"{n} must be [S, H_kv, head_dim] of the query dtype")
+    check(lib().paged_attention_decode_prefix_step(
+        a[0], a[1], _ptr(new_key), _ptr(new_value), *a[2:18], int(partition_tokens),
+        *_prefix_args(plan_dev, totals, workspace), _stream(stream)))
 
 
 def paged_attention_prefill(out, query, key_cache, value_cache, block_tables, context_lens,

@@ -69,6 +69,10 @@ SIGNATURES = {
     "paged_attention_decode_prefix": (i32, [vp, vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, i32,
                                             i32, f32, i32, i32, f32, f32, i32, vp, vp, i32, vp, vp,
                                             vp, vp, i32, i32, i32, vp, sz, vp]),
+    "paged_attention_decode_prefix_step": (i32, [vp, vp, vp, vp, vp, vp, vp, i32, vp, i32, i32,
+                                                 i32, i32, i32, i32, f32, i32, i32, f32, f32, i32,
+                                                 vp, vp, i32, vp, vp, vp, vp, i32, i32, i32, vp,
+                                                 sz, vp]),
     "paged_attention_prefill": (i32, [vp, vp, vp, vp, vp, i32, vp, vp, i32, i32, i32, i32, i32,
                                       i32, i32, f32, i32, i32, f32, f32, vp]),
     "paged_attention_splitk_reduce": (i32, [vp, vp, sz, vp, i32, i32, i32, i32, i32, i32, vp]),

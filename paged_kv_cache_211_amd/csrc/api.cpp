@@ -393,19 +393,19 @@ int paged_attention_decode_step_streamk(void* out, const void* query, const void
   return streamk_common(c, new_key, new_value, tile_offsets, total_tiles, workers, true, stream);
 }
 
-int paged_attention_decode_prefix(void* out, const void* query, const void* key_cache,
-                                  const void* value_cache, const int32_t* block_tables,
-                                  int max_blocks_per_seq, const int32_t* context_lens,
-                                  int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
-                                  int block_size, int num_blocks, float scale, pkv_dtype q_dtype,
-                                  pkv_dtype cache_dtype, float k_scale, float v_scale,
-                                  int partition_tokens, const int32_t* group_offsets,
-                                  const int32_t* group_prefix_blocks, int num_groups,
-                                  const int32_t* row_offsets, const int32_t* suffix_offsets,
-                                  const int32_t* token_start, const int32_t* prefix_item_offsets,
-                                  int total_rows, int total_suffix_partitions,
-                                  int total_prefix_items, void* workspace,
-                                  size_t workspace_bytes, void* stream) {
+// The shared-prefix decode, and with new_key / new_value its decode step.
+static int prefix_common(void* out, const void* query, const void* new_key,
+                         const void* new_value, const void* key_cache, const void* value_cache,
+                         const int32_t* block_tables, int max_blocks_per_seq,
+                         const int32_t* context_lens, int num_seqs, int num_q_heads,
+                         int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                         float scale, pkv_dtype q_dtype, pkv_dtype cache_dtype, float k_scale,
+                         float v_scale, int partition_tokens, const int32_t* group_offsets,
+                         const int32_t* group_prefix_blocks, int num_groups,
+                         const int32_t* row_offsets, const int32_t* suffix_offsets,
+                         const int32_t* token_start, const int32_t* prefix_item_offsets,
+                         int total_rows, int total_suffix_partitions, int total_prefix_items,
+                         void* workspace, size_t workspace_bytes, bool step, void* stream) {
   if (partition_tokens <= 0) return fail(PKV_ERR_INVALID, "partition_tokens must be > 0");
   if (total_rows < num_seqs || total_suffix_partitions < 0 || total_prefix_items < 0 ||
       num_groups < 0)
@@ -413,6 +413,7 @@ int paged_attention_decode_prefix(void* out, const void* query, const void* key_
   if (!group_offsets || !group_prefix_blocks || !row_offsets || !suffix_offsets ||
       !token_start || !prefix_item_offsets)
     return fail(PKV_ERR_INVALID, "null pointer argument");
+  if (step && (!new_key || !new_value)) return fail(PKV_ERR_INVALID, "null pointer argument");
   // validate as a split-K call over total_rows partial rows
   DecodeCall c{out, query, key_cache, value_cache, block_tables, max_blocks_per_seq, context_lens,
                num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, scale,
@@ -435,15 +436,33 @@ int paged_attention_decode_prefix(void* out, const void* query, const void* key_
   p.n_groups = num_groups;
   p.total_items = total_prefix_items;
   p.total_rows = total_rows;
+  p.step = step ? 1 : 0;
+  DecodeArgs b = a;   // the split-K pass over each sequence's own tokens
+  b.part_off = suffix_offsets;
+  b.total_parts = total_suffix_partitions;
+  b.t_start = token_start;
+  b.row_off = row_offsets;
+  // decode step: the suffix wave that reads a sequence's last block stores
+  // its new token, else a store launch goes first
+  const bool in_kernel = step && total_suffix_partitions > 0 && decode_prefix_step_in_kernel(a);
+  if (step) {
+    b.new_k = new_key;
+    b.new_v = new_value;
+    if (!in_kernel) {
+      rc = hip_status(launch_kv_write_tail(new_key, new_value, (void*)key_cache,
+                                           (void*)value_cache, block_tables, max_blocks_per_seq,
+                                           context_lens, num_seqs, num_kv_heads, head_dim,
+                                           block_size, num_blocks, cache_dtype, 1.f, 1.f, stream,
+                                           token_start),
+                      "shared-prefix decode step store launch");
+      if (rc) return rc;
+    }
+  }
   if (total_suffix_partitions > 0) {
     // the prefix pass and the split-K pass over each sequence's own tokens
     // in one launch (they write disjoint partial rows)
-    DecodeArgs b = a;
-    b.part_off = suffix_offsets;
-    b.total_parts = total_suffix_partitions;
-    b.t_start = token_start;
-    b.row_off = row_offsets;
-    rc = hip_status(launch_decode_prefix_fused(a, b, p, stream), "shared-prefix decode launch");
+    rc = hip_status(launch_decode_prefix_fused(a, b, p, stream, in_kernel),
+                    "shared-prefix decode launch");
   } else {
     rc = hip_status(launch_decode_prefix(a, p, stream), "shared-prefix decode launch");
   }
@@ -451,6 +470,47 @@ int paged_attention_decode_prefix(void* out, const void* query, const void* key_
   return hip_status(launch_splitk_reduce(out, a.ws, row_offsets, num_seqs, num_q_heads, head_dim,
                                          total_rows, q_dtype, stream, 1),
                     "shared-prefix reduce launch");
+}
+
+int paged_attention_decode_prefix(void* out, const void* query, const void* key_cache,
+                                  const void* value_cache, const int32_t* block_tables,
+                                  int max_blocks_per_seq, const int32_t* context_lens,
+                                  int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                                  int block_size, int num_blocks, float scale, pkv_dtype q_dtype,
+                                  pkv_dtype cache_dtype, float k_scale, float v_scale,
+                                  int partition_tokens, const int32_t* group_offsets,
+                                  const int32_t* group_prefix_blocks, int num_groups,
+                                  const int32_t* row_offsets, const int32_t* suffix_offsets,
+                                  const int32_t* token_start, const int32_t* prefix_item_offsets,
+                                  int total_rows, int total_suffix_partitions,
+                                  int total_prefix_items, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  return prefix_common(out, query, nullptr, nullptr, key_cache, value_cache, block_tables,
+                       max_blocks_per_seq, context_lens, num_seqs, num_q_heads, num_kv_heads,
+                       head_dim, block_size, num_blocks, scale, q_dtype, cache_dtype, k_scale,
+                       v_scale, partition_tokens, group_offsets, group_prefix_blocks, num_groups,
+                       row_offsets, suffix_offsets, token_start, prefix_item_offsets, total_rows,
+                       total_suffix_partitions, total_prefix_items, workspace, workspace_bytes,
+                       false, stream);
+}
+
+int paged_attention_decode_prefix_step(
+    void* out, const void* query, const void* new_key, const void* new_value, void* key_cache,
+    void* value_cache, const int32_t* block_tables, int max_blocks_per_seq,
+    const int32_t* context_lens, int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+    int block_size, int num_blocks, float scale, pkv_dtype q_dtype, pkv_dtype cache_dtype,
+    float k_scale, float v_scale, int partition_tokens, const int32_t* group_offsets,
+    const int32_t* group_prefix_blocks, int num_groups, const int32_t* row_offsets,
+    const int32_t* suffix_offsets, const int32_t* token_start, const int32_t* prefix_item_offsets,
+    int total_rows, int total_suffix_partitions, int total_prefix_items, void* workspace,
+    size_t workspace_bytes, void* stream) {
+  return prefix_common(out, query, new_key, new_value, key_cache, value_cache, block_tables,
+                       max_blocks_per_seq, context_lens, num_seqs, num_q_heads, num_kv_heads,
+                       head_dim, block_size, num_blocks, scale, q_dtype, cache_dtype, k_scale,
+                       v_scale, partition_tokens, group_offsets, group_prefix_blocks, num_groups,
+                       row_offsets, suffix_offsets, token_start, prefix_item_offsets, total_rows,
+                       total_suffix_partitions, total_prefix_items, workspace, workspace_bytes,
+                       true, stream);
 }
 
 int paged_attention_prefill(void* out, const void* query, const void* key_cache,

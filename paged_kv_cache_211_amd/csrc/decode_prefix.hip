@@ -65,6 +65,9 @@ __device__ __forceinline__ void prefix_body(const DecodeArgs& a, const PrefixArg
   const int s0 = p.group_off[grp], members = p.group_off[grp + 1] - s0;
   const int G = a.Hq / a.Hkv;
   int pblocks = p.group_blocks[grp];
+  // decode step: a member whose new token (position L - 1) lies in the
+  // group's shared blocks would be stored into blocks this pass reads
+  const long long shared_tokens = (long long)pblocks * BS;
   bool bad = false;
   if (pblocks > a.max_blocks) { pblocks = a.max_blocks; bad = true; }   // beyond the table
   const int npre = (pblocks + kPrefixPieceBlocks - 1) / kPrefixPieceBlocks;
@@ -213,14 +216,15 @@ __device__ __forceinline__ void prefix_body(const DecodeArgs& a, const PrefixArg
     const float lt = sum_xor16(row16_sum(l_run[r]));
     const int base = __shfl(prow_l, rr / G - mfirst);
     if (rr < members * G) {
+      const bool nan_row = bad || (p.step && a.lens[s0 + rr / G] <= shared_tokens);
       const int qh = hkv * G + rr % G;
       const size_t pi = (size_t)(base + pp) * a.Hq + qh;
       float* o = ws_o + pi * D + col;
 #pragma unroll
-      for (int m = 0; m < 4; ++m) o[32 * m] = bad ? NAN : acc[m][r];
+      for (int m = 0; m < 4; ++m) o[32 * m] = nan_row ? NAN : acc[m][r];
       if (col == 0) {
         ws_ml[pi * 2] = m_run[r];
-        ws_ml[pi * 2 + 1] = bad ? NAN : lt;
+        ws_ml[pi * 2 + 1] = nan_row ? NAN : lt;
       }
     }
   }
@@ -238,8 +242,12 @@ void decode_prefix_kernel(const DecodeArgs a, PrefixArgs p) {
 // the shared-prefix plan gives (row_off[s] + part).  The suffixes are short
 // (tens of blocks), so a wave that takes all of an item's tiles pays the
 // item's start (query, table, first tiles) once instead of four times and
-// needs no merge through LDS.
-template <int HPW>
+// needs no merge through LDS.  STORE (decode step, one wave per (sequence,
+// kv head, partition)): the wave whose partition ends at the context's end
+// reads the block of the new token, so it stores the token first, as the
+// split-K decode step does (from tile_loop's start hook, waiting for the
+// store only before loading that block).
+template <int HPW, bool STORE>
 __device__ __forceinline__ void suffix_wave(const DecodeArgs& b, int x, int lane,
                                             float (*p_w)[kPBS], u32x4* q_w) {
   using St = valu::ValuHeads<PKV_BF16, kPD, kPBS, HPW, kQLds>;
@@ -260,11 +268,18 @@ __device__ __forceinline__ void suffix_wave(const DecodeArgs& b, int x, int lane
   }
   st.reset();
   const int t1 = wk.t1;
+  const bool my_store = STORE && !wk.bad && wk.L > 0 && wk.t0 < wk.L && wk.t1 == wk.L;
   tile_loop<kBufs, NLOAD, 1>(tbl, wk.t0 / kPBS, wk.jend, b.nb,
                              (const uint8_t*)b.kc + head_off + lane * 16,
                              (const uint8_t*)b.vc + head_off + lane * 16, (size_t)b.Hkv * TILE,
                              lane, bad, [&](int j, const u32x4* kr, const u32x4* vr) {
                                st.tile(b.qk_mult, j, t1, kr, vr, p_w, lane);
+                             },
+                             my_store ? wk.jend - 1 : -1, [&] {
+                               if constexpr (STORE) {
+                                 if (my_store)
+                                   store_new_token<PKV_BF16, kPD, kPBS>(b, wk.s, wk.hkv, wk.L, lane);
+                               }
                              });
   float* ws_o = b.ws;
   float* ws_ml = b.ws + (size_t)b.ws_rows * b.Hq * D;
@@ -289,8 +304,9 @@ __device__ __forceinline__ void suffix_wave(const DecodeArgs& b, int x, int lane
 // wave per item.
 // Both are bound by memory latency, not bandwidth, so side by side on the
 // same compute units they hide each other's waits; npre is a multiple of 8
-// so the split-K workgroups keep their XCD order.
-template <int HPW>
+// so the split-K workgroups keep their XCD order.  STORE: the decode step's
+// store in the suffix waves.
+template <int HPW, bool STORE>
 __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void decode_prefix_fused_kernel(const DecodeArgs a, const DecodeArgs b, PrefixArgs p, int npre) {
   if ((int)blockIdx.x < npre) {
@@ -299,7 +315,7 @@ void decode_prefix_fused_kernel(const DecodeArgs a, const DecodeArgs b, PrefixAr
     __shared__ float p_lds[kWaves][HPW][kPBS];
     __shared__ u32x4 q_lds[kQLds ? kWaves : 1][kQLds ? HPW * kPD * 2 / 16 : 1];
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    suffix_wave<HPW>(b, ((int)blockIdx.x - npre) * kWaves + w, threadIdx.x & 63, p_lds[w],
+    suffix_wave<HPW, STORE>(b, ((int)blockIdx.x - npre) * kWaves + w, threadIdx.x & 63, p_lds[w],
                      q_lds[kQLds ? w : 0]);
   }
 }
@@ -307,21 +323,31 @@ void decode_prefix_fused_kernel(const DecodeArgs a, const DecodeArgs b, PrefixAr
 }  // namespace
 
 int launch_decode_prefix_fused(const DecodeArgs& a, const DecodeArgs& b, const PrefixArgs& p,
-                               void* stream) {
+                               void* stream, bool store) {
   const int npre = ((p.total_items + kWaves - 1) / kWaves + 7) / 8 * 8;
   return valu::with_hpw<PKV_BF16, kPD, kPBS>(a.Hq / a.Hkv, [&](auto h) {
     constexpr int HPW = decltype(h)::value;
     const int groups = b.Hq / b.Hkv / HPW;
     const long long items = (long long)b.total_parts * b.Hkv * groups;   // one wave each
+    if (store && groups != 1) return (int)hipErrorInvalidValue;
     dim3 block(kWaves * 64), grid(npre + (unsigned)((items + kWaves - 1) / kWaves));
-    hipLaunchKernelGGL(decode_prefix_fused_kernel<HPW>, grid, block, 0, (hipStream_t)stream, a, b,
-                       p, npre);
+    if (store)
+      hipLaunchKernelGGL((decode_prefix_fused_kernel<HPW, true>), grid, block, 0,
+                         (hipStream_t)stream, a, b, p, npre);
+    else
+      hipLaunchKernelGGL((decode_prefix_fused_kernel<HPW, false>), grid, block, 0,
+                         (hipStream_t)stream, a, b, p, npre);
     return (int)hipGetLastError();
   });
 }
 
 bool decode_prefix_supported(const DecodeArgs& a) {
   return a.q_dtype == PKV_BF16 && a.kv_dtype == PKV_BF16 && a.D == kPD && a.BS == kPBS;
+}
+
+bool decode_prefix_step_in_kernel(const DecodeArgs& a) {
+  const int G = a.Hq / a.Hkv;
+  return decode_prefix_supported(a) && valu::heads_per_wg<PKV_BF16, kPD, kPBS>(G) == G;
 }
 
 int launch_decode_prefix(const DecodeArgs& a, const PrefixArgs& p, void* stream) {

@@ -151,7 +151,9 @@ __global__ __launch_bounds__(256) void kv_write_block_kernel(const uint16_t* __r
 // Decode-step scatter: one thread per (sequence, kv head, key unit); row s
 // of key/value is sequence s's new token, stored at position lens[s] - 1 in
 // the slot its block table gives.  Sequences of length 0, beyond the table or
-// with an out-of-range block id are skipped.
+// with an out-of-range block id are skipped, and so, with t_start (the
+// shared-prefix decode step), is a sequence whose new token lies before its
+// own blocks (lens[s] <= t_start[s]).
 template <int CACHE>
 __global__ __launch_bounds__(256) void kv_write_tail_kernel(const void* __restrict__ key,
                                                             const void* __restrict__ value,
@@ -161,7 +163,8 @@ __global__ __launch_bounds__(256) void kv_write_tail_kernel(const void* __restri
                                                             int max_blocks,
                                                             const int32_t* __restrict__ lens, int S,
                                                             int H, int D, int BS, int nb,
-                                                            float k_inv, float v_inv) {
+                                                            float k_inv, float v_inv,
+                                                            const int32_t* __restrict__ t_start) {
   constexpr int X = 16 / (CACHE == PKV_F32 ? 4 : CACHE == PKV_BF16 ? 2 : 1);
   const int units = D / X;
   const long gid = (long)blockIdx.x * blockDim.x + threadIdx.x;
@@ -171,6 +174,7 @@ __global__ __launch_bounds__(256) void kv_write_tail_kernel(const void* __restri
   const int s = (int)(gid / ((long)units * H));
   const int L = lens[s];
   if (L <= 0 || L > max_blocks * BS) return;
+  if (t_start && L <= t_start[s]) return;
   const int pos = L - 1;
   const int blk = tables[(size_t)s * max_blocks + pos / BS];
   if ((unsigned)blk >= (unsigned)nb) return;
@@ -317,7 +321,7 @@ int launch_kv_write(const void* key, const void* value, void* kc, void* vc, cons
 int launch_kv_write_tail(const void* key, const void* value, void* kc, void* vc,
                          const int32_t* tables, int max_blocks, const int32_t* lens, int S, int H,
                          int D, int BS, int nb, pkv_dtype cache, float k_inv, float v_inv,
-                         void* stream) {
+                         void* stream, const int32_t* t_start) {
   hipStream_t st = (hipStream_t)stream;
   const int X = 16 / elem_bytes(cache);
   const long n = (long)S * H * (D / X);
@@ -326,13 +330,13 @@ int launch_kv_write_tail(const void* key, const void* value, void* kc, void* vc,
   auto k8 = (uint8_t*)kc, v8 = (uint8_t*)vc;
   if (cache == PKV_F32)
     hipLaunchKernelGGL((kv_write_tail_kernel<PKV_F32>), grid, block, 0, st, key, value, k8, v8,
-                       tables, max_blocks, lens, S, H, D, BS, nb, k_inv, v_inv);
+                       tables, max_blocks, lens, S, H, D, BS, nb, k_inv, v_inv, t_start);
   else if (cache == PKV_BF16)
     hipLaunchKernelGGL((kv_write_tail_kernel<PKV_BF16>), grid, block, 0, st, key, value, k8, v8,
-                       tables, max_blocks, lens, S, H, D, BS, nb, k_inv, v_inv);
+                       tables, max_blocks, lens, S, H, D, BS, nb, k_inv, v_inv, t_start);
   else
     hipLaunchKernelGGL((kv_write_tail_kernel<PKV_FP8_E4M3>), grid, block, 0, st, key, value, k8,
-                       v8, tables, max_blocks, lens, S, H, D, BS, nb, k_inv, v_inv);
+                       v8, tables, max_blocks, lens, S, H, D, BS, nb, k_inv, v_inv, t_start);
   return (int)hipGetLastError();
 }
 

@@ -97,6 +97,9 @@ struct PrefixArgs {
   const int32_t* row_off = nullptr;
   const int32_t* suf_off = nullptr;
   int n_groups = 0, total_items = 0, total_rows = 0;
+  // decode step: members whose new token lies in the shared blocks
+  // (lens <= group_blocks * BS) get NaN rows
+  int step = 0;
 };
 
 // Chunked prefill (prefill.hip): sequence s owns query rows q_start[s] ..
@@ -134,10 +137,15 @@ int launch_sk_reduce(const DecodeArgs& a, void* stream);
 // Shared-prefix decode (decode_prefix.hip): bf16 query and cache, head_dim
 // 128, block size 16.
 bool decode_prefix_supported(const DecodeArgs& a);
+// whether the suffix pass has one wave per (sequence, kv head, partition), so
+// that the decode step can store the new tokens inside the launch
+bool decode_prefix_step_in_kernel(const DecodeArgs& a);
 int launch_decode_prefix(const DecodeArgs& a, const PrefixArgs& p, void* stream);
-// the prefix pass (a) and the suffix split-K pass (b) in one launch
+// the prefix pass (a) and the suffix split-K pass (b) in one launch; store:
+// the decode step's new-token store (b.new_k / b.new_v), only where
+// decode_prefix_step_in_kernel
 int launch_decode_prefix_fused(const DecodeArgs& a, const DecodeArgs& b, const PrefixArgs& p,
-                               void* stream);
+                               void* stream, bool store = false);
 int launch_swap_blocks(void* dk, void* dv, const void* sk, const void* sv, const int32_t* pairs,
                        int n, size_t block_bytes, int src_nb, int dst_nb, void* stream);
 bool prefill_supported(pkv_dtype q, pkv_dtype kv, int D, int BS);
@@ -176,10 +184,11 @@ bool decode_supported(pkv_dtype q, pkv_dtype kv, int D, int BS, int G);
 int launch_kv_write(const void* key, const void* value, void* kc, void* vc, const int32_t* slots,
                     int T, int H, int D, int BS, int nb, pkv_dtype src, pkv_dtype cache,
                     float k_inv, float v_inv, void* stream);
+// t_start (device, optional): sequence s is skipped when lens[s] <= t_start[s]
 int launch_kv_write_tail(const void* key, const void* value, void* kc, void* vc,
                          const int32_t* tables, int max_blocks, const int32_t* lens, int S, int H,
                          int D, int BS, int nb, pkv_dtype cache, float k_inv, float v_inv,
-                         void* stream);
+                         void* stream, const int32_t* t_start = nullptr);
 int launch_copy_blocks(void* kc, void* vc, const int32_t* pairs, int n, size_t block_bytes,
                        int nb, void* stream);
 int launch_read_probe(const void* src, size_t bytes, void* sink, int blocks, void* stream);

@@ -13,7 +13,7 @@ import numpy as np
 import torch
 
 from . import (BlockAllocator, empty_pools, paged_attention_decode, paged_attention_decode_prefix,
-               paged_attention_decode_queue,
+               paged_attention_decode_prefix_step, paged_attention_decode_queue,
                paged_attention_decode_step, paged_attention_prefix_plan,
                paged_attention_decode_step_streamk, paged_attention_decode_streamk,
                paged_attention_partition_offsets, paged_attention_streamk_workers,
@@ -264,6 +264,15 @@ class PagedKVCache:
         the decode launch where the kernel allows."""
         S, Hq, D = query.shape
         out = torch.empty_like(query) if out is None else out
+        if inp.get("prefix") is not None:
+            ws = self.workspace(inp["prefix_totals"][0], Hq, D)
+            paged_attention_decode_prefix_step(out, query, new_key, new_value, self.key_cache,
+                                               self.value_cache, inp["block_tables"],
+                                               inp["context_lens"], scale, inp["partition_tokens"],
+                                               inp["prefix"], inp["prefix_totals"], ws,
+                                               k_scale=self.k_scale, v_scale=self.v_scale,
+                                               stream=stream)
+            return out
         if inp["streamk"]:
             paged_attention_decode_step_streamk(
                 out, query, new_key, new_value, self.key_cache, self.value_cache,

@@ -14,7 +14,7 @@ from oracle import replay
 from synth import device as H
 
 from .tolerances import TOL
-from .test_gpu_parity import oracle_out
+from .test_gpu_parity import check_cache_bits, oracle_out
 
 pytestmark = pytest.mark.gpu
 
@@ -147,3 +147,110 @@ def test_prefix_full_size_sampled():
     err = np.abs(got[seqs] - ref[seqs]).max()
     print(f"  sampled seqs {seqs}: max abs err {err:.3e}", flush=True)
     assert err <= TOL[c.kv_dtype]
+
+
+# ---- the decode step on the shared-prefix schedule --------------------------
+# The device cache is built with each sequence's decode token allocated but
+# not stored (its slot keeps the NaN poison), so an output that read the slot
+# before the step stored it is NaN.
+
+
+def prefix_step(cache, step, wl, P, inp=None):
+    c = wl.cfg
+    if inp is None:
+        inp = cache.decode_inputs(range(c.S), P, prefix=True, num_q_heads=c.H_q,
+                                  prefix_min_blocks=1)
+    out = torch.full_like(step["query"], float("nan"))
+    cache.decode_step(step["query"], step["key"], step["value"], inp, c.scale, out=out)
+    torch.cuda.synchronize()
+    return out.double().cpu().numpy(), inp
+
+
+@pytest.mark.parametrize("G", [4, 8, 1, 3])
+def test_prefix_step_parity_and_bits(G):
+    """Against the oracle and bit for bit against paged_kv_write followed by
+    the shared-prefix decode.  G = 1 and 4 store inside the decode launch
+    (one suffix wave per sequence and kv head); G = 3 and 8 store first."""
+    import paged_kv_cache_211_amd as pkv
+    wl = _workload(G, seed=160 + G)
+    c = wl.cfg
+    n = pkv.paged_attention_decode_step_launches(c.H_q, c.H_kv, c.d, c.bs, torch.bfloat16,
+                                                 torch.bfloat16, c.partition)
+    _case(f"shared-prefix decode step, G={G}, {n} launches")
+    st, _ = replay.build(wl)
+    ref, _ = oracle_out(wl, st)
+    for P in (c.bs, c.partition):
+        cs, ss = H.build(wl, poison=True, write_step=False)
+        got, _ = prefix_step(cs, ss, wl, P)
+        assert np.isfinite(got).all(), P
+        err = np.abs(got - ref).max()
+        print(f"  partition {P}: max abs err {err:.3e}", flush=True)
+        assert err <= TOL[c.kv_dtype], (P, err)
+        check_cache_bits(cs, st, wl, np.arange(c.S))
+        cw, sw = H.build(wl, poison=True, write_step=True)
+        want, _ = prefix_decode(cw, sw, wl, P)
+        assert np.array_equal(got, want), P
+
+
+def test_prefix_step_full_size_bits():
+    """The full prefix workload (128 sequences, 64 shared blocks): the step
+    equals the write followed by the decode bit for bit, and the cache bits of
+    sampled sequences equal the oracle's."""
+    wl = synth.make(4)
+    c = wl.cfg
+    _case(f"shared-prefix decode step, full prefix workload S={c.S}")
+    seqs = [0, 1, c.S // 2, c.S - 1]
+    st, _ = replay.build(wl, only_seqs=seqs)
+    cs, ss = H.build(wl, poison=True, write_step=False)
+    got, inp = prefix_step(cs, ss, wl, c.partition)
+    assert inp["prefix"]["group_prefix_blocks"].cpu().tolist() == [c.prefix // c.bs]
+    assert np.isfinite(got).all()
+    check_cache_bits(cs, st, wl, np.array(seqs))
+    cw, sw = H.build(wl, poison=True, write_step=True)
+    want, _ = prefix_decode(cw, sw, wl, c.partition)
+    assert np.array_equal(got, want)
+
+
+@pytest.mark.parametrize("G", [4, 8])
+def test_prefix_step_token_in_shared_blocks(G):
+    """A sequence whose step length ends inside its group's shared blocks
+    (a new token that would land in a shared block): NaN output row, nothing
+    stored for it; every other sequence as in the normal step."""
+    from paged_kv_cache_211_amd import paged_attention_prefix_plan
+    wl = _workload(G, seed=170 + G)
+    c = wl.cfg
+    _case(f"shared-prefix decode step, new token inside the shared blocks, G={G}")
+    st, _ = replay.build(wl)
+    ref, _ = oracle_out(wl, st)
+    cs, ss = H.build(wl, poison=True, write_step=False)
+    inp = cs.decode_inputs(range(c.S), c.partition, prefix=True, num_q_heads=c.H_q,
+                           prefix_min_blocks=1)
+    pblocks = int(inp["prefix"]["group_prefix_blocks"][0])
+    bad = 3
+    lens = inp["lens_host"].copy()
+    lens[bad] = pblocks * c.bs        # its last token is the shared blocks' last
+    inp["context_lens"] = torch.from_numpy(lens).cuda()
+    go = inp["prefix"]["group_offsets"].cpu().numpy()
+    plan = paged_attention_prefix_plan(lens, go, np.array([pblocks]), c.bs, c.partition, c.H_q,
+                                       c.H_kv)
+    inp["prefix"] = {k: torch.from_numpy(plan[k]).cuda()
+                     for k in ("group_offsets", "group_prefix_blocks", "row_offsets",
+                               "suffix_offsets", "token_start", "prefix_item_offsets")}
+    inp["prefix_totals"] = plan["totals"]
+    bits = lambda t: t.view(torch.int16)   # bf16 pools; NaN poison compares by bits
+    kc0, vc0 = bits(cs.key_cache).clone(), bits(cs.value_cache).clone()
+    got, _ = prefix_step(cs, ss, wl, c.partition, inp=inp)
+    assert np.isnan(got[bad]).all()
+    others = [s for s in range(c.S) if s != bad]
+    assert np.isfinite(got[others]).all()
+    assert np.abs(got[others] - ref[others]).max() <= TOL[c.kv_dtype]
+    # the cache changed exactly in the other sequences' new-token slots
+    slots = ss["slots"]
+    changed_k = (bits(cs.key_cache) != kc0).nonzero()[:, 0].unique().cpu().numpy()
+    changed_v = (bits(cs.value_cache) != vc0).nonzero()[:, 0].unique().cpu().numpy()
+    want_blocks = np.unique(np.delete(slots, bad) // c.bs)
+    assert set(changed_k.tolist()) <= set(want_blocks.tolist())
+    assert set(changed_v.tolist()) <= set(want_blocks.tolist())
+    assert int(slots[bad]) // c.bs not in set(changed_k.tolist()) | set(changed_v.tolist())
+    shared = set(inp["block_tables"][bad, :pblocks].cpu().tolist())
+    assert not (shared & (set(changed_k.tolist()) | set(changed_v.tolist())))

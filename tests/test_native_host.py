@@ -345,6 +345,24 @@ def test_decode_argument_validation_needs_no_gpu(pkv):
     assert L.paged_attention_decode_noalloc(None, fake, fake, fake, fake, 4, fake, 2, 8, 2, 128, 16,
                                             10, 0.1, 1, 1, 1.0, 1.0, 0, None, 0, None) == -1
     assert b"workspace" in L.pkv_last_error() or L.pkv_last_error() != b""
+    # the shared-prefix decode step: bf16 only, both new rows required, the
+    # plan's totals checked, all before any launch
+    def pcall(**kw):
+        a = dict(good, nk=fake, nv=fake, P=32, rows=4, nsuf=2, items=2, ws=fake, wsb=1 << 30)
+        a.update(kw)
+        return L.paged_attention_decode_prefix_step(
+            a["out"], a["q"], a["nk"], a["nv"], a["kc"], a["vc"], a["tb"], a["mb"], a["lens"],
+            a["S"], a["Hq"], a["Hkv"], a["D"], a["bs"], a["nb"], a["scale"], a["qd"], a["cd"],
+            a["ks"], a["vs"], a["P"], fake, fake, 1, fake, fake, fake, fake, a["rows"],
+            a["nsuf"], a["items"], a["ws"], a["wsb"], None)
+
+    assert pcall(nk=None) == -1
+    assert pcall(nv=None) == -1
+    assert pcall(P=0) == -1
+    assert pcall(rows=1) == -1              # fewer partial rows than sequences
+    assert pcall(cd=2, bs=32) == -2         # fp8 cache
+    assert b"shared-prefix" in L.pkv_last_error()
+    assert pcall(D=64) == -2
     w = L.paged_kv_write(fake, fake, fake, fake, fake, 4, 2, 96, 16, 10, 1, 1, 1.0, 1.0, None)
     assert w == -2
     w = L.paged_kv_write(fake, fake, fake, fake, fake, 4, 2, 128, 16, 10, 1, 2, -1.0, 1.0, None)
