@@ -57,7 +57,7 @@ PREFILL_METRIC = "chunked prefill µs/step (store chunk + causal attention) + ma
 ELEM = {"f32": 4, "bf16": 2, "fp8": 1}
 # sources of the decode kernels: a counter file taken on other sources is stale
 SRC_FILES = ("decode.hip", "decode_valu.h", "decode_f32.hip", "decode_bf16.hip", "decode_fp8.hip",
-             "decode_mfma.hip", "decode_common.h", "pkv_device.h")
+             "decode_mfma.hip", "decode_prefix.hip", "decode_common.h", "pkv_device.h")
 
 
 def log(*a):
