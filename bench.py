@@ -762,9 +762,7 @@ def main():
     # the same reads without the arithmetic (split-K schedules): the rate the
     # decode's access pattern itself reaches on this device
     paged_probe_us = None
-    mfma_shape = c.kv_dtype == "fp8" and c.q_dtype == "bf16" and c.G % 8 == 0 and c.d == 128 \
-        and c.bs == 32   # the matrix-core kernel reads each tile once per kv head: another pattern
-    if P and not (PF or SK or mfma_shape):
+    if P and not (PF or SK):
         psink = torch.zeros(4, dtype=torch.int32, device=dev)
 
         def run_paged_probe(i):

@@ -584,10 +584,11 @@ int paged_kv_gather(void* k_out, void* v_out, const void* key_cache, const void*
  * 1). */
 int pkv_hbm_read_probe(const void* buffer, size_t bytes, void* sink, int workgroups, void* stream);
 
-/* pkv_paged_read_probe -- measurement aid: the reads of paged_attention_
- * decode's vector-ALU split-K kernel and nothing else (same grid, workgroup
- * order, block-table walk and tile ring; no arithmetic, no partials, no
- * reduce).  Arguments as paged_attention_decode without out, query, scale
+/* pkv_paged_read_probe -- measurement aid: the reads of the split-K kernel
+ * paged_attention_decode runs for this shape (the vector-ALU kernel, or the
+ * matrix-core kernel of fp8 caches with 8 query heads per kv head) and
+ * nothing else (same grid, workgroup order, block-table walk and tile ring;
+ * no arithmetic, no partials, no reduce).  Arguments as paged_attention_decode without out, query, scale
  * and the workspace (k/v scales do not matter); partition_tokens must be > 0.
  * sink: 16-byte aligned device memory of which at most 4 bytes are written.
  * Timing it gives the rate that the decode's access pattern (scattered

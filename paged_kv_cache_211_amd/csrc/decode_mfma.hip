@@ -72,6 +72,10 @@ constexpr int kD = 128, kBS = 32, kHPW = 8;
 constexpr int kTile = kBS * kD;         // bytes of an fp8 (block, kv head) tile
 constexpr int kNLoad = kTile / 1024;    // 4 loads of 16 bytes per lane
 constexpr int kQBytes = kHPW * kD * 2;  // the 8 query rows of an item (bf16)
+// split-K partitions shorter than this many tokens keep two tiles in flight
+// per wave (the skewed fp8 workload at 512-token partitions: step 303 -> 299
+// us; at 1536 one tile measures 1% faster)
+constexpr int kDeepBelow = 1024;
 
 // The 8 query heads of one kv head held by one wave: the query as MFMA A
 // operands, the online-softmax state of rows r = 0..3 (head 4g + r) and the
@@ -223,7 +227,9 @@ struct MfmaHeads {
 // for the 8 query heads qh0 .. qh0+7 of kv head hkv, then the output rows
 // (final_out) or the partial rows prow0 + h (h = 0..7) of ws_o / ws_ml.
 // prow: this wave's LDS rows.  store_new: first store the sequence's new
-// token (decode step; the wave reads the block that receives it).
+// token (decode step; the wave reads the block that receives it).  NBUF:
+// tiles in flight per wave.
+template <int NBUF = kMfmaBufs>
 __device__ __forceinline__ void mfma_item(const DecodeArgs& a, int s, int hkv, int qh0, int jfirst,
                                           int jend, int t1, bool bad, bool final_out, size_t prow0,
                                           float* ws_o, float* ws_ml, uint16_t (*prow)[kBS],
@@ -235,7 +241,7 @@ __device__ __forceinline__ void mfma_item(const DecodeArgs& a, int s, int hkv, i
   MfmaHeads h;
   h.set_q((const uint16_t*)a.q + ((size_t)s * a.Hq + qh0) * kD, col, g);
   h.reset();
-  tile_loop<kMfmaBufs, kNLoad, 1>(
+  tile_loop<NBUF, kNLoad, 1>(
       tbl, jfirst, jend, a.nb, (const uint8_t*)a.kc + head_off + lane * 16,
       (const uint8_t*)a.vc + head_off + col * 32 + g * 16, blk_stride, lane, bad,
       [&](int j, const u32x4* kr, const u32x4* vr) { h.tile(a.qk_mult, j, t1, kr, vr, prow, col, g); },
@@ -293,8 +299,10 @@ __device__ __forceinline__ MItem split_item(const DecodeArgs& a, int x, int nhg,
 // head).  One pass (SPLIT = false): item = sequence.  STORE (decode step,
 // one group of 8 query heads per kv head): the wave that reads a sequence's
 // last block first stores the sequence's new token; it is that block's only
-// reader.
-template <int NW, bool SPLIT, bool STORE = false>
+// reader.  NBUF: tiles in flight per wave (two for split-K partitions shorter
+// than kDeepBelow tokens, whose items are short enough that the first
+// tiles' latency is a large share of each).
+template <int NW, bool SPLIT, bool STORE = false, int NBUF = kMfmaBufs>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void decode_mfma_fp8_kernel(const DecodeArgs a) {
   __shared__ uint16_t p_lds[NW][kHPW][kBS];
@@ -309,7 +317,7 @@ void decode_mfma_fp8_kernel(const DecodeArgs a) {
   float* ws_ml = a.ws + (size_t)a.total_parts * a.Hq * kD;
   if constexpr (SPLIT) {
     const MItem it = split_item<STORE>(a, item * nhg + hg, nhg, lane, a.part_off, a.lens);
-    mfma_item(a, it.s, it.hkv, it.qh0, it.j0, it.jend, it.t1, it.bad, it.final_out,
+    mfma_item<NBUF>(a, it.s, it.hkv, it.qh0, it.j0, it.jend, it.t1, it.bad, it.final_out,
               (size_t)it.row * a.Hq + it.qh0, a.ws, ws_ml, p_lds[w], lane, it.store, it.L);
   } else {
     const int s = item, hkv = hg / (G / kHPW);
@@ -318,9 +326,40 @@ void decode_mfma_fp8_kernel(const DecodeArgs a) {
     bool bad = false;
     if (L < 0) { L = 0; bad = true; }
     if (L > a.max_blocks * kBS) { L = a.max_blocks * kBS; bad = true; }
-    mfma_item(a, s, hkv, qh0, 0, (L + kBS - 1) / kBS, L, bad, true, 0, a.ws, ws_ml, p_lds[w],
+    mfma_item<NBUF>(a, s, hkv, qh0, 0, (L + kBS - 1) / kBS, L, bad, true, 0, a.ws, ws_ml, p_lds[w],
               lane, STORE && !bad && L > 0, L);
   }
+}
+
+// Paged read probe for this kernel's shape (a measurement aid): the split-K
+// kernel above without its arithmetic -- same grid, item mapping
+// (split_item), block-table walk, tile ring and per-lane addresses (value
+// rows permuted as the products need them) -- every tile folded into a
+// checksum that is stored only on a value nobody expects.
+template <int NW, int NBUF>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
+void paged_read_probe_mfma_kernel(const DecodeArgs a, uint32_t* __restrict__ sink) {
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int col = lane & 31, g = lane >> 5;
+  const int nhg = a.Hkv * (a.Hq / a.Hkv / kHPW);
+  const int hg = blockIdx.x % nhg;
+  const int item = (blockIdx.x / nhg) * NW + w;
+  if (item >= a.total_parts) return;
+  const MItem it = split_item<false>(a, item * nhg + hg, nhg, lane, a.part_off, a.lens);
+  bool bad = it.bad;
+  const int32_t* __restrict__ tbl = a.tables + (size_t)it.s * a.max_blocks;
+  const size_t head_off = (size_t)it.hkv * kTile;
+  uint32_t acc = 0;
+  tile_loop<NBUF, kNLoad, 1>(
+      tbl, it.j0, it.jend, a.nb, (const uint8_t*)a.kc + head_off + lane * 16,
+      (const uint8_t*)a.vc + head_off + col * 32 + g * 16, (size_t)a.Hkv * kTile, lane, bad,
+      [&](int, const u32x4* kr, const u32x4* vr) {
+#pragma unroll
+        for (int l = 0; l < kNLoad; ++l)
+          acc ^= kr[l].x ^ kr[l].y ^ kr[l].z ^ kr[l].w ^ vr[l].x ^ vr[l].y ^ vr[l].z ^ vr[l].w;
+      });
+  if (acc == 0x9e3779b9u && !bad) sink[0] = acc;
 }
 
 // ---- persistent split-K with a work counter --------------------------------
@@ -576,6 +615,19 @@ bool decode_queue_supported(const DecodeArgs& a) {
          a.S <= kMaxCachedSeqs && n_items < (1ll << kCountBits) - (1ll << 20);
 }
 
+int launch_paged_read_probe_mfma(const DecodeArgs& a, uint32_t* sink, void* stream) {
+  if (a.partition <= 0) return (int)hipErrorInvalidValue;
+  const int nhg = a.Hkv * (a.Hq / a.Hkv / 8);
+  dim3 block(kWaves * 64), grid((a.total_parts + kWaves - 1) / kWaves * nhg);
+  if (a.partition < kDeepBelow)
+    hipLaunchKernelGGL((paged_read_probe_mfma_kernel<kWaves, 2>), grid, block, 0,
+                       (hipStream_t)stream, a, sink);
+  else
+    hipLaunchKernelGGL((paged_read_probe_mfma_kernel<kWaves, kMfmaBufs>), grid, block, 0,
+                       (hipStream_t)stream, a, sink);
+  return (int)hipGetLastError();
+}
+
 int launch_decode_mfma(const DecodeArgs& a, void* stream, bool store) {
   hipStream_t st = (hipStream_t)stream;
   const int groups = a.Hq / a.Hkv / 8;
@@ -584,7 +636,12 @@ int launch_decode_mfma(const DecodeArgs& a, void* stream, bool store) {
   const int nhg = a.Hkv * groups;
   const int items = a.partition > 0 ? a.total_parts : a.S;
   dim3 grid((items + kWaves - 1) / kWaves * nhg);
-  if (a.partition > 0) {
+  if (a.partition > 0 && a.partition < kDeepBelow) {
+    if (store)
+      hipLaunchKernelGGL((decode_mfma_fp8_kernel<kWaves, true, true, 2>), grid, block, 0, st, a);
+    else
+      hipLaunchKernelGGL((decode_mfma_fp8_kernel<kWaves, true, false, 2>), grid, block, 0, st, a);
+  } else if (a.partition > 0) {
     if (store)
       hipLaunchKernelGGL((decode_mfma_fp8_kernel<kWaves, true, true>), grid, block, 0, st, a);
     else

@@ -1,5 +1,6 @@
 // Paged read probe (a measurement aid): the vector-ALU split-K decode's
-// memory reads without its arithmetic.  Same grid, same workgroup order,
+// memory reads without its arithmetic (shapes the matrix-core kernel serves
+// go to its own probe, decode_mfma.hip).  Same grid, same workgroup order,
 // same item mapping (locate), same block-table walk and tile ring
 // (tile_loop): every key and value tile the decode reads is read here, and
 // only folded into a checksum.  Timing it gives the rate this access
@@ -58,6 +59,7 @@ int launch_probe_t(const DecodeArgs& a, uint32_t* sink, hipStream_t st) {
 
 int launch_paged_read_probe(const DecodeArgs& a, uint32_t* sink, void* stream) {
   hipStream_t st = (hipStream_t)stream;
+  if (decode_mfma_eligible(a)) return launch_paged_read_probe_mfma(a, sink, stream);
   switch (a.kv_dtype) {
     case PKV_F32: return launch_probe_t<PKV_F32>(a, sink, st);
     case PKV_BF16: return launch_probe_t<PKV_BF16>(a, sink, st);

@@ -155,9 +155,12 @@ int launch_prefill(const PrefillArgs& a, void* stream);
 // (decode_mfma.hip); launch_decode routes eligible calls there.
 bool decode_mfma_eligible(const DecodeArgs& a);
 int launch_decode_mfma(const DecodeArgs& a, void* stream, bool store = false);
-// Paged read probe (paged_probe.hip): the vector-ALU split-K decode's reads,
-// no arithmetic; at most one word stored to sink.
+// Paged read probe (paged_probe.hip): the split-K decode's reads for this
+// shape (vector-ALU kernel, or the matrix-core kernel's through
+// launch_paged_read_probe_mfma in decode_mfma.hip), no arithmetic; at most
+// one word stored to sink.
 int launch_paged_read_probe(const DecodeArgs& a, uint32_t* sink, void* stream);
+int launch_paged_read_probe_mfma(const DecodeArgs& a, uint32_t* sink, void* stream);
 // The work-counter split-K schedule (fp8 matrix-core shape only): whether a
 // call qualifies, and its launch.
 bool decode_queue_supported(const DecodeArgs& a);
