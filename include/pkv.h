@@ -637,7 +637,12 @@ int pkv_paged_read_probe(const void* key_cache, const void* value_cache,
  *     PKV_ERR_INVALID; block_table returns its host slots;
  *   - a clock ticks on add, fork (the child), append, swap_in and touch,
  *     stamping that sequence; lru names the resident sequence with at least
- *     one block, all unshared, whose stamp is oldest (PKV_ERR_SEQ if none).
+ *     one block, all unshared, whose stamp is oldest (PKV_ERR_SEQ if none);
+ *   - the same events count a sequence's uses (a new or forked sequence
+ *     starts at 1); lfu names, among the same candidates, the one with the
+ *     fewest uses, the oldest stamp among equals (least frequently used:
+ *     §4.1 advises LRU for document processing and LFU for batch work; its
+ *     comparison table is missing, so the choice stays with the caller).
  *  The pairs drive paged_kv_swap_blocks, which moves the data.
  * ------------------------------------------------------------------------- */
 typedef struct pkv_alloc pkv_alloc;
@@ -687,6 +692,8 @@ int pkv_alloc_swap_in(pkv_alloc* a, int64_t seq, int32_t* pairs_out, int cap, in
 int pkv_alloc_touch(pkv_alloc* a, int64_t seq);
 /* *seq_out = the least recently used sequence that can be swapped out. */
 int pkv_alloc_lru(const pkv_alloc* a, int64_t* seq_out);
+/* *seq_out = the least frequently used sequence that can be swapped out. */
+int pkv_alloc_lfu(const pkv_alloc* a, int64_t* seq_out);
 /* 1 if seq is swapped out, 0 if resident, or a negative error. */
 int pkv_alloc_is_swapped(const pkv_alloc* a, int64_t seq);
 int pkv_alloc_num_host_free(const pkv_alloc* a);

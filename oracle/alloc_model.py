@@ -47,7 +47,12 @@ of policy; only its stated rules below are pinned):
   * least recently used: a logical clock ticks on add, fork (the child),
     append, swap_in and touch, stamping that sequence; ``lru()`` names the
     resident sequence with at least one block, all of them unshared, whose
-    stamp is oldest.
+    stamp is oldest;
+  * least frequently used ("PagedAttention Kernel…" §4.1 advises it for
+    batch work, LRU for document processing): the same events count each
+    sequence's uses, a new or forked sequence starting at one; ``lfu()``
+    names, among the same candidates, the one with the fewest uses, the
+    oldest stamp breaking ties.
 
 Pins (tests/test_oracle_alloc.py): the invariants the pages state (only the
 last block of a sequence may be partly filled; block count = ceil(len/bs);
@@ -90,6 +95,7 @@ class AllocModel:
         self.num_host = 0
         self.swapped: set[int] = set()
         self.stamp: dict[int, int] = {}
+        self.uses: dict[int, int] = {}
         self.clock = 0
 
     # -- helpers ---------------------------------------------------------
@@ -103,6 +109,7 @@ class AllocModel:
     def _tick(self, seq: int):
         self.clock += 1
         self.stamp[seq] = self.clock
+        self.uses[seq] = self.uses.get(seq, 0) + 1
 
     def _resident(self, seq: int):
         if seq not in self.tables:
@@ -181,6 +188,7 @@ class AllocModel:
                 self._drop(b)
         del self.lens[seq]
         del self.stamp[seq]
+        del self.uses[seq]
 
     def set_host_pool(self, num_host_blocks: int):
         if num_host_blocks < 0:
@@ -231,12 +239,18 @@ class AllocModel:
             raise AllocError(ERR_SEQ, f"unknown sequence {seq}")
         self._tick(seq)
 
-    def lru(self) -> int:
+    def _victims(self) -> list[int]:
         cands = [s for s, t in self.tables.items()
                  if s not in self.swapped and t and all(self.ref[b] == 1 for b in t)]
         if not cands:
             raise AllocError(ERR_SEQ, "no sequence can be swapped out")
-        return min(cands, key=lambda s: self.stamp[s])
+        return cands
+
+    def lru(self) -> int:
+        return min(self._victims(), key=lambda s: self.stamp[s])
+
+    def lfu(self) -> int:
+        return min(self._victims(), key=lambda s: (self.uses[s], self.stamp[s]))
 
     # -- queries ---------------------------------------------------------
     def table(self, seq: int) -> list[int]:

@@ -649,6 +649,11 @@ class BlockAllocator:
         check(lib().pkv_alloc_lru(self._h, ctypes.byref(out)))
         return int(out.value)
 
+    def lfu(self) -> int:
+        out = ctypes.c_int64(0)
+        check(lib().pkv_alloc_lfu(self._h, ctypes.byref(out)))
+        return int(out.value)
+
     def is_swapped(self, seq: int) -> bool:
         return bool(check_nonneg(lib().pkv_alloc_is_swapped(self._h, int(seq))))
 

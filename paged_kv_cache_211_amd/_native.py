@@ -102,6 +102,7 @@ SIGNATURES = {
     "pkv_alloc_swap_in": (i32, [vp, i64, pi32, i32, ctypes.POINTER(i32)]),
     "pkv_alloc_touch": (i32, [vp, i64]),
     "pkv_alloc_lru": (i32, [vp, ctypes.POINTER(i64)]),
+    "pkv_alloc_lfu": (i32, [vp, ctypes.POINTER(i64)]),
     "pkv_alloc_is_swapped": (i32, [vp, i64]),
     "pkv_alloc_num_host_free": (i32, [vp]),
 }

@@ -34,7 +34,8 @@ struct pkv_alloc {
     std::vector<int32_t> table;     // device blocks, or host slots when swapped
     int64_t len = 0;
     bool swapped = false;
-    int64_t stamp = 0;
+    int64_t stamp = 0;              // clock at the last use
+    int64_t uses = 0;               // uses counted on the same events
   };
   std::unordered_map<int64_t, Seq> seqs;
 };
@@ -49,6 +50,31 @@ void drop_ref(pkv_alloc* a, int32_t b) {
 
 int swapped_out(int64_t seq) {
   return pkv::fail(PKV_ERR_INVALID, "sequence %lld is swapped out", (long long)seq);
+}
+
+// The resident sequence with at least one block, all unshared, that is
+// smallest in (by_uses ? uses : 0, stamp): the victim of either policy.
+int pick_victim(const pkv_alloc* a, bool by_uses, int64_t* seq_out) {
+  if (!a || !seq_out) return pkv::fail(PKV_ERR_INVALID, "null argument");
+  bool found = false;
+  int64_t best = 0, best_uses = 0, best_stamp = 0;
+  for (const auto& kv : a->seqs) {
+    const pkv_alloc::Seq& s = kv.second;
+    if (s.swapped || s.table.empty()) continue;
+    bool shared = false;
+    for (int32_t b : s.table) shared = shared || a->ref[b] != 1;
+    if (shared) continue;
+    const int64_t u = by_uses ? s.uses : 0;
+    if (!found || u < best_uses || (u == best_uses && s.stamp < best_stamp)) {
+      found = true;
+      best = kv.first;
+      best_uses = u;
+      best_stamp = s.stamp;
+    }
+  }
+  if (!found) return pkv::fail(PKV_ERR_SEQ, "no sequence can be swapped out");
+  *seq_out = best;
+  return PKV_OK;
 }
 
 }  // namespace
@@ -96,6 +122,7 @@ int pkv_alloc_add_seq(pkv_alloc* a, int64_t seq) {
   if (a->seqs.count(seq)) return pkv::fail(PKV_ERR_SEQ, "sequence %lld exists", (long long)seq);
   pkv_alloc::Seq s;
   s.stamp = ++a->clock;
+  s.uses = 1;
   a->seqs.emplace(seq, std::move(s));
   return PKV_OK;
 }
@@ -109,6 +136,7 @@ int pkv_alloc_fork(pkv_alloc* a, int64_t parent, int64_t child) {
   pkv_alloc::Seq c = it->second;  // copy before emplace may rehash
   for (int32_t b : c.table) ++a->ref[b];
   c.stamp = ++a->clock;
+  c.uses = 1;   // a new sequence: its own count
   a->seqs.emplace(child, std::move(c));
   return PKV_OK;
 }
@@ -162,6 +190,7 @@ int pkv_alloc_append(pkv_alloc* a, int64_t seq, int n_tokens, int32_t* slots_out
   }
   if (n_cow_out) *n_cow_out = n_cow;
   s.stamp = ++a->clock;
+  ++s.uses;
   return PKV_OK;
 }
 
@@ -240,6 +269,7 @@ int pkv_alloc_swap_in(pkv_alloc* a, int64_t seq, int32_t* pairs_out, int cap, in
   }
   s.swapped = false;
   s.stamp = ++a->clock;
+  ++s.uses;
   if (n_out) *n_out = (int)n;
   return PKV_OK;
 }
@@ -249,29 +279,13 @@ int pkv_alloc_touch(pkv_alloc* a, int64_t seq) {
   auto it = a->seqs.find(seq);
   if (it == a->seqs.end()) return no_seq(seq);
   it->second.stamp = ++a->clock;
+  ++it->second.uses;
   return PKV_OK;
 }
 
-int pkv_alloc_lru(const pkv_alloc* a, int64_t* seq_out) {
-  if (!a || !seq_out) return pkv::fail(PKV_ERR_INVALID, "null argument");
-  bool found = false;
-  int64_t best = 0, best_stamp = 0;
-  for (const auto& kv : a->seqs) {
-    const pkv_alloc::Seq& s = kv.second;
-    if (s.swapped || s.table.empty()) continue;
-    bool shared = false;
-    for (int32_t b : s.table) shared = shared || a->ref[b] != 1;
-    if (shared) continue;
-    if (!found || s.stamp < best_stamp) {
-      found = true;
-      best = kv.first;
-      best_stamp = s.stamp;
-    }
-  }
-  if (!found) return pkv::fail(PKV_ERR_SEQ, "no sequence can be swapped out");
-  *seq_out = best;
-  return PKV_OK;
-}
+int pkv_alloc_lru(const pkv_alloc* a, int64_t* seq_out) { return pick_victim(a, false, seq_out); }
+
+int pkv_alloc_lfu(const pkv_alloc* a, int64_t* seq_out) { return pick_victim(a, true, seq_out); }
 
 int pkv_alloc_is_swapped(const pkv_alloc* a, int64_t seq) {
   if (!a) return pkv::fail(PKV_ERR_INVALID, "null allocator");

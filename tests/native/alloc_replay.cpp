@@ -10,7 +10,7 @@
 //   add S | fork P C | free S | touch S | pool N
 //   append S N                    -> rc, slots, copy-on-write pairs
 //   out S | in S                  -> rc, swap pairs
-//   lru                           -> rc, sequence
+//   lru | lfu                     -> rc, sequence
 //   state K s_0 .. s_{K-1}        -> free list, refcounts, host free count,
 //                                    then len / swapped / table of each s_i
 //   poff P N L_0 ..               -> rc, partition offsets
@@ -102,9 +102,9 @@ int main() {
         pairs.resize(2 * (size_t)n);
         put(out, pairs);
       }
-    } else if (cmd == "lru") {
+    } else if (cmd == "lru" || cmd == "lfu") {
       int64_t s = -1;
-      const int rc = pkv_alloc_lru(a, &s);
+      const int rc = cmd == "lru" ? pkv_alloc_lru(a, &s) : pkv_alloc_lfu(a, &s);
       out << "rc " << rc;
       if (rc == PKV_OK) out << ' ' << (long long)s;
     } else if (cmd == "state") {

@@ -186,6 +186,30 @@ def test_swap_hand_traced_example():
     assert m.free_list() == [2, 0] and m.table(1) == [3, 1]
 
 
+def test_lfu_hand_traced_example():
+    """Least frequently used, traced by hand: add, fork (the child),
+    append, swap_in and touch each count one use; the fewest uses wins, the
+    oldest stamp breaks ties; sequences holding shared blocks never qualify.
+    The trace ends where the two policies name different sequences."""
+    m = AllocModel(6, 2, range(6))
+    m.add_seq(0); m.append(0, 2)             # uses 2, stamp 2
+    m.add_seq(1); m.append(1, 2); m.append(1, 1)   # uses 3, stamp 5
+    assert (m.lru(), m.lfu()) == (0, 0)
+    m.touch(0)                               # uses 3, stamp 6: a tie on uses
+    assert (m.lru(), m.lfu()) == (1, 1)
+    m.touch(0)                               # uses 4, stamp 7
+    assert (m.lru(), m.lfu()) == (1, 1)
+    m.touch(1)                               # uses 4, stamp 8: a tie, 0 older
+    assert (m.lru(), m.lfu()) == (0, 0)
+    m.touch(1); m.touch(1)                   # uses 6, stamp 10
+    m.add_seq(2); m.append(2, 1)             # uses 2, stamp 12
+    assert (m.lru(), m.lfu()) == (0, 2)
+    m.fork(2, 3)                             # 2 and 3 share a block: neither qualifies
+    assert (m.lru(), m.lfu()) == (0, 0)
+    m.free_seq(0)
+    assert (m.lru(), m.lfu()) == (1, 1)
+
+
 def test_swap_rules_on_random_ops():
     """Random ops with swaps: every device block is held by resident tables
     only, host slots by swapped tables only, lengths survive swaps, and the
@@ -200,17 +224,18 @@ def test_swap_rules_on_random_ops():
         host = [None] * nh
         label = {}                          # (seq, logical block) -> label it must hold
         live, nxt, order = [], 0, []        # order: test's own recency list
+        uses = {}                           # the test's own use counts
         for step in range(60):
             r = rng.random()
             try:
                 if r < 0.15 or not live:
-                    m.add_seq(nxt); live.append(nxt); order.append(nxt); nxt += 1
+                    m.add_seq(nxt); live.append(nxt); order.append(nxt); uses[nxt] = 1; nxt += 1
                 elif r < 0.25:
                     p = int(rng.choice(live))
                     m.fork(p, nxt)
                     for j in range(len(m.table(nxt))):
                         label[(nxt, j)] = label[(p, j)]
-                    live.append(nxt); order.append(nxt); nxt += 1
+                    live.append(nxt); order.append(nxt); uses[nxt] = 1; nxt += 1
                 elif r < 0.55:
                     s = int(rng.choice(live))
                     before = len(m.table(s)) if not m.is_swapped(s) else None
@@ -220,7 +245,7 @@ def test_swap_rules_on_random_ops():
                     for j, b in enumerate(m.table(s)):
                         if j >= before:
                             dev[b] = label[(s, j)] = (trial, step, s, j)
-                    order.remove(s); order.append(s)
+                    order.remove(s); order.append(s); uses[s] += 1
                 elif r < 0.7:
                     s = int(rng.choice(live))
                     for b, h in m.swap_out(s):
@@ -229,13 +254,13 @@ def test_swap_rules_on_random_ops():
                     s = int(rng.choice(live))
                     for h, b in m.swap_in(s):
                         dev[b] = host[h]
-                    order.remove(s); order.append(s)
+                    order.remove(s); order.append(s); uses[s] += 1
                 elif r < 0.9:
                     s = int(rng.choice(live))
-                    m.touch(s); order.remove(s); order.append(s)
+                    m.touch(s); order.remove(s); order.append(s); uses[s] += 1
                 else:
                     s = int(rng.choice(live))
-                    m.free_seq(s); live.remove(s); order.remove(s)
+                    m.free_seq(s); live.remove(s); order.remove(s); del uses[s]
                     for k in [k for k in label if k[0] == s]:
                         del label[k]
             except AllocError:
@@ -261,6 +286,10 @@ def test_swap_rules_on_random_ops():
                     and all(m.refcount(b) == 1 for b in m.table(s))]
             if elig:
                 assert m.lru() == elig[0]
+                # LFU: fewest uses by the test's own count, recency breaking ties
+                assert m.lfu() == min(elig, key=lambda s: (uses[s], order.index(s)))
             else:
                 with pytest.raises(AllocError):
                     m.lru()
+                with pytest.raises(AllocError):
+                    m.lfu()

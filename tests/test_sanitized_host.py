@@ -109,6 +109,9 @@ class SanAlloc:
     def lru(self):
         return self._rc(self.d.call("lru"))[2]
 
+    def lfu(self):
+        return self._rc(self.d.call("lfu"))[2]
+
     def state(self, seqs):
         r = self.d.call("state", len(seqs), *seqs)
         assert r[0] == "free"
@@ -138,7 +141,7 @@ def same(san, model, op, *args):
     except AllocError as e:
         r_s, err_s = None, e.code
     assert err_m == err_s, (op, args, err_m, err_s)
-    if err_m is None and op in ("append", "swap_out", "swap_in", "lru"):
+    if err_m is None and op in ("append", "swap_out", "swap_in", "lru", "lfu"):
         if op == "append":
             assert list(r_s[0]) == list(r_m[0]) and r_s[1] == [tuple(p) for p in r_m[1]]
         else:
@@ -197,8 +200,10 @@ def test_random_ops_with_swaps_under_sanitizers(driver):
                 same(s, m, "swap_in", int(rng.choice(live)))
             elif r < 0.8:
                 same(s, m, "touch", int(rng.choice(live)))
-            elif r < 0.85:
+            elif r < 0.82:
                 same(s, m, "lru")
+            elif r < 0.85:
+                same(s, m, "lfu")
             elif r < 0.88:
                 same(s, m, "set_host_pool", int(rng.integers(0, 12)))
             elif r < 0.91:
