@@ -75,6 +75,7 @@ def test_swap_round_trip(cfg_id, n_out, staged):
     for _ in range(n_out):
         v = cache.alloc.lru()
         assert v == st.model.lru()
+        assert cache.alloc.lfu() == st.model.lfu()   # the other victim policy agrees too
         pairs = cache.swap_out(v, staged=staged)
         assert pairs == st.model.swap_out(v)
         OL.move_blocks(hk, hv, st.kc, st.vc, pairs)
