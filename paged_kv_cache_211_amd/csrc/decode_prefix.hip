@@ -141,16 +141,19 @@ __device__ __forceinline__ void prefix_body(const DecodeArgs& a, const PrefixArg
     const size_t base1 = two ? block_base(i + 1) : base0;
     const size_t kb = (col < 16 ? base0 : base1);
     // ---- loads: 8 key units (one per dim slice), 4 value rows per block ----
+    // Plain (cached) loads: every row block of the group re-reads these
+    // blocks, so they should stay in the L2; the non-temporal policy of the
+    // streamed suffix tiles would mark them for early eviction.
     u32x4 kr[8], vr[2][4];
     // key unit (chunk 2sl + g, token col % 16) at ((2sl + g) * BS + token) * 16
     const uint8_t* kp = (const uint8_t*)a.kc + kb + (size_t)(g * BS + (col & 15)) * 16;
 #pragma unroll
-    for (int sl = 0; sl < 8; ++sl) kr[sl] = load16(kp + (size_t)sl * 2 * BS * 16);
+    for (int sl = 0; sl < 8; ++sl) kr[sl] = *(const u32x4*)(kp + (size_t)sl * 2 * BS * 16);
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
       const uint8_t* vp = (const uint8_t*)a.vc + (b == 0 ? base0 : base1) + col * (BS * 2) + g * 16;
 #pragma unroll
-      for (int m = 0; m < 4; ++m) vr[b][m] = load16(vp + (size_t)m * 32 * BS * 2);
+      for (int m = 0; m < 4; ++m) vr[b][m] = *(const u32x4*)(vp + (size_t)m * 32 * BS * 2);
     }
 
     // ---- scores S[row][token] for the 32 tokens of the pair ----
