@@ -306,14 +306,19 @@ __device__ __forceinline__ void suffix_wave(const DecodeArgs& b, int x, int lane
 // a), the rest the suffix pass over each sequence's own tokens (args b), one
 // wave per item.
 // Both are bound by memory latency, not bandwidth, so side by side on the
-// same compute units they hide each other's waits; npre is a multiple of 8
-// so the split-K workgroups keep their XCD order.  STORE: the decode step's
-// store in the suffix waves.
+// same compute units they hide each other's waits; npre is a multiple of 8,
+// so the regrouping of the prefix items by XCD below is a permutation of
+// [0, npre) and the split-K workgroups keep their XCD order.  STORE: the
+// decode step's store in the suffix waves.
 template <int HPW, bool STORE>
 __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void decode_prefix_fused_kernel(const DecodeArgs a, const DecodeArgs b, PrefixArgs p, int npre) {
   if ((int)blockIdx.x < npre) {
-    prefix_body<kWaves>(a, p, blockIdx.x);
+    // Workgroup ids go round robin over the 8 XCDs: XCD x runs the
+    // contiguous eighth x of the prefix items, so the workgroups that read
+    // one piece (consecutive items) share that XCD's L2.
+    const int bx = (int)blockIdx.x;
+    prefix_body<kWaves>(a, p, (bx % 8) * (npre / 8) + bx / 8);
   } else {
     __shared__ float p_lds[kWaves][HPW][kPBS];
     __shared__ u32x4 q_lds[kQLds ? kWaves : 1][kQLds ? HPW * kPD * 2 / 16 : 1];
