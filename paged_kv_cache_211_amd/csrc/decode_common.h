@@ -218,7 +218,7 @@ __device__ __forceinline__ Work locate(const DecodeArgs& a, int hpw, int lane, i
   wk.qh0 = wk.hkv * G + (hg % groups) * hpw;
   wk.item = item;
   int part;
-  int tstart = 0;
+  int tstart = 0, nsuf = 0;
   if constexpr (SPLIT) {
     if (a.t_start) {
       wk.s = min(__builtin_amdgcn_readfirstlane(find_seq(a.part_off, a.S, item, lane)), a.S - 1);
@@ -232,6 +232,7 @@ __device__ __forceinline__ Work locate(const DecodeArgs& a, int hpw, int lane, i
     if (a.t_start) {   // shared-prefix suffix pass: always a partial row
       tstart = a.t_start[wk.s];
       wk.item = a.row_off[wk.s] + part;
+      nsuf = wk.nparts;
       wk.nparts = 2;
     }
   } else {
@@ -247,6 +248,13 @@ __device__ __forceinline__ Work locate(const DecodeArgs& a, int hpw, int lane, i
   // split-K offsets must describe this length: ceil(L / P) partitions (one
   // for L = 0); stale offsets would drop tokens or leave rows unwritten
   if (SPLIT && !a.t_start && wk.nparts != split_parts(L, a.partition)) wk.bad = true;
+  // suffix pass: ceil((L - tstart) / P) partitions of the sequence's own
+  // tokens (a sequence without own tokens may hold one empty partition)
+  if (SPLIT && a.t_start) {
+    const int own = L - tstart;
+    const int want = own > 0 ? (int)(((int64_t)own + a.partition - 1) / a.partition) : 0;
+    if (own < 0 || (nsuf != want && !(want == 0 && nsuf == 1))) wk.bad = true;
+  }
   wk.L = L;
   wk.t0 = SPLIT ? tstart + part * a.partition : 0;
   wk.t1 = SPLIT ? min(L, wk.t0 + a.partition) : L;

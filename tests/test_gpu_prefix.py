@@ -66,7 +66,8 @@ def test_prefix_detected_groups(G):
     go, gb = cache.shared_prefix_groups(range(c.S), min_blocks=1)
     # one group of every sequence sharing the prefix's full blocks
     assert go.tolist() == [0, c.S] and gb.tolist() == [c.prefix // c.bs]
-    for P in (c.bs, c.partition, 4 * c.partition):
+    # one-block suffix partitions, the workload's, and longer than any suffix
+    for P in (c.bs, c.partition, 4 * c.partition, 1 << 16):
         got, inp = prefix_decode(cache, step, wl, P)
         assert inp["prefix_totals"][2] > 0
         assert np.isfinite(got).all()
@@ -112,6 +113,86 @@ def test_prefix_explicit_groups(groups):
         got, _ = prefix_decode(cache, step, wl, P, groups=(np.array(groups[0]), np.array(groups[1])))
         assert np.isfinite(got).all()
         assert np.abs(got - ref).max() <= TOL[c.kv_dtype], P
+
+
+@pytest.mark.parametrize("G", [4, 1])
+def test_prefix_contexts_ending_at_the_shared_blocks(G):
+    """Contexts that end exactly where the shared blocks end (no own token),
+    one token after them, and inside the first own block, attended over by
+    the decode (not the step), with suffix partitions of one block, of the
+    workload's length and longer than any suffix."""
+    from oracle import attention as OA
+    from paged_kv_cache_211_amd import paged_attention_prefix_plan
+    wl = _workload(G, seed=180 + G)
+    c = wl.cfg
+    _case(f"shared-prefix decode, contexts ending at the shared blocks, G={G}")
+    st, _ = replay.build(wl)
+    cache, step = H.build(wl, poison=True)
+    go, gb = cache.shared_prefix_groups(range(c.S), min_blocks=1)
+    pt = int(gb[0]) * c.bs
+    lens = np.asarray(wl.context_lens).astype(np.int64).copy()
+    lens[1], lens[4], lens[c.S - 1] = pt, pt + 1, pt
+    lens[2] = min(int(lens[2]), pt + c.bs - 3)
+    ref, _ = OA.paged_decode(wl.q, c.q_dtype, st.kc, st.vc, st.tables(c.S), lens, bs=c.bs,
+                             cache_dtype=c.kv_dtype, scale=c.scale, k_scale=c.k_scale,
+                             v_scale=c.v_scale)
+    for P in (c.bs, c.partition, 1 << 16):
+        inp = cache.decode_inputs(range(c.S), P, prefix=True, num_q_heads=c.H_q,
+                                  prefix_min_blocks=1)
+        inp["context_lens"] = torch.from_numpy(lens.astype(np.int32)).cuda()
+        plan = paged_attention_prefix_plan(lens.astype(np.int32), go, gb, c.bs, P, c.H_q, c.H_kv)
+        inp["prefix"] = {k: torch.from_numpy(plan[k]).cuda()
+                         for k in ("group_offsets", "group_prefix_blocks", "row_offsets",
+                                   "suffix_offsets", "token_start", "prefix_item_offsets")}
+        inp["prefix_totals"] = plan["totals"]
+        got, _ = prefix_decode(cache, step, wl, P, inp=inp)
+        assert np.isfinite(got).all()
+        err = np.abs(got - ref).max()
+        print(f"  partition {P}: suffix partitions {plan['totals'][1]}, max abs err {err:.3e}",
+              flush=True)
+        assert err <= TOL[c.kv_dtype], (P, err)
+
+
+def test_prefix_stale_suffix_offsets_poison_only_their_sequence():
+    """A plan made for a context one block shorter than the one the device
+    reads: where that changes the sequence's suffix partition count, its
+    output is NaN (not a silently truncated attention); where it does not,
+    the partitions still follow the device length and the output is right.
+    Every other sequence is right either way."""
+    from paged_kv_cache_211_amd import paged_attention_prefix_plan
+    wl = _workload(4, seed=190)
+    c = wl.cfg
+    _case("shared-prefix decode, stale suffix offsets for one sequence")
+    st, _ = replay.build(wl)
+    ref, _ = oracle_out(wl, st)
+    cache, step = H.build(wl, poison=True)
+    go, gb = cache.shared_prefix_groups(range(c.S), min_blocks=1)
+    lens = np.asarray(wl.context_lens).astype(np.int32)
+    pt = int(gb[0]) * c.bs
+    stale = int(np.argmax(lens))
+    assert lens[stale] > pt + c.bs
+    planned = lens.copy()
+    planned[stale] -= c.bs
+    seen_nan = False
+    for P in (c.bs, c.partition):
+        inp = cache.decode_inputs(range(c.S), P, prefix=True, num_q_heads=c.H_q,
+                                  prefix_min_blocks=1)
+        plan = paged_attention_prefix_plan(planned, go, gb, c.bs, P, c.H_q, c.H_kv)
+        inp["prefix"] = {k: torch.from_numpy(plan[k]).cuda()
+                         for k in ("group_offsets", "group_prefix_blocks", "row_offsets",
+                                   "suffix_offsets", "token_start", "prefix_item_offsets")}
+        inp["prefix_totals"] = plan["totals"]
+        got, _ = prefix_decode(cache, step, wl, P, inp=inp)
+        own = lambda L: -(-(int(L) - pt) // P)
+        if own(planned[stale]) != own(lens[stale]):
+            assert np.isnan(got[stale]).all(), P
+            seen_nan = True
+        else:
+            assert np.abs(got[stale] - ref[stale]).max() <= TOL[c.kv_dtype], P
+        others = [s for s in range(c.S) if s != stale]
+        assert np.isfinite(got[others]).all()
+        assert np.abs(got[others] - ref[others]).max() <= TOL[c.kv_dtype], P
+    assert seen_nan   # one block fewer is one partition fewer at P = block size
 
 
 def test_prefix_bad_block_poisons_the_group():
