@@ -396,10 +396,11 @@ int paged_attention_decode_step_streamk(void* out, const void* query, const void
  * (group_offsets, group_prefix_blocks, row_offsets, suffix_offsets,
  * token_start, prefix_item_offsets) with its three totals; workspace of
  * paged_attention_workspace_bytes(total_rows, num_q_heads, head_dim) bytes.
- * Three launches on `stream`.  A block id out of range in a group's prefix
- * makes every member's output NaN; a sequence whose context length gives
- * another count of suffix partitions than suffix_offsets (a plan made for
- * other lengths) gets a NaN output row.
+ * Two launches on `stream` (both passes in one, then the reduce).  A block
+ * id out of range in a group's prefix makes every member's output NaN; a
+ * sequence whose context length gives another count of suffix partitions
+ * than suffix_offsets (a plan made for other lengths) gets a NaN output
+ * row.
  * ------------------------------------------------------------------------- */
 int paged_attention_prefix_plan(const int32_t* context_lens_host, int num_seqs,
                                 const int32_t* group_offsets_host,
