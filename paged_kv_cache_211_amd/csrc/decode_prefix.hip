@@ -323,6 +323,10 @@ void decode_prefix_fused_kernel(const DecodeArgs a, const DecodeArgs b, PrefixAr
     __shared__ float p_lds[kWaves][HPW][kPBS];
     __shared__ u32x4 q_lds[kQLds ? kWaves : 1][kQLds ? HPW * kPD * 2 / 16 : 1];
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    // the suffix waves' streams end the launch (the longest suffixes run
+    // last), so their instructions go first when a prefix wave on the same
+    // SIMD is ready too
+    __builtin_amdgcn_s_setprio(1);
     suffix_wave<HPW, STORE>(b, ((int)blockIdx.x - npre) * kWaves + w, threadIdx.x & 63, p_lds[w],
                      q_lds[kQLds ? w : 0]);
   }
